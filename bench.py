@@ -1,0 +1,323 @@
+"""Benchmark of the width-6 verifier projection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+
+A step is one verifier projection of the ffn_up workload: Q8_1 quantization
+of the six f32 activation rows [6][5120] followed by the Q4_0 x Q8_1
+product against an [17408][5120] Q4_0 weight (q8_1_quantize +
+q4_0_mmvq_m6).  Twelve copies of the weight (601 MB, more than twice the
+256 MB last-level cache) are used round-robin so every step streams its
+weight from HBM; inputs are resident in device memory before timing starts.
+
+Printed: one JSON line with the effective weight bandwidth of a step
+(value, GB/s), the mmvq kernel's roofline against the 8 TB/s HBM peak, the
+fused Q6_K LM-head top-1 time on the lm_head workload, the per-M times of the
+down_sweep workload, and the oracle's CPU throughput on a bounded sample.
+
+Profiling helpers (one kernel family per process, for rocprofv3):
+    python bench.py --profile-target mmvq_m6|lmhead_top1|down_sweep|copy [--reps R]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ROTATE = 12
+PMC_RECORD = os.path.join(ROOT, "profiles", "pmc_q4_0_mmvq_m6_ffn_up.json")
+KERNEL_SOURCES = ["block_quantized_gemv_q8_amd/csrc/q4_0_mmvq.hip",
+                  "block_quantized_gemv_q8_amd/csrc/bq8_dev.h"]
+
+METRIC = "µs + effective weight GB/s (% of HBM peak) per Q4_0 M=6 proj; LM-head top-1 µs"
+
+
+def q4_0_bytes(N, K):
+    return N * (K // 32) * 18
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every launch uses)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.torch.cuda.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def setup_ffn_up(torch, bq, synth):
+    cfg = synth.FFN_UP
+    N, K, M = cfg["N"], cfg["K"], cfg["M"]
+    w, x = synth.ffn_up()
+    w0 = torch.from_numpy(w).to("cuda")
+    ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+    xd = torch.from_numpy(x).to("cuda")
+    xq = torch.empty((M, K // 32 * 36), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    return dict(N=N, K=K, M=M, ws=ws, x=xd, xq=xq, y=y, w_host=w, x_host=x)
+
+
+def step_ffn_up(bq, s, i):
+    bq.q8_1_quantize(s["x"], s["xq"])
+    bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
+
+
+def time_mmvq_only(torch, bq, s, reps):
+    bq.q8_1_quantize(s["x"], s["xq"])
+    for i in range(20):
+        bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
+    with Timer(torch) as t:
+        for i in range(reps):
+            bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
+    return t.ms * 1000.0 / reps
+
+
+def setup_lm_head(torch, bq, synth):
+    cfg = synth.LM_HEAD
+    N, K = cfg["N"], cfg["K"]
+    raw = synth.q6k_raw_weights_device(cfg["seed"], N, K)
+    pack = bq.q6k_pack_expand(raw, N, K)
+    del raw
+    rng = np.random.default_rng(cfg["seed"])
+    x = torch.from_numpy(synth.normal_rows(rng, cfg["M"], K)).to("cuda")
+    ids = torch.empty((cfg["rows"],), dtype=torch.int32, device="cuda")
+    scratch = torch.empty((bq.q6k_lmhead_top1_scratch_bytes(N, K, cfg["rows"]),),
+                          dtype=torch.uint8, device="cuda")
+    return dict(N=N, K=K, pack=pack, x=x, ids=ids, scratch=scratch, row0=cfg["row0"],
+                rows=cfg["rows"])
+
+
+def time_lm_head(torch, bq, s, reps):
+    def call():
+        bq.q6k_lmhead_top1(s["pack"], s["N"], s["K"], s["x"], s["row0"], s["rows"], s["ids"],
+                           s["scratch"])
+    for _ in range(5):
+        call()
+    with Timer(torch) as t:
+        for _ in range(reps):
+            call()
+    return t.ms * 1000.0 / reps
+
+
+def time_down_sweep(torch, bq, synth, reps):
+    cfg = synth.DOWN_SWEEP
+    N, K = cfg["N"], cfg["K"]
+    w, x = synth.down_sweep()
+    w0 = torch.from_numpy(w).to("cuda")
+    ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+    xq = bq.q8_1_quantize(torch.from_numpy(x).to("cuda"))
+    out = {}
+    for m in cfg["Ms"]:
+        f = getattr(bq, f"q4_0_mmvq_m{m}")
+        y = torch.empty((m, N), dtype=torch.float32, device="cuda")
+        for i in range(10):
+            f(ws[i % ROTATE], xq, y)
+        with Timer(torch) as t:
+            for i in range(reps):
+                f(ws[i % ROTATE], xq, y)
+        us = t.ms * 1000.0 / reps
+        out[str(m)] = {"us": round(us, 3), "GBps": round(q4_0_bytes(N, K) / us / 1e3, 1)}
+    return out
+
+
+def cpu_baseline(synth, budget_s=10.0):
+    """The oracle, as written, on the full ffn_up workload, repeated for
+    about budget_s seconds of wall time on the host's cores."""
+    import oracle
+
+    cfg = synth.FFN_UP
+    N, K, M = cfg["N"], cfg["K"], cfg["M"]
+    w, x = synth.ffn_up()
+    oracle.lib()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        xq = oracle.q8_1_quantize(x)
+        oracle.q4_0_gemv(w, N, K, xq, M)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s and n >= 3:
+            break
+    return {"value": round(n * q4_0_bytes(N, K) / el / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} full ffn_up projections (Q8_1 quantize of [6][5120] + Q4_0 GEMV "
+                      f"[17408x5120], M=6) in {el:.1f} s"}
+
+
+def pmc_traffic(per_launch_algo_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter record,
+    if it was taken on the current kernel source; else None."""
+    try:
+        with open(PMC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def profile_target(torch, bq, synth, target, reps):
+    if target == "copy":
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy: {reps} x {n} bytes")
+        return
+    if target == "mmvq_m6":
+        s = setup_ffn_up(torch, bq, synth)
+        bq.q8_1_quantize(s["x"], s["xq"])
+        for i in range(reps):
+            bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
+    elif target == "lmhead_top1":
+        s = setup_lm_head(torch, bq, synth)
+        for _ in range(reps):
+            bq.q6k_lmhead_top1(s["pack"], s["N"], s["K"], s["x"], s["row0"], s["rows"], s["ids"],
+                               s["scratch"])
+    elif target == "down_sweep":
+        time_down_sweep(torch, bq, synth, reps)
+    torch.cuda.synchronize()
+    log(f"{target}: done")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--profile-target", default=None)
+    ap.add_argument("--reps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each MI355X runs its "
+              "own shard; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_quantized_gemv_q8_amd as bq
+    from block_quantized_gemv_q8_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    bq.lib()
+
+    if args.profile_target:
+        profile_target(torch, bq, synth, args.profile_target, args.reps)
+        return
+
+    log("bench: ffn_up setup")
+    s = setup_ffn_up(torch, bq, synth)
+    N, K, M = s["N"], s["K"], s["M"]
+    wbytes = q4_0_bytes(N, K)
+    for i in range(args.warmup):
+        step_ffn_up(bq, s, i)
+    with Timer(torch) as t:
+        for i in range(args.steps):
+            step_ffn_up(bq, s, i)
+    step_us = t.ms * 1000.0 / args.steps
+    value = wbytes / step_us / 1e3  # GB/s
+    log(f"bench: step {step_us:.3f} us, {value:.1f} GB/s")
+
+    mmvq_us = time_mmvq_only(torch, bq, s, max(args.steps, 100))
+    achieved = wbytes / mmvq_us / 1e3
+    log(f"bench: mmvq_m6 {mmvq_us:.3f} us, {achieved:.1f} GB/s")
+
+    log("bench: lm_head setup")
+    lm = setup_lm_head(torch, bq, synth)
+    lm_us = time_lm_head(torch, bq, lm, 50)
+    pack_bytes = lm["pack"].numel()
+    log(f"bench: lmhead_top1 {lm_us:.2f} us, {pack_bytes / lm_us / 1e3:.1f} GB/s")
+    del lm
+
+    log("bench: down_sweep")
+    sweep = time_down_sweep(torch, bq, synth, 100)
+    log(f"bench: sweep {sweep}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline(synth)
+
+    traffic = pmc_traffic(wbytes)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1000.0, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_0 x q8_1 (int8 dot, f32 accumulate)",
+        "data": "synthetic (seeded; weights and activations resident in HBM, 12 rotating "
+                "weight copies)",
+        "config": {
+            "workload": "ffn_up: Q8_1 quantize of [6][5120] f32 + Q4_0 [17408x5120] M=6 "
+                        "projection",
+            "N": N, "K": K, "M": M,
+            "weight_bytes": wbytes,
+            "step_us": round(step_us, 3),
+            "mmvq_us": round(mmvq_us, 3),
+            "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+            "pct_hbm_peak_mmvq": round(100 * achieved / HBM_PEAK_GBS, 2),
+            "lmhead_top1_us": round(lm_us, 2),
+            "lmhead_pack_bytes": pack_bytes,
+            "lmhead_GBps": round(pack_bytes / lm_us / 1e3, 1),
+            "down_sweep": sweep,
+            "device": torch.cuda.get_device_name(0),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "q4_0_mmvq_m6 (ffn_up, 50,135,040 algorithmic bytes per launch)",
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+"""Thin Python binding of libbq8 (include/bq8.h): argument marshalling only.
+
+Each function takes torch tensors on the current HIP device, checks their
+dtype and shape, and calls the C entry point of the same name with raw device
+pointers and the current stream (``torch.cuda.current_stream()``).  Every
+step of the computation runs in the library's HIP kernels; there is no other
+code path.  Output tensors may be passed in (preallocated) or are allocated
+here with ``torch.empty``.  A nonzero status from the library raises
+``Bq8Error``.  If libbq8.so has not been built the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime libbq8 links against (same soname)
+
+from . import synth
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbq8.so")
+
+QK = 32
+QK_K = 256
+Q4_0_BYTES = 18
+Q8_1_BYTES = 36
+Q6_K_BYTES = 210
+MAX_M = 17
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_ST = ctypes.c_int32
+
+
+class Bq8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbq8.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libbq8.so not found at {LIB_PATH}; build it with "
+                "`python -m block_quantized_gemv_q8_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.bq8_status_string.restype = ctypes.c_char_p
+        L.bq8_status_string.argtypes = [_ST]
+        L.bq8_abi_version.restype = ctypes.c_int32
+        L.bq8_abi_version.argtypes = []
+        L.q8_1_quantize.restype = _ST
+        L.q8_1_quantize.argtypes = [_P, _I64, _I64, _P, _P]
+        for m in range(1, MAX_M + 1):
+            f = getattr(L, f"q4_0_mmvq_m{m}")
+            f.restype = _ST
+            f.argtypes = [_P, _I64, _I64, _P, _P, _P]
+        L.q4_0_mmvq.restype = _ST
+        L.q4_0_mmvq.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
+        L.q6k_pack_bytes.restype = _I64
+        L.q6k_pack_bytes.argtypes = [_I64, _I64]
+        L.q6k_pack_expand.restype = _ST
+        L.q6k_pack_expand.argtypes = [_P, _I64, _I64, _P, _I64, _P]
+        L.q6k_lmhead_top1_scratch_bytes.restype = _I64
+        L.q6k_lmhead_top1_scratch_bytes.argtypes = [_I64, _I64, _I64]
+        L.q6k_lmhead_top1.restype = _ST
+        L.q6k_lmhead_top1.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P, _P, _I64, _P]
+        L.silu_mul_q8_1.restype = _ST
+        L.silu_mul_q8_1.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
+        L.rms_norm_q8_1.restype = _ST
+        L.rms_norm_q8_1.argtypes = [_P, _I64, _I64, ctypes.c_float, _P, _P, _P]
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        msg = lib().bq8_status_string(status).decode()
+        raise Bq8Error(fn, status, msg)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    return t
+
+
+def status_string(status: int) -> str:
+    return lib().bq8_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return int(lib().bq8_abi_version())
+
+
+# ----------------------------------------------------------------- Q8_1
+def q8_1_quantize(x: torch.Tensor, xq: torch.Tensor | None = None) -> torch.Tensor:
+    """f32 [M][K] -> Q8_1 uint8 [M][K/32*36]."""
+    M, K = x.shape
+    xq = _out(xq, (M, K // QK * Q8_1_BYTES), torch.uint8, x.device, "xq")
+    _check("q8_1_quantize", lib().q8_1_quantize(_dev(x, "x", torch.float32), M, K,
+                                                _dev(xq, "xq", torch.uint8), _stream()))
+    return xq
+
+
+# ----------------------------------------------------------------- Q4_0
+def _q4_0_shape(w: torch.Tensor):
+    N, row_bytes = w.shape
+    if row_bytes % Q4_0_BYTES:
+        raise ValueError("w rows must hold whole 18-byte Q4_0 blocks")
+    return N, row_bytes // Q4_0_BYTES * QK
+
+
+def q4_0_mmvq(w: torch.Tensor, xq: torch.Tensor, M: int, y: torch.Tensor | None = None):
+    """Q4_0 w uint8 [N][K/32*18] times M Q8_1 rows -> f32 y [M][N]."""
+    N, K = _q4_0_shape(w)
+    if xq.numel() < M * (K // QK) * Q8_1_BYTES:
+        raise ValueError("xq holds fewer than M quantized rows of length K")
+    y = _out(y, (M, N), torch.float32, w.device, "y")
+    _check("q4_0_mmvq", lib().q4_0_mmvq(_dev(w, "w", torch.uint8), N, K,
+                                        _dev(xq, "xq", torch.uint8), M,
+                                        _dev(y, "y", torch.float32), _stream()))
+    return y
+
+
+def _make_mmvq(m: int):
+    name = f"q4_0_mmvq_m{m}"
+
+    def fn(w: torch.Tensor, xq: torch.Tensor, y: torch.Tensor | None = None):
+        N, K = _q4_0_shape(w)
+        if xq.numel() < m * (K // QK) * Q8_1_BYTES:
+            raise ValueError("xq holds fewer than M quantized rows of length K")
+        y = _out(y, (m, N), torch.float32, w.device, "y")
+        _check(name, getattr(lib(), name)(_dev(w, "w", torch.uint8), N, K,
+                                          _dev(xq, "xq", torch.uint8),
+                                          _dev(y, "y", torch.float32), _stream()))
+        return y
+
+    fn.__name__ = name
+    fn.__doc__ = f"Q4_0 x Q8_1 at M={m}: y [{m}][N] = W x^T (C entry point {name})."
+    return fn
+
+
+for _m in range(1, MAX_M + 1):
+    globals()[f"q4_0_mmvq_m{_m}"] = _make_mmvq(_m)
+del _m
+
+
+# ----------------------------------------------------------------- Q6_K
+def q6k_pack_bytes(N: int, K: int) -> int:
+    return int(lib().q6k_pack_bytes(N, K))
+
+
+def q6k_pack_expand(raw: torch.Tensor, N: int, K: int, pack: torch.Tensor | None = None):
+    """raw Q6_K uint8 [N][K/256*210] -> expanded pack uint8 [q6k_pack_bytes]."""
+    nbytes = q6k_pack_bytes(N, K)
+    if nbytes < 0:
+        raise ValueError("invalid Q6_K shape")
+    if raw.numel() != N * (K // QK_K) * Q6_K_BYTES:
+        raise ValueError("raw does not hold N x K/256 superblocks")
+    pack = _out(pack, (nbytes,), torch.uint8, raw.device, "pack")
+    _check("q6k_pack_expand", lib().q6k_pack_expand(_dev(raw, "raw", torch.uint8), N, K,
+                                                    _dev(pack, "pack", torch.uint8),
+                                                    pack.numel(), _stream()))
+    return pack
+
+
+def q6k_lmhead_top1_scratch_bytes(N: int, K: int, rows: int) -> int:
+    return int(lib().q6k_lmhead_top1_scratch_bytes(N, K, rows))
+
+
+def q6k_lmhead_top1(pack: torch.Tensor, N: int, K: int, x: torch.Tensor, row0: int, rows: int,
+                    ids: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
+    """Greedy ids int32 [rows] of rows row0.. of f32 x [M][K] through the pack."""
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [M][K]")
+    ids = _out(ids, (rows,), torch.int32, x.device, "ids")
+    need = q6k_lmhead_top1_scratch_bytes(N, K, rows)
+    if scratch is None:
+        scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check("q6k_lmhead_top1", lib().q6k_lmhead_top1(
+        _dev(pack, "pack", torch.uint8), N, K, _dev(x, "x", torch.float32), M, row0, rows,
+        _dev(ids, "ids", torch.int32), _dev(scratch, "scratch", torch.uint8), scratch.numel(),
+        _stream()))
+    return ids
+
+
+# --------------------------------------------------------- layer glue
+def silu_mul_q8_1(g: torch.Tensor, u: torch.Tensor, hq: torch.Tensor | None = None,
+                  h: torch.Tensor | None = None):
+    """hq = Q8_1(SiLU(g) * u); if h is given it receives the f32 product."""
+    M, N = g.shape
+    if tuple(u.shape) != (M, N):
+        raise ValueError("g and u must have the same shape")
+    hq = _out(hq, (M, N // QK * Q8_1_BYTES), torch.uint8, g.device, "hq")
+    hp = None if h is None else _dev(_out(h, (M, N), torch.float32, g.device, "h"), "h")
+    _check("silu_mul_q8_1", lib().silu_mul_q8_1(_dev(g, "g", torch.float32),
+                                                _dev(u, "u", torch.float32), M, N, hp,
+                                                _dev(hq, "hq", torch.uint8), _stream()))
+    return hq
+
+
+def rms_norm_q8_1(y: torch.Tensor, eps: float, xq: torch.Tensor | None = None,
+                  x: torch.Tensor | None = None):
+    """xq = Q8_1(y / sqrt(mean(y^2) + eps)) per row; x receives the f32 rows."""
+    M, K = y.shape
+    xq = _out(xq, (M, K // QK * Q8_1_BYTES), torch.uint8, y.device, "xq")
+    xp = None if x is None else _dev(_out(x, (M, K), torch.float32, y.device, "x"), "x")
+    _check("rms_norm_q8_1", lib().rms_norm_q8_1(_dev(y, "y", torch.float32), M, K, float(eps),
+                                                xp, _dev(xq, "xq", torch.uint8), _stream()))
+    return xq
+
+
+__all__ = ["Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "q4_0_mmvq",
+           *[f"q4_0_mmvq_m{m}" for m in range(1, MAX_M + 1)], "q6k_pack_bytes",
+           "q6k_pack_expand", "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1",
+           "silu_mul_q8_1", "rms_norm_q8_1", "synth"]

@@ -1,0 +1,89 @@
+// Internal device helpers shared by the libbq8 kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bq8.h"
+
+// Entry points of the C ABI; everything else stays hidden.
+#define BQ8_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace bq8 {
+
+constexpr int QK = 32;          // values per Q4_0 / Q8_1 block
+constexpr int QK_K = 256;       // values per Q6_K superblock
+constexpr int Q4_0_BYTES = 18;  // fp16 d + 16 nibble bytes
+constexpr int Q8_1_BYTES = 36;  // fp16 d + fp16 s + 32 int8
+constexpr int Q6_K_BYTES = 210; // ql[128] qh[64] scales[16] fp16 d
+constexpr int WAVE = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Exact binary16 -> binary32 of raw bits (v_cvt_f32_f16).
+__device__ __forceinline__ float h2f(uint32_t bits)
+{
+    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+    return (float)h;
+}
+
+// Round-to-nearest-even binary32 -> binary16 bits (v_cvt_f16_f32 under the
+// default rounding mode; fp16 denormals are kept).
+__device__ __forceinline__ uint32_t f2h(float f)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Signed int8 x4 dot product with int32 accumulate (v_dot4_i32_i8).
+__device__ __forceinline__ int dot4(int a, int b, int c)
+{
+    return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// Four unsigned nibble values (0..15, one per byte) -> four signed bytes
+// holding value - 8.  Adding 0x78 keeps every byte below 0x88, so no carry
+// crosses a byte; flipping bit 7 then subtracts 128: (x + 120) - 128 = x - 8.
+__device__ __forceinline__ int nib_minus8(uint32_t nibbles)
+{
+    return (int)((nibbles + 0x78787878u) ^ 0x80808080u);
+}
+
+// Quantize one 32-value Q8_1 block held one value per lane by 32 adjacent
+// lanes (lane32 = lane index within the group).  Arithmetic in binary32:
+// amax over the block, d = amax / 127 (correctly rounded division),
+// q = x / d rounded half away from zero and clamped to +-127 (d == 0 gives
+// q = 0), s = d * sum(q).  Lane 0 of the group writes d and s; every lane
+// writes its quant.  `blk` points at the block's 36 output bytes.
+__device__ __forceinline__ void q8_1_block_store(float v, int lane32, bool valid, uint8_t *blk)
+{
+    float a = fabsf(v);
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1)
+        a = fmaxf(a, __shfl_xor(a, off, 32));
+    const float d = a / 127.0f;
+    int q = 0;
+    if (d != 0.0f) {
+        q = (int)roundf(v / d);
+        q = q > 127 ? 127 : (q < -127 ? -127 : q);
+    }
+    int s = q;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1)
+        s += __shfl_xor(s, off, 32);
+    if (valid) {
+        blk[4 + lane32] = (uint8_t)(int8_t)q;
+        if (lane32 == 0) {
+            const float sf = d * (float)s;
+            *reinterpret_cast<uint32_t *>(blk) = f2h(d) | (f2h(sf) << 16);
+        }
+    }
+}
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline bq8_status launch_status()
+{
+    return hipGetLastError() == hipSuccess ? BQ8_OK : BQ8_ERR_HIP;
+}
+
+} // namespace bq8

@@ -1,0 +1,373 @@
+// Q6_K expansion and the fused Q6_K LM-head projection with greedy top-1.
+//
+// "Q6_K M=6 fused DFlash top-1 production record":
+//   "Why this was slow" -- the Q6_K output tensor is expanded once into signed
+//     int8 quants, int8 subscales and fp16 superblock scales; a kernel then
+//     quantizes the useful activation rows, reuses each weight slice across
+//     all of them and reduces to greedy ids without writing logits;
+//   "Outcome" -- only decoder rows 1..5 of the six-row block are projected;
+//   "Exactness and safety contracts" -- lowest-token-ID finite-tie rule, and
+//     the exact pack layout and byte count;
+//   "Memory and startup" -- the pack size for [5120, 248320].
+// Formats: include/bq8.h.
+//
+// Top-1 mapping on gfx950: lane <-> vocabulary row n (64 rows per wave,
+// 4 waves per workgroup, grid-stride over 64-row tiles).  A lane streams its
+// row of the pack in 128-byte runs (eight 128-bit loads), and the R quantized
+// activation rows -- identical for every lane -- come through scalar loads.
+// Per 32 values and activation row: 8 x v_dot4 give the two 16-value integer
+// dots, which the two int8 subscales combine exactly in int32; the result is
+// scaled by d_w * d_x (exact in binary32) and accumulated in binary32, in the
+// same order for every row, so equal weight rows give bitwise equal logits.
+// Each lane keeps, per activation row, a 64-bit key
+//     (order-preserving bits of the logit) << 32 | (0xFFFFFFFF - id)
+// whose maximum is the largest logit with the lowest id among ties.  Keys
+// meet by wave butterflies, then in LDS, then in one slot per workgroup in
+// the caller's scratch; the last workgroup to finish (atomic counter) reduces
+// the slots and writes the ids.  No logit ever reaches memory, and max over
+// integers makes the result independent of scheduling.
+#include "bq8_dev.h"
+
+namespace bq8 {
+
+// ------------------------------------------------------------- expansion
+// One wave per superblock (grid-stride).  Lane l produces the four codes
+// 4l..4l+3: value e of the superblock lies in half h = e/128; within it,
+// c = (e%128)/32 picks the low (c < 2) or high nibble of ql[64h + 32(c&1) + l']
+// and bits 2c..2c+1 of qh[32h + l'], with l' = e%32.
+__global__ __launch_bounds__(256) void q6k_expand_kernel(const uint8_t *__restrict__ raw,
+                                                         int64_t nsb, int8_t *__restrict__ Q,
+                                                         int8_t *__restrict__ SC,
+                                                         uint16_t *__restrict__ D)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int e = 4 * lane;
+    const int h = e >> 7;
+    const int c = (e & 127) >> 5;
+    const int l0 = e & 31;
+    const int ql_off = 64 * h + 32 * (c & 1) + l0;
+    const int qh_off = 128 + 32 * h + l0;
+    const int lo_shift = (c < 2) ? 0 : 4;
+    const int hi_shift = 2 * c;
+    for (int64_t i = wave_id; i < nsb; i += nwaves) {
+        const uint8_t *blk = raw + i * Q6_K_BYTES;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t lo = (blk[ql_off + t] >> lo_shift) & 0x0Fu;
+            const uint32_t hi = (blk[qh_off + t] >> hi_shift) & 0x03u;
+            const uint32_t code = lo | (hi << 4);
+            packed |= ((code - 32u) & 0xFFu) << (8 * t);
+        }
+        reinterpret_cast<uint32_t *>(Q + i * QK_K)[lane] = packed;
+        if (lane < 4) {
+            const uint8_t *s = blk + 192 + 4 * lane;
+            reinterpret_cast<uint32_t *>(SC + i * 16)[lane] =
+                (uint32_t)s[0] | ((uint32_t)s[1] << 8) | ((uint32_t)s[2] << 16) |
+                ((uint32_t)s[3] << 24);
+        }
+        if (lane == 4)
+            D[i] = (uint16_t)(blk[208] | (blk[209] << 8));
+    }
+}
+
+// ------------------------------------------------------------- top-1
+constexpr int TOP1_THREADS = 256;
+constexpr int TOP1_WAVES = TOP1_THREADS / WAVE;
+constexpr int TOP1_MAX_GRID = 1024;
+constexpr int TOP1_MAX_ROWS = 8;
+constexpr int64_t SCRATCH_HEADER = 256; // [0,4): completion counter
+
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t id)
+{
+    if (v == 0.0f)
+        v = 0.0f; // -0 ties with +0
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)k, off, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off, 64);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        k = o > k ? o : k;
+    }
+    return k;
+}
+
+// Rows 0..R-1 of x starting at row0 -> Q8_1 in scratch; reset the counter.
+__global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restrict__ x,
+                                                            int nblocks,
+                                                            uint8_t *__restrict__ xq,
+                                                            uint32_t *__restrict__ counter)
+{
+    const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+    const int blk = gid >> 5;
+    const int j = gid & 31;
+    const bool valid = blk < nblocks;
+    const float v = valid ? x[(size_t)blk * QK + j] : 0.0f;
+    q8_1_block_store(v, j, valid, xq + (size_t)blk * Q8_1_BYTES);
+    if (gid == 0)
+        *counter = 0u;
+}
+
+template <int R>
+__global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_kernel(
+    const int8_t *__restrict__ Q, const int8_t *__restrict__ SC, const uint16_t *__restrict__ D,
+    int N, int K, const uint8_t *__restrict__ xq, uint64_t *__restrict__ slots,
+    uint32_t *__restrict__ counter, int32_t *__restrict__ ids)
+{
+    __shared__ uint64_t wave_best[TOP1_WAVES][R];
+    __shared__ uint32_t is_last;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = K / QK;
+    const int nsb = K / QK_K;
+    const int ntiles = (N + WAVE - 1) / WAVE;
+
+    uint64_t best[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        best[r] = 0;
+
+    for (int t = blockIdx.x * TOP1_WAVES + wave; t < ntiles; t += gridDim.x * TOP1_WAVES) {
+        const int n_raw = t * WAVE + lane;
+        const int n = n_raw < N ? n_raw : N - 1; // loads stay in bounds
+        const int8_t *qrow = Q + (size_t)n * K;
+        const int8_t *srow = SC + (size_t)n * (K / 16);
+        const uint16_t *drow = D + (size_t)n * nsb;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[r] = 0.0f;
+        for (int sb = 0; sb < nsb; ++sb) {
+            const u32x4 scw = *reinterpret_cast<const u32x4 *>(srow + sb * 16);
+            const float dw = h2f(drow[sb]);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const u32x4 *p = reinterpret_cast<const u32x4 *>(qrow + sb * QK_K + half * 128);
+                uint32_t wq[32];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const u32x4 v = __builtin_nontemporal_load(p + i);
+                    wq[4 * i + 0] = v[0];
+                    wq[4 * i + 1] = v[1];
+                    wq[4 * i + 2] = v[2];
+                    wq[4 * i + 3] = v[3];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // 32-block b = sb*8 + half*4 + j uses subscales 2*(half*4+j) and +1
+                    const int sbi = 2 * (half * 4 + j);
+                    const uint32_t scword = scw[sbi >> 2];
+                    const int sca = __builtin_amdgcn_sbfe(scword, 8 * (sbi & 3), 8);
+                    const int scb = __builtin_amdgcn_sbfe(scword, 8 * ((sbi & 3) + 1), 8);
+                    const int b = sb * 8 + half * 4 + j;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t *xb = reinterpret_cast<const uint32_t *>(
+                            xq + ((size_t)r * nb + b) * Q8_1_BYTES);
+                        int sa = dot4((int)wq[8 * j + 0], (int)xb[1], 0);
+                        sa = dot4((int)wq[8 * j + 1], (int)xb[2], sa);
+                        sa = dot4((int)wq[8 * j + 2], (int)xb[3], sa);
+                        sa = dot4((int)wq[8 * j + 3], (int)xb[4], sa);
+                        int sbv = dot4((int)wq[8 * j + 4], (int)xb[5], 0);
+                        sbv = dot4((int)wq[8 * j + 5], (int)xb[6], sbv);
+                        sbv = dot4((int)wq[8 * j + 6], (int)xb[7], sbv);
+                        sbv = dot4((int)wq[8 * j + 7], (int)xb[8], sbv);
+                        const int I = sa * sca + sbv * scb;
+                        acc[r] = fmaf((float)I, dw * h2f(xb[0]), acc[r]);
+                    }
+                }
+            }
+        }
+        if (n_raw < N) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float v = acc[r];
+                if (!__builtin_isnan(v)) {
+                    const uint64_t k = make_key(v, (uint32_t)n_raw);
+                    best[r] = k > best[r] ? k : best[r];
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint64_t k = wave_max_u64(best[r]);
+        if (lane == 0)
+            wave_best[wave][r] = k;
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+        uint64_t k = 0;
+#pragma unroll
+        for (int w = 0; w < TOP1_WAVES; ++w)
+            k = wave_best[w][threadIdx.x] > k ? wave_best[w][threadIdx.x] : k;
+        slots[(size_t)blockIdx.x * R + threadIdx.x] = k;
+    }
+    // publish this workgroup's slot, then count it
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        is_last = (atomicAdd(counter, 1u) == gridDim.x - 1) ? 1u : 0u;
+    __syncthreads();
+    if (!is_last)
+        return;
+    __threadfence();
+    // the last workgroup reduces every slot; thread r*32+i handles row r
+    for (int r = 0; r < R; ++r) {
+        uint64_t k = 0;
+        for (int g = threadIdx.x; g < (int)gridDim.x; g += TOP1_THREADS) {
+            const uint64_t s = __hip_atomic_load(&slots[(size_t)g * R + r], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            k = s > k ? s : k;
+        }
+        k = wave_max_u64(k);
+        if (lane == 0)
+            wave_best[wave][r] = k;
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+        uint64_t k = 0;
+#pragma unroll
+        for (int w = 0; w < TOP1_WAVES; ++w)
+            k = wave_best[w][threadIdx.x] > k ? wave_best[w][threadIdx.x] : k;
+        // no finite logit at all -> -1
+        ids[threadIdx.x] = (k == 0) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+    }
+}
+
+static int64_t top1_grid(int64_t N)
+{
+    const int64_t tiles = (N + WAVE - 1) / WAVE;
+    int64_t g = (tiles + TOP1_WAVES - 1) / TOP1_WAVES;
+    return g > TOP1_MAX_GRID ? TOP1_MAX_GRID : g;
+}
+
+static bool top1_shape_ok(int64_t N, int64_t K)
+{
+    return N >= 1 && N < (int64_t(1) << 31) - 1 && K >= QK_K && K % QK_K == 0 &&
+           N * K < (int64_t(1) << 40) && K < (int64_t(1) << 24);
+}
+
+static int64_t xq_area(int64_t K, int64_t rows)
+{
+    const int64_t b = rows * (K / QK) * Q8_1_BYTES;
+    return (b + 255) / 256 * 256;
+}
+
+template <int R>
+static void launch_top1(const int8_t *Q, const int8_t *SC, const uint16_t *D, int N, int K,
+                        const uint8_t *xq, uint64_t *slots, uint32_t *counter, int32_t *ids,
+                        int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(q6k_top1_kernel<R>, dim3(grid), dim3(TOP1_THREADS), 0, s, Q, SC, D, N, K,
+                       xq, slots, counter, ids);
+}
+
+} // namespace bq8
+
+using namespace bq8;
+
+BQ8_EXPORT int64_t q6k_pack_bytes(int64_t N, int64_t K)
+{
+    if (N < 1 || K < QK_K || K % QK_K != 0 || N > (int64_t(1) << 40) / K)
+        return -1;
+    return N * K + N * (K / 16) + 2 * N * (K / QK_K);
+}
+
+BQ8_EXPORT bq8_status q6k_pack_expand(const void *raw, int64_t N, int64_t K, void *pack,
+                                      int64_t pack_bytes, void *stream)
+{
+    if (!raw || !pack)
+        return BQ8_ERR_NULL;
+    if (N < 1 || N >= (int64_t(1) << 31) || q6k_pack_bytes(N, K) < 0)
+        return BQ8_ERR_SHAPE;
+    if (!aligned(raw, 2) || !aligned(pack, 16))
+        return BQ8_ERR_ALIGN;
+    if (pack_bytes != q6k_pack_bytes(N, K))
+        return BQ8_ERR_SIZE;
+    const int64_t nsb = N * (K / QK_K);
+    int8_t *Q = (int8_t *)pack;
+    int8_t *SC = Q + N * K;
+    uint16_t *D = (uint16_t *)(SC + N * (K / 16));
+    int64_t grid = (nsb + 3) / 4; // 4 waves per workgroup, one superblock each
+    if (grid > 65536)
+        grid = 65536;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(q6k_expand_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                       (const uint8_t *)raw, nsb, Q, SC, D);
+    return launch_status();
+}
+
+BQ8_EXPORT int64_t q6k_lmhead_top1_scratch_bytes(int64_t N, int64_t K, int64_t rows)
+{
+    if (!top1_shape_ok(N, K) || rows < 1 || rows > TOP1_MAX_ROWS)
+        return -1;
+    return SCRATCH_HEADER + xq_area(K, rows) + top1_grid(N) * rows * (int64_t)sizeof(uint64_t);
+}
+
+BQ8_EXPORT bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, const float *x,
+                                      int64_t M, int64_t row0, int64_t rows, int32_t *ids,
+                                      void *scratch, int64_t scratch_bytes, void *stream)
+{
+    if (!pack || !x || !ids || !scratch)
+        return BQ8_ERR_NULL;
+    if (!top1_shape_ok(N, K) || rows < 1 || rows > TOP1_MAX_ROWS || M < 1 || row0 < 0 ||
+        row0 + rows > M || M * K >= (int64_t(1) << 31))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(pack, 16) || !aligned(x, 4) || !aligned(ids, 4) || !aligned(scratch, 16))
+        return BQ8_ERR_ALIGN;
+    if (scratch_bytes < q6k_lmhead_top1_scratch_bytes(N, K, rows))
+        return BQ8_ERR_SIZE;
+    const int8_t *Q = (const int8_t *)pack;
+    const int8_t *SC = Q + N * K;
+    const uint16_t *D = (const uint16_t *)(SC + N * (K / 16));
+    uint8_t *base = (uint8_t *)scratch;
+    uint32_t *counter = (uint32_t *)base;
+    uint8_t *xq = base + SCRATCH_HEADER;
+    uint64_t *slots = (uint64_t *)(xq + xq_area(K, rows));
+    const int nblocks = (int)(rows * (K / QK));
+    const int grid = (int)top1_grid(N);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(q6k_top1_prep_kernel, dim3((nblocks * 32 + 255) / 256), dim3(256), 0, s,
+                       x + row0 * K, nblocks, xq, counter);
+    if (hipGetLastError() != hipSuccess)
+        return BQ8_ERR_HIP;
+    const int n = (int)N, k = (int)K;
+    switch (rows) {
+    case 1: launch_top1<1>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
+    case 2: launch_top1<2>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
+    case 3: launch_top1<3>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
+    case 4: launch_top1<4>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
+    case 5: launch_top1<5>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
+    case 6: launch_top1<6>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
+    case 7: launch_top1<7>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
+    case 8: launch_top1<8>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
+    }
+    return launch_status();
+}
+
+BQ8_EXPORT const char *bq8_status_string(bq8_status status)
+{
+    switch (status) {
+    case BQ8_OK: return "ok";
+    case BQ8_ERR_NULL: return "a required pointer is NULL";
+    case BQ8_ERR_SHAPE: return "a size is out of range or not a block multiple";
+    case BQ8_ERR_ALIGN: return "a pointer is not aligned as documented";
+    case BQ8_ERR_SIZE: return "a byte count (pack or scratch) is not what is needed";
+    case BQ8_ERR_HIP: return "the HIP runtime reported a launch error";
+    default: return "unknown status";
+    }
+}
+
+BQ8_EXPORT int32_t bq8_abi_version(void) { return BQ8_ABI_VERSION; }

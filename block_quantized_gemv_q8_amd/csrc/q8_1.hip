@@ -1,0 +1,151 @@
+// Q8_1 activation quantization and the verifier-layer glue that ends in a
+// Q8_1 requantization (SiLU(gate)*up, and the weightless RMS step feeding the
+// next layer).
+//
+// "Qwen3.6 27B B70 follow-up: Q8 activation cache, FP8 artifacts, MTP
+// blocker", section "Q8_1 activation cache prototype": one exact Q8_1
+// activation is reused by sibling Q4_0 matmuls.  "Qwen3.6 27B Q4_0
+// DFlash/SYCL closure", "Closed or negative paths": the down-to-next-RMS/Q8
+// boundary.  Block format and arithmetic: include/bq8.h.
+//
+// Layout on the device: 32 adjacent lanes own one 32-value block, one value
+// per lane, so a wave64 quantizes two blocks; amax and sum(q) are butterfly
+// reductions inside each 32-lane half.  The work is a few hundred KB at most,
+// so the kernels are launch-latency bound, not bandwidth bound.
+#include "bq8_dev.h"
+
+namespace bq8 {
+
+__global__ __launch_bounds__(256) void q8_1_quantize_kernel(const float *__restrict__ x,
+                                                            int nblocks,
+                                                            uint8_t *__restrict__ xq)
+{
+    const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+    const int blk = gid >> 5;
+    const int j = gid & 31;
+    const bool valid = blk < nblocks;
+    const float v = valid ? x[(size_t)blk * QK + j] : 0.0f;
+    q8_1_block_store(v, j, valid, xq + (size_t)blk * Q8_1_BYTES);
+}
+
+__global__ __launch_bounds__(256) void silu_mul_q8_1_kernel(const float *__restrict__ g,
+                                                            const float *__restrict__ u,
+                                                            int nblocks, float *__restrict__ h,
+                                                            uint8_t *__restrict__ hq)
+{
+    const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+    const int blk = gid >> 5;
+    const int j = gid & 31;
+    const bool valid = blk < nblocks;
+    float v = 0.0f;
+    if (valid) {
+        const size_t i = (size_t)blk * QK + j;
+        const float gv = g[i];
+        v = gv / (1.0f + expf(-gv)) * u[i];
+        if (h)
+            h[i] = v;
+    }
+    q8_1_block_store(v, j, valid, hq + (size_t)blk * Q8_1_BYTES);
+}
+
+// One workgroup per row: sum of squares with a fixed reduction tree
+// (per-thread strided partials, then a wave butterfly, then the waves in
+// index order), so the result does not depend on scheduling.
+constexpr int RMS_THREADS = 256;
+
+__global__ __launch_bounds__(RMS_THREADS) void rms_norm_q8_1_kernel(const float *__restrict__ y,
+                                                                    int K, float eps,
+                                                                    float *__restrict__ x,
+                                                                    uint8_t *__restrict__ xq)
+{
+    __shared__ float wave_sums[RMS_THREADS / WAVE];
+    const int m = blockIdx.x;
+    const float *row = y + (size_t)m * K;
+    float ss = 0.0f;
+    for (int k = threadIdx.x; k < K; k += RMS_THREADS) {
+        const float v = row[k];
+        ss = fmaf(v, v, ss);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        ss += __shfl_xor(ss, off, 64);
+    if ((threadIdx.x & 63) == 0)
+        wave_sums[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < RMS_THREADS / WAVE; ++w)
+        tot += wave_sums[w];
+    const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+
+    const int nb = K / QK;
+    uint8_t *out = xq + (size_t)m * nb * Q8_1_BYTES;
+    // 256 threads = 8 groups of 32 lanes; group g handles blocks g, g+8, ...
+    const int grp = threadIdx.x >> 5;
+    const int j = threadIdx.x & 31;
+    for (int b0 = 0; b0 < nb; b0 += RMS_THREADS / QK) {
+        const int b = b0 + grp;
+        const bool valid = b < nb;
+        float v = 0.0f;
+        if (valid) {
+            v = row[b * QK + j] * inv;
+            if (x)
+                x[(size_t)m * K + b * QK + j] = v;
+        }
+        q8_1_block_store(v, j, valid, out + (size_t)b * Q8_1_BYTES);
+    }
+}
+
+} // namespace bq8
+
+using namespace bq8;
+
+BQ8_EXPORT bq8_status q8_1_quantize(const float *x, int64_t M, int64_t K, void *xq, void *stream)
+{
+    if (!x || !xq)
+        return BQ8_ERR_NULL;
+    if (M < 1 || K < QK || K % QK != 0 || M * K >= (int64_t(1) << 31))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(x, 4) || !aligned(xq, 4))
+        return BQ8_ERR_ALIGN;
+    const int nblocks = (int)(M * K / QK);
+    const int threads = 256;
+    const int grid = (int)((M * K + threads - 1) / threads);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(q8_1_quantize_kernel, dim3(grid), dim3(threads), 0, (hipStream_t)stream, x,
+                       nblocks, (uint8_t *)xq);
+    return launch_status();
+}
+
+BQ8_EXPORT bq8_status silu_mul_q8_1(const float *g, const float *u, int64_t M, int64_t N, float *h,
+                                    void *hq, void *stream)
+{
+    if (!g || !u || !hq)
+        return BQ8_ERR_NULL;
+    if (M < 1 || N < QK || N % QK != 0 || M * N >= (int64_t(1) << 31))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(g, 4) || !aligned(u, 4) || !aligned(hq, 4) || (h && !aligned(h, 4)))
+        return BQ8_ERR_ALIGN;
+    const int nblocks = (int)(M * N / QK);
+    const int threads = 256;
+    const int grid = (int)((M * N + threads - 1) / threads);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(silu_mul_q8_1_kernel, dim3(grid), dim3(threads), 0, (hipStream_t)stream, g, u,
+                       nblocks, h, (uint8_t *)hq);
+    return launch_status();
+}
+
+BQ8_EXPORT bq8_status rms_norm_q8_1(const float *y, int64_t M, int64_t K, float eps, float *x,
+                                    void *xq, void *stream)
+{
+    if (!y || !xq)
+        return BQ8_ERR_NULL;
+    if (M < 1 || M > 64 || K < QK || K % QK != 0 || M * K >= (int64_t(1) << 31) || !(eps > 0.0f))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(y, 4) || !aligned(xq, 4) || (x && !aligned(x, 4)))
+        return BQ8_ERR_ALIGN;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(rms_norm_q8_1_kernel, dim3((unsigned)M), dim3(RMS_THREADS), 0,
+                       (hipStream_t)stream, y, (int)K, eps, x, (uint8_t *)xq);
+    return launch_status();
+}

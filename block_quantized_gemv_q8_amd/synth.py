@@ -49,6 +49,12 @@ LM_HEAD_TIES = ((0, 248319), (1, 256), (255, 256))
 STREAM = dict(name="stream", layers=64, hidden=5120, ffn=17408, M=6, seed=5)
 
 
+def random_bytes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform random bytes (``Generator.bytes``) as a uint8 array."""
+    n = int(np.prod(shape))
+    return np.frombuffer(rng.bytes(n), dtype=np.uint8).reshape(shape)
+
+
 def _f16_bits(values_f32: np.ndarray) -> np.ndarray:
     """fp16 bit patterns of f32 values (numpy's round-to-nearest-even)."""
     return np.asarray(values_f32, np.float32).astype(np.float16).view(np.uint16)
@@ -62,7 +68,7 @@ def q4_0_weights(rng: np.random.Generator, N: int, K: int,
     assert K % QK == 0
     nb = K // QK
     d = rng.uniform(d_range[0], d_range[1], size=(N, nb)).astype(np.float32)
-    qs = rng.integers(0, 256, size=(N, nb, 16), dtype=np.uint8)
+    qs = random_bytes(rng, (N, nb, 16))
     w = np.empty((N, nb, Q4_0_BYTES), np.uint8)
     w[:, :, 0:2] = _f16_bits(d).astype("<u2").view(np.uint8).reshape(N, nb, 2)
     w[:, :, 2:] = qs
@@ -77,7 +83,7 @@ def q6k_raw_weights(rng: np.random.Generator, N: int, K: int,
     assert K % QK_K == 0
     ns = K // QK_K
     raw = np.empty((N, ns, Q6_K_BYTES), np.uint8)
-    raw[:, :, 0:192] = rng.integers(0, 256, size=(N, ns, 192), dtype=np.uint8)
+    raw[:, :, 0:192] = random_bytes(rng, (N, ns, 192))
     raw[:, :, 192:208] = rng.integers(sc_range[0], sc_range[1] + 1, size=(N, ns, 16),
                                       dtype=np.int8).view(np.uint8)
     d = rng.uniform(d_range[0], d_range[1], size=(N, ns)).astype(np.float32)
@@ -160,3 +166,22 @@ def q4_0_weights_device(seed: int, N: int, K: int, device="cuda", d_range=Q4_0_D
     qs = torch.randint(0, 256, (N, nb, 16), dtype=torch.uint8, device=device, generator=g)
     dbytes = d.to(torch.float16).view(torch.uint8).reshape(N, nb, 2)
     return torch.cat([dbytes, qs], dim=2).reshape(N, nb * Q4_0_BYTES).contiguous()
+
+
+def q6k_raw_weights_device(seed: int, N: int, K: int, device="cuda", d_range=Q6_K_D_RANGE,
+                           sc_range=Q6_K_SC_RANGE):
+    """Random raw Q6_K superblocks generated on the device (same
+    distributions as ``q6k_raw_weights``; a different random stream).
+    Returns a uint8 tensor [N][K/256*210]."""
+    import torch
+
+    ns = K // QK_K
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    qbytes = torch.randint(0, 256, (N, ns, 192), dtype=torch.uint8, device=device, generator=g)
+    sc = torch.randint(sc_range[0], sc_range[1] + 1, (N, ns, 16), dtype=torch.int8, device=device,
+                       generator=g).view(torch.uint8)
+    d = torch.empty((N, ns), dtype=torch.float32, device=device)
+    d.uniform_(d_range[0], d_range[1], generator=g)
+    dbytes = d.to(torch.float16).view(torch.uint8).reshape(N, ns, 2)
+    return torch.cat([qbytes, sc, dbytes], dim=2).reshape(N, ns * Q6_K_BYTES).contiguous()

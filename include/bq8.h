@@ -1,0 +1,191 @@
+/*
+ * bq8.h -- C ABI of libbq8: block-quantized GEMV kernels for AMD Instinct
+ * MI355X (gfx950, CDNA4).
+ *
+ * The hot path is the width-6 speculative verifier projection and the fused
+ * draft LM head of two web pages:
+ *   "Qwen3.6 27B Q4_0 DFlash/SYCL closure" -- Q4_0 x Q8_1 MMVQ with direct
+ *     coverage of every row count 1..17 ("What materially worked"), width-6
+ *     gate/up and down projections, the down-to-next-RMS/Q8 boundary
+ *     ("Closed or negative paths");
+ *   "Q6_K M=6 fused DFlash top-1 production record" -- the Q6_K output
+ *     weight expanded once to int8 quants + int8 subscales + fp16 superblock
+ *     scales, a kernel that quantizes the useful activation rows, reuses each
+ *     weight slice across all of them and reduces each row to its greedy
+ *     token id without writing logits ("Why this was slow"), with the
+ *     lowest-token-ID finite-tie contract ("Exactness and safety contracts");
+ *   "Qwen3.6 27B B70 follow-up: Q8 activation cache, FP8 artifacts, MTP
+ *     blocker" -- one exact Q8_1 activation reused by sibling Q4_0 matmuls
+ *     ("Q8_1 activation cache prototype").
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the comment says otherwise.  The
+ *     caller allocates and owns every buffer; the library allocates nothing
+ *     and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work; results are valid once the stream reaches
+ *     them.  Nothing synchronizes inside the library.
+ *   - Arguments are validated on the host BEFORE anything is enqueued.  On a
+ *     validation failure the call returns a nonzero status and no output
+ *     byte is touched.  BQ8_ERR_HIP reports a failed launch.
+ *   - fp16 fields are raw IEEE binary16 bits, little-endian.
+ *   - Calls on one stream are ordered; concurrent calls on different
+ *     streams must not share output or scratch buffers.
+ *
+ * Formats (block layouts follow the public GGUF formats the pages' .gguf
+ * model files use):
+ *   Q8_1  32 activations in 36 bytes: d (fp16), s (fp16), q[32] (int8);
+ *         d = max|x|/127, q = x/d rounded half away from zero, s = d*sum(q).
+ *   Q4_0  32 weights in 18 bytes: d (fp16), qs[16]; element j < 16 is the
+ *         low nibble of qs[j], element j+16 the high nibble; value d*(q-8).
+ *   Q6_K  256 weights in 210 bytes: ql[128], qh[64], scales[16] (int8),
+ *         d (fp16); value d * scales[e/16] * (u - 32) for a 6-bit code u.
+ *   Expanded Q6_K pack: three planar row-major arrays,
+ *         Q int8 [N][K] at 0, SC int8 [N][K/16] at N*K,
+ *         D fp16 [N][K/256] at N*K + N*K/16  (total q6k_pack_bytes(N, K)).
+ */
+#ifndef BQ8_H
+#define BQ8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BQ8_ABI_VERSION 1
+
+typedef int32_t bq8_status;
+enum {
+    BQ8_OK = 0,
+    BQ8_ERR_NULL = 1,  /* a required pointer is NULL                         */
+    BQ8_ERR_SHAPE = 2, /* a size is out of range or not a block multiple     */
+    BQ8_ERR_ALIGN = 3, /* a pointer is not aligned as documented             */
+    BQ8_ERR_SIZE = 4,  /* a byte count (pack, scratch) is not what is needed */
+    BQ8_ERR_HIP = 5    /* the HIP runtime reported a launch error            */
+};
+
+/* Host.  Static, never-freed description of a status code. */
+const char *bq8_status_string(bq8_status status);
+
+/* Host.  BQ8_ABI_VERSION of the built library. */
+int32_t bq8_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Q8_1 activation quantization.
+ * x:  f32 [M][K] row-major, 4-byte aligned.
+ * xq: Q8_1 [M][K/32] blocks of 36 bytes, row-major by (row, block),
+ *     4-byte aligned; fully overwritten.  One quantized activation may feed
+ *     any number of sibling q4_0_mmvq_* calls (the Q8_1 activation cache of
+ *     the follow-up page, made explicit).
+ * Shape: M >= 1, K >= 32, K % 32 == 0, M*K < 2^31.
+ * Subnormal amax: d = amax/127 may round to 0 (then the block is all zero)
+ * or lose precision (quants are clamped to +-127).  NaN/Inf inputs are
+ * outside the contract.
+ * ---------------------------------------------------------------------- */
+bq8_status q8_1_quantize(const float *x, int64_t M, int64_t K, void *xq, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Q4_0 x Q8_1 matrix-vector products at M activation rows, one entry point
+ * per M = 1..17 (the closure page's direct MMVQ coverage through rows 9-17:
+ * no row count falls back to re-reading the weight once per row).
+ *   y[m][n] = sum_k W[n][k] * X[m][k]
+ * with W the dequantized Q4_0 weight and X the dequantized Q8_1 rows.
+ * w:  Q4_0 [N][K/32] blocks of 18 bytes, row-major, 16-byte aligned.
+ * xq: Q8_1 [M][K/32] (from q8_1_quantize), 4-byte aligned.
+ * y:  f32 [M][N] row-major, 4-byte aligned; fully overwritten.
+ * Shape: 1 <= N < 2^31, K >= 32, K % 32 == 0, N*K/32*18 < 2^40.
+ * Each weight byte is read from memory once per call whatever M is.
+ * Accumulation is binary32 over exact per-block integer dots, in a fixed
+ * order: results are bitwise reproducible run to run, and equal weight rows
+ * give bitwise equal outputs.
+ * ---------------------------------------------------------------------- */
+bq8_status q4_0_mmvq_m1(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m2(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m3(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m4(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m5(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m6(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m7(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m8(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m9(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m10(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m11(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m12(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m13(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m14(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m15(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m16(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+bq8_status q4_0_mmvq_m17(const void *w, int64_t N, int64_t K, const void *xq, float *y, void *stream);
+
+/* Same as q4_0_mmvq_m<M> with M (1..17) as an argument. */
+bq8_status q4_0_mmvq(const void *w, int64_t N, int64_t K, const void *xq, int64_t M, float *y,
+                     void *stream);
+
+/* ------------------------------------------------------------------------
+ * Q6_K expansion (run once, at load time).  The fused-head page expands the
+ * output tensor once into signed int8 quants, int8 subscales and fp16
+ * superblock scales ("Why this was slow") and requires "the exact expected
+ * layout and byte count" of the pack ("Exactness and safety contracts").
+ * q6k_pack_bytes: host; N*K + N*K/16 + 2*N*K/256, or -1 if the shape is
+ * invalid.  [248320 x 5120] gives 1,360,793,600 ("Memory and startup").
+ * raw:  Q6_K [N][K/256] superblocks of 210 bytes, row-major, 2-byte aligned.
+ * pack: expanded pack (layout above), 16-byte aligned, pack_bytes bytes,
+ *       fully overwritten.
+ * Shape: 1 <= N < 2^31, K >= 256, K % 256 == 0.
+ * pack_bytes != q6k_pack_bytes(N, K) -> BQ8_ERR_SIZE.
+ * ---------------------------------------------------------------------- */
+int64_t q6k_pack_bytes(int64_t N, int64_t K);
+bq8_status q6k_pack_expand(const void *raw, int64_t N, int64_t K, void *pack, int64_t pack_bytes,
+                           void *stream);
+
+/* ------------------------------------------------------------------------
+ * Fused Q6_K LM-head projection + greedy top-1 ("Q6_K M=6 fused DFlash
+ * top-1 production record": only decoder rows 1..5 of the six-row block are
+ * projected, each weight slice is reused across all of them, and each row is
+ * reduced on the device to the lowest token id among its maximal logits;
+ * logits are never written to memory).
+ * pack:    expanded Q6_K pack of an [N][K] weight (q6k_pack_expand).
+ * x:       f32 [M][K] row-major activations, 4-byte aligned.
+ * row0, rows: project rows row0 .. row0+rows-1 of x (the hot path uses
+ *          M = 6, row0 = 1, rows = 5); 1 <= rows <= 8, row0 + rows <= M.
+ * ids:     int32 [rows]; ids[r] is the greedy token id of row row0 + r.
+ * scratch: device workspace of at least q6k_lmhead_top1_scratch_bytes(N, K,
+ *          rows) bytes, 16-byte aligned (quantized rows and per-row keys);
+ *          its contents on entry do not matter.
+ * Shape: 1 <= N < 2^31 - 1, K >= 256, K % 256 == 0, N*K < 2^40.
+ * Tie rule: among equal maximal logits the lowest id wins; -0 equals +0.
+ * Equal weight rows give bitwise equal logits, so planted duplicate rows
+ * always resolve to the lower id.
+ * q6k_lmhead_top1_scratch_bytes: host; -1 if the shape is invalid.
+ * ---------------------------------------------------------------------- */
+int64_t q6k_lmhead_top1_scratch_bytes(int64_t N, int64_t K, int64_t rows);
+bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, const float *x, int64_t M,
+                           int64_t row0, int64_t rows, int32_t *ids, void *scratch,
+                           int64_t scratch_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Verifier-layer glue between projections (a width-6 FFN block whose gate
+ * and up projections share one Q8_1 activation and whose down projection
+ * consumes SiLU(gate)*up requantized to Q8_1; the closure page's width-6
+ * gate/up and down projections and its down-to-next-RMS/Q8 boundary).
+ *
+ * silu_mul_q8_1: h = g / (1 + exp(-g)) * u elementwise, then hq = Q8_1(h).
+ *   g, u: f32 [M][N] row-major; h: optional f32 [M][N] copy of h (NULL to
+ *   skip); hq: Q8_1 [M][N/32].  Shape: M >= 1, N >= 32, N % 32 == 0,
+ *   M*N < 2^31.  4-byte alignment.
+ * rms_norm_q8_1: x = y / sqrt(mean_k(y^2) + eps) per row, then xq = Q8_1(x).
+ *   y: f32 [M][K]; x: optional f32 [M][K] copy (NULL to skip); xq: Q8_1
+ *   [M][K/32].  Shape: 1 <= M <= 64, K >= 32, K % 32 == 0, M*K < 2^31;
+ *   eps > 0.  4-byte alignment.
+ * ---------------------------------------------------------------------- */
+bq8_status silu_mul_q8_1(const float *g, const float *u, int64_t M, int64_t N, float *h, void *hq,
+                         void *stream);
+bq8_status rms_norm_q8_1(const float *y, int64_t M, int64_t K, float eps, float *x, void *xq,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQ8_H */

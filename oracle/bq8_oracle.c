@@ -337,6 +337,7 @@ void orc_q6k_pack_expand(const uint8_t *raw, int64_t N, int64_t K, uint8_t *pack
     int8_t *SC = (int8_t *)(pack + N * K);
     uint8_t *D = pack + N * K + N * (K / 16);
     const int64_t nsb = N * (K / QK_K);
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < nsb; ++i) {
         uint16_t dbits;
         orc_q6k_decode(raw + i * Q6_K_BYTES, 1, QK_K, Q + i * QK_K, SC + i * 16, &dbits);

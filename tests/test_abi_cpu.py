@@ -1,0 +1,161 @@
+"""The C-ABI library loads, exports every symbol the header declares, and
+rejects bad arguments on the host before touching the device.  None of these
+calls reaches the GPU: every case fails validation, which happens before any
+HIP call, or is a host-only size query."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bq8.h")
+
+OK, NULL, SHAPE, ALIGN, SIZE, HIP = 0, 1, 2, 3, 4, 5
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[a-z_0-9 ]+?\*?\s*\b([a-z_0-9]+)\s*\(", text, re.M)) -
+                  {"if", "extern"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    import block_quantized_gemv_q8_amd as b
+
+    return b.lib()
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for m in range(1, 18):
+        assert f"q4_0_mmvq_m{m}" in names
+    for n in ["q8_1_quantize", "q4_0_mmvq", "q6k_pack_bytes", "q6k_pack_expand",
+              "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1", "bq8_status_string",
+              "bq8_abi_version", "silu_mul_q8_1", "rms_norm_q8_1"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_exports_nothing_else():
+    import subprocess
+    import block_quantized_gemv_q8_amd as b
+
+    out = subprocess.run(["nm", "-D", "--defined-only", b.api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == set(_declared_functions())
+
+
+def test_version_and_status_strings(L):
+    import block_quantized_gemv_q8_amd as b
+
+    assert b.abi_version() == 1
+    for s in range(6):
+        assert len(b.status_string(s)) > 0
+    assert b.status_string(99) == "unknown status"
+
+
+def test_pack_bytes_and_scratch_queries(L):
+    import block_quantized_gemv_q8_amd as b
+
+    assert b.q6k_pack_bytes(248320, 5120) == 1360793600
+    assert b.q6k_pack_bytes(1, 256) == 256 + 16 + 2
+    assert b.q6k_pack_bytes(0, 256) == -1
+    assert b.q6k_pack_bytes(4, 255) == -1
+    assert b.q6k_pack_bytes(4, 384) == -1
+    s = b.q6k_lmhead_top1_scratch_bytes(248320, 5120, 5)
+    assert 0 < s < 1 << 20
+    assert b.q6k_lmhead_top1_scratch_bytes(248320, 5120, 0) == -1
+    assert b.q6k_lmhead_top1_scratch_bytes(248320, 5120, 9) == -1
+    assert b.q6k_lmhead_top1_scratch_bytes(2 ** 31, 256, 1) == -1
+
+
+# Fake, never-dereferenced device addresses: every call below must fail
+# validation and return without any HIP call.
+A = 0x10000  # 64 KiB aligned
+
+
+def test_quantize_validation(L):
+    assert L.q8_1_quantize(None, 1, 32, A, None) == NULL
+    assert L.q8_1_quantize(A, 1, 32, None, None) == NULL
+    assert L.q8_1_quantize(A, 0, 32, A, None) == SHAPE
+    assert L.q8_1_quantize(A, 1, 48, A, None) == SHAPE
+    assert L.q8_1_quantize(A, 1, 0, A, None) == SHAPE
+    assert L.q8_1_quantize(A, 1 << 16, 1 << 15, A, None) == SHAPE
+    assert L.q8_1_quantize(A + 2, 1, 32, A, None) == ALIGN
+    assert L.q8_1_quantize(A, 1, 32, A + 1, None) == ALIGN
+
+
+@pytest.mark.parametrize("m", [1, 6, 17])
+def test_mmvq_validation(L, m):
+    f = getattr(L, f"q4_0_mmvq_m{m}")
+    assert f(None, 8, 64, A, A, None) == NULL
+    assert f(A, 8, 64, None, A, None) == NULL
+    assert f(A, 8, 64, A, None, None) == NULL
+    assert f(A, 0, 64, A, A, None) == SHAPE
+    assert f(A, 8, 48, A, A, None) == SHAPE
+    assert f(A, 8, 0, A, A, None) == SHAPE
+    assert f(A, 1 << 31, 64, A, A, None) == SHAPE
+    assert f(A + 4, 8, 64, A, A, None) == ALIGN
+    assert f(A, 8, 64, A + 2, A, None) == ALIGN
+    assert f(A, 8, 64, A, A + 2, None) == ALIGN
+
+
+def test_mmvq_dispatch_rejects_bad_m(L):
+    assert L.q4_0_mmvq(A, 8, 64, A, 0, A, None) == SHAPE
+    assert L.q4_0_mmvq(A, 8, 64, A, 18, A, None) == SHAPE
+    assert L.q4_0_mmvq(None, 8, 64, A, 6, A, None) == NULL
+
+
+def test_expand_validation(L):
+    n = 1360793600
+    assert L.q6k_pack_expand(None, 248320, 5120, A, n, None) == NULL
+    assert L.q6k_pack_expand(A, 248320, 5120, None, n, None) == NULL
+    assert L.q6k_pack_expand(A, 248320, 5000, A, n, None) == SHAPE
+    assert L.q6k_pack_expand(A, 0, 5120, A, n, None) == SHAPE
+    assert L.q6k_pack_expand(A + 1, 248320, 5120, A, n, None) == ALIGN
+    assert L.q6k_pack_expand(A, 248320, 5120, A + 8, n, None) == ALIGN
+    assert L.q6k_pack_expand(A, 248320, 5120, A, n - 1, None) == SIZE
+    assert L.q6k_pack_expand(A, 248320, 5120, A, n + 16, None) == SIZE
+
+
+def test_top1_validation(L):
+    s = L.q6k_lmhead_top1_scratch_bytes(248320, 5120, 5)
+    args = dict(pack=A, N=248320, K=5120, x=A, M=6, row0=1, rows=5, ids=A, scratch=A, sb=s)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.q6k_lmhead_top1(a["pack"], a["N"], a["K"], a["x"], a["M"], a["row0"], a["rows"],
+                                 a["ids"], a["scratch"], a["sb"], None)
+
+    assert call(pack=None) == NULL
+    assert call(x=None) == NULL
+    assert call(ids=None) == NULL
+    assert call(scratch=None) == NULL
+    assert call(K=5000) == SHAPE
+    assert call(N=0) == SHAPE
+    assert call(rows=0) == SHAPE
+    assert call(rows=9, M=12) == SHAPE
+    assert call(row0=2) == SHAPE          # rows 2..6 of 6
+    assert call(row0=-1) == SHAPE
+    assert call(pack=A + 4) == ALIGN
+    assert call(x=A + 2) == ALIGN
+    assert call(scratch=A + 8) == ALIGN
+    assert call(sb=s - 1) == SIZE
+
+
+def test_layer_glue_validation(L):
+    assert L.silu_mul_q8_1(None, A, 6, 64, None, A, None) == NULL
+    assert L.silu_mul_q8_1(A, A, 6, 48, None, A, None) == SHAPE
+    assert L.silu_mul_q8_1(A, A, 6, 64, A + 2, A, None) == ALIGN
+    assert L.rms_norm_q8_1(None, 6, 64, ctypes.c_float(1e-6), None, A, None) == NULL
+    assert L.rms_norm_q8_1(A, 65, 64, ctypes.c_float(1e-6), None, A, None) == SHAPE
+    assert L.rms_norm_q8_1(A, 6, 64, ctypes.c_float(0.0), None, A, None) == SHAPE
+    assert L.rms_norm_q8_1(A, 6, 64, ctypes.c_float(1e-6), None, A + 1, None) == ALIGN

@@ -1,0 +1,347 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle.
+
+Bars: Q8_1 bytes, expanded packs and top-1 ids bit-exact; float outputs
+|gpu - oracle| <= 1e-5 * sum_b |t_b| + 1e-6 with t_b the 32-block
+contributions (the oracle returns that sum as `bound`); top-1 ids equal the
+oracle's unless the oracle's gap between the two candidates is within the
+two rows' tolerances and the rows differ.  Shapes span several tiles, a
+ragged tail, the unaligned-K path and the full workloads.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import block_quantized_gemv_q8_amd as bq  # noqa: E402
+from block_quantized_gemv_q8_amd import synth  # noqa: E402
+
+DEV = "cuda:0"
+REL, ABS = 1e-5, 1e-6
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_close(gpu, ref, bound, what):
+    err = np.abs(gpu.astype(np.float64) - ref)
+    tol = REL * bound + ABS
+    bad = err > tol
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at "
+                             f"{tuple(i)}: gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r} "
+                             f"tol={tol[tuple(i)]!r}")
+    return float((err / tol).max())
+
+
+def check_ids(gpu_ids, ref_ids, logits, bound, pack_rows_equal=None):
+    for r, (g, o) in enumerate(zip(gpu_ids, ref_ids)):
+        if g == o:
+            continue
+        assert 0 <= g < logits.shape[1], f"row {r}: id {g} out of range"
+        gap = logits[r, o] - logits[r, g]
+        tol = REL * (bound[r, o] + bound[r, g]) + 2 * ABS
+        assert gap <= tol, f"row {r}: gpu {g} oracle {o} gap {gap} > {tol}"
+        if pack_rows_equal is not None:
+            assert not pack_rows_equal(g, o), f"row {r}: equal weight rows must give the lower id"
+
+
+# ------------------------------------------------------------------ Q8_1
+def _quantize_inputs():
+    rng = np.random.default_rng(101)
+    cases = []
+    for M, K in [(1, 32), (3, 96), (6, 5120), (17, 17408)]:
+        x = synth.normal_rows(rng, M, K)
+        x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20
+        cases.append(x)
+    # edge blocks: zero, constant, exact half-way ties, tiny/subnormal amax
+    e = np.zeros((4, 128), np.float32)
+    e[0, 32:64] = 3.25
+    k = np.arange(31, dtype=np.float64)
+    e[1, 0] = 127 / 128
+    e[1, 1:32] = (k + 0.5) / 128
+    e[1, 32:64] = -e[1, 0:32]
+    e[2, 0:32] = np.float32(3e-43)
+    e[2, 32] = np.float32(1e-45)
+    e[2, 64:96] = np.float32(1e-40) * np.linspace(-1, 1, 32, dtype=np.float32)
+    e[3] = np.float32(6.1e-5) * rng.standard_normal(128).astype(np.float32)
+    cases.append(e)
+    return cases
+
+
+@pytest.mark.parametrize("case", range(5))
+def test_q8_1_quantize_bitexact(case):
+    x = _quantize_inputs()[case]
+    say(f"q8_1_quantize case {case} shape {x.shape}")
+    xq = host(bq.q8_1_quantize(dev(x)))
+    assert (xq == oracle.q8_1_quantize(x)).all()
+
+
+# ------------------------------------------------------------------ Q4_0
+SMALL_SHAPES = [(200, 512), (70, 96), (1, 32), (64, 256), (130, 1024), (333, 2304)]
+
+
+@pytest.mark.parametrize("N,K", SMALL_SHAPES)
+def test_mmvq_every_m_small(N, K):
+    w, x = synth.random_q4_0_case(1000 + N + K, N, K, 17)
+    xq = oracle.q8_1_quantize(x)
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
+    wd, xqd = dev(w), dev(xq)
+    for m in range(1, 18):
+        say(f"q4_0_mmvq_m{m} N={N} K={K}")
+        y = host(getattr(bq, f"q4_0_mmvq_m{m}")(wd, xqd))
+        assert_close(y, ref[:m], bound[:m], f"m{m} N{N} K{K}")
+        y2 = host(bq.q4_0_mmvq(wd, xqd, m))
+        assert (y2 == y).all()
+
+
+def test_mmvq_tiny_workload():
+    w, x = synth.tiny()
+    N, K, M = 256, 256, 1
+    xqd = bq.q8_1_quantize(dev(x))
+    xq = host(xqd)
+    assert (xq == oracle.q8_1_quantize(x)).all()
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, M)
+    y = host(bq.q4_0_mmvq_m1(dev(w), xqd))
+    assert_close(y, ref, bound, "tiny")
+
+
+def test_mmvq_ffn_up_workload_full():
+    w, x = synth.ffn_up()
+    N, K, M = 17408, 5120, 6
+    say("ffn_up full: quantize + q4_0_mmvq_m6")
+    xqd = bq.q8_1_quantize(dev(x))
+    xq = host(xqd)
+    assert (xq == oracle.q8_1_quantize(x)).all()
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, M)
+    y = host(bq.q4_0_mmvq_m6(dev(w), xqd))
+    r = assert_close(y, ref, bound, "ffn_up")
+    say(f"ffn_up max err/tol = {r:.3g}")
+
+
+def test_mmvq_down_sweep_full():
+    w, x = synth.down_sweep()
+    N, K = 5120, 17408
+    xqd = bq.q8_1_quantize(dev(x))
+    xq = host(xqd)
+    assert (xq == oracle.q8_1_quantize(x)).all()
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
+    wd = dev(w)
+    for m in synth.DOWN_SWEEP["Ms"]:
+        say(f"down_sweep q4_0_mmvq_m{m}")
+        y = host(getattr(bq, f"q4_0_mmvq_m{m}")(wd, xqd))
+        assert_close(y, ref[:m], bound[:m], f"down m{m}")
+
+
+def test_mmvq_deterministic_and_row_independent():
+    N, K, M = 1000, 5120, 6
+    w, x = synth.random_q4_0_case(77, N, K, M)
+    w[500] = w[3]
+    w[999] = w[3]
+    wd = dev(w)
+    xqd = bq.q8_1_quantize(dev(x))
+    ys = [host(bq.q4_0_mmvq_m6(wd, xqd)) for _ in range(3)]
+    assert all((ys[0] == y).all() for y in ys[1:])
+    assert (ys[0][:, 500] == ys[0][:, 3]).all() and (ys[0][:, 999] == ys[0][:, 3]).all()
+
+
+def test_mmvq_leaves_guard_bytes():
+    N, K, M = 150, 512, 9
+    w, x = synth.random_q4_0_case(78, N, K, M)
+    buf = torch.full((M * N + 64,), 12345.0, dtype=torch.float32, device=DEV)
+    y = buf[:M * N].view(M, N)
+    xqbuf = torch.full((M * K // 32 * 36 + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+    xq = xqbuf[:M * K // 32 * 36].view(M, K // 32 * 36)
+    bq.q8_1_quantize(dev(x), xq)
+    bq.q4_0_mmvq_m9(dev(w), xq, y)
+    b = host(buf)
+    assert (b[M * N:] == 12345.0).all()
+    assert (host(xqbuf)[-64:] == 0xA5).all()
+    ref, bound = oracle.q4_0_gemv(w, N, K, host(xq), M)
+    assert_close(b[:M * N].reshape(M, N), ref, bound, "guarded")
+
+
+# ------------------------------------------------------------------ Q6_K
+@pytest.mark.parametrize("N,K", [(1, 256), (70, 512), (333, 1280)])
+def test_q6k_expand_bitexact_small(N, K):
+    rng = np.random.default_rng(200 + N)
+    raw = synth.q6k_raw_weights(rng, N, K)
+    say(f"q6k_pack_expand N={N} K={K}")
+    pack = host(bq.q6k_pack_expand(dev(raw), N, K))
+    assert (pack == oracle.q6k_pack_expand(raw, N, K)).all()
+
+
+@pytest.mark.parametrize("N,K,rows", [(300, 512, 5), (64, 256, 1), (1000, 1280, 8), (1, 256, 3),
+                                      (4097, 768, 5)])
+def test_top1_small(N, K, rows):
+    rng = np.random.default_rng(300 + N + rows)
+    raw = synth.q6k_raw_weights(rng, N, K)
+    x = synth.normal_rows(rng, rows + 1, K)
+    pack = oracle.q6k_pack_expand(raw, N, K)
+    say(f"q6k_lmhead_top1 N={N} K={K} rows={rows}")
+    ids = host(bq.q6k_lmhead_top1(dev(pack), N, K, dev(x), 1, rows))
+    oid, logits, bound, _ = oracle.q6k_lmhead_top1(pack, N, K, x, 1, rows)
+    check_ids(ids, oid, logits, bound)
+
+
+def test_top1_small_planted_ties():
+    N, K = 700, 512
+    rng = np.random.default_rng(310)
+    raw = synth.q6k_raw_weights(rng, N, K)
+    x = synth.normal_rows(rng, 6, K)
+    for lo, hi in [(0, 699), (1, 256), (255, 256), (63, 64), (127, 128)]:
+        r2 = raw.copy()
+        r2[lo] = r2[hi] = _dominant_raw_row(x[1:6], K)
+        pack = oracle.q6k_pack_expand(r2, N, K)
+        say(f"top1 small tie ({lo},{hi})")
+        ids = host(bq.q6k_lmhead_top1(dev(pack), N, K, dev(x), 1, 5))
+        oid, logits, _, _ = oracle.q6k_lmhead_top1(pack, N, K, x, 1, 5)
+        assert list(oid) == [lo] * 5
+        assert list(ids) == [lo] * 5
+    # every activation row zero: all logits are zero, id 0 everywhere
+    pack = oracle.q6k_pack_expand(raw, N, K)
+    ids = host(bq.q6k_lmhead_top1(dev(pack), N, K, dev(np.zeros((6, K), np.float32)), 1, 5))
+    assert list(ids) == [0] * 5
+
+
+def _dominant_raw_row(xrows, K):
+    """A raw Q6_K row whose logit exceeds every random row's for all given
+    activation rows: quants follow the sign pattern of sum_r x_r/|x_r|, with
+    the largest subscale and d = 1e-3 (encoded by the oracle's codec)."""
+    v = (xrows / np.linalg.norm(xrows, axis=1, keepdims=True)).sum(axis=0)
+    q = np.clip(np.round(31 * v / np.abs(v).max()), -32, 31).astype(np.int8)[None, :]
+    sc = np.full((1, K // 16), 63, np.int8)
+    d = np.full((1, K // 256), np.float16(1e-3).view(np.uint16), np.uint16)
+    return oracle.q6k_encode(q, sc, d, 1, K)[0]
+
+
+@pytest.fixture(scope="module")
+def lm_head_full():
+    N, K = synth.LM_HEAD["N"], synth.LM_HEAD["K"]
+    say("lm_head: generating raw Q6_K [248320 x 5120]")
+    raw, x = synth.lm_head()
+    rawd = dev(raw)
+    say("lm_head: q6k_pack_expand on the device")
+    packd = bq.q6k_pack_expand(rawd, N, K)
+    pack = oracle.q6k_pack_expand(raw, N, K)
+    return dict(N=N, K=K, raw=raw, x=x, rawd=rawd, packd=packd, pack=pack)
+
+
+def test_q6k_expand_full_bitexact(lm_head_full):
+    f = lm_head_full
+    say("lm_head: compare 1,360,793,600-byte packs")
+    assert f["packd"].numel() == 1360793600
+    assert (host(f["packd"]) == f["pack"]).all()
+
+
+def test_top1_lm_head_full(lm_head_full):
+    f = lm_head_full
+    N, K = f["N"], f["K"]
+    say("lm_head: q6k_lmhead_top1 rows 1..5")
+    xd = dev(f["x"])
+    ids = host(bq.q6k_lmhead_top1(f["packd"], N, K, xd, 1, 5))
+    oid, logits, bound, _ = oracle.q6k_lmhead_top1(f["pack"], N, K, f["x"], 1, 5)
+    say(f"lm_head ids gpu {list(ids)} oracle {list(oid)}")
+    check_ids(ids, oid, logits, bound)
+    again = [host(bq.q6k_lmhead_top1(f["packd"], N, K, xd, 1, 5)) for _ in range(2)]
+    assert all((a == ids).all() for a in again)
+    f["logits"], f["bound"] = logits, bound
+
+
+TILE_PAIRS = [(63, 64), (1023, 1024), (65535, 65536), (131071, 131072), (248318, 248319)]
+
+
+def _tie_pairs():
+    import os
+    out = []
+    path = os.path.join(os.path.dirname(__file__), "golden", "lm_head_tie_pairs.txt")
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            out.append(tuple(int(v) for v in line.split()))
+    return out
+
+
+@pytest.mark.parametrize("pair", _tie_pairs() + TILE_PAIRS)
+def test_top1_lm_head_planted_ties(lm_head_full, pair):
+    f = lm_head_full
+    N, K = f["N"], f["K"]
+    lo, hi = pair
+    x = f["x"]
+    row = _dominant_raw_row(x[1:6], K)
+    say(f"lm_head tie pair ({lo},{hi})")
+    orig = f["raw"][[lo, hi]].copy()
+    try:
+        f["rawd"][lo] = torch.from_numpy(row).to(DEV)
+        f["rawd"][hi] = torch.from_numpy(row).to(DEV)
+        bq.q6k_pack_expand(f["rawd"], N, K, f["packd"])
+        ids = host(bq.q6k_lmhead_top1(f["packd"], N, K, dev(x), 1, 5))
+    finally:
+        f["rawd"][lo] = torch.from_numpy(orig[0]).to(DEV)
+        f["rawd"][hi] = torch.from_numpy(orig[1]).to(DEV)
+        bq.q6k_pack_expand(f["rawd"], N, K, f["packd"])
+        torch.cuda.synchronize()
+    # oracle: the planted rows' logits beat every other row's
+    sub = oracle.q6k_pack_expand(np.stack([row, row]), 2, K)
+    pl, _ = oracle.q6k_pack_logits(sub, 2, K, oracle.q8_1_quantize(x[1:6]), 5)
+    if "logits" not in f:
+        _, f["logits"], f["bound"], _ = oracle.q6k_lmhead_top1(f["pack"], N, K, x, 1, 5)
+    assert (pl[:, 0] == pl[:, 1]).all()
+    assert (pl[:, 0] > f["logits"].max(axis=1)).all()
+    assert list(ids) == [lo] * 5
+
+
+def test_top1_lm_head_zero_activations(lm_head_full):
+    f = lm_head_full
+    x = np.zeros((6, f["K"]), np.float32)
+    x[0] = 1.0  # row 0 is never projected
+    ids = host(bq.q6k_lmhead_top1(f["packd"], f["N"], f["K"], dev(x), 1, 5))
+    assert list(ids) == [0] * 5
+
+
+# ------------------------------------------------------------- layer glue
+def test_silu_mul_q8_1_stage():
+    rng = np.random.default_rng(400)
+    M, N = 6, 17408
+    g = (rng.standard_normal((M, N)) * 3).astype(np.float32)
+    u = (rng.standard_normal((M, N)) * 2).astype(np.float32)
+    g[0, :8] = [0, -0.0, 80, -80, 100, -100, 1e-30, -1e-30]
+    h = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    hq = host(bq.silu_mul_q8_1(dev(g), dev(u), h=h))
+    hg = host(h)
+    ref = oracle.silu_mul(g, u)
+    err = np.abs(hg.astype(np.float64) - ref)
+    assert (err <= REL * np.abs(ref) + ABS).all()
+    assert (hq == oracle.q8_1_quantize(hg)).all()
+    hq2 = host(bq.silu_mul_q8_1(dev(g), dev(u)))
+    assert (hq2 == hq).all()
+
+
+def test_rms_norm_q8_1_stage():
+    rng = np.random.default_rng(401)
+    M, K = 6, 5120
+    y = (rng.standard_normal((M, K)) * 40).astype(np.float32)
+    y[5] = 0.0
+    xo = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    xq = host(bq.rms_norm_q8_1(dev(y), 1e-6, x=xo))
+    xg = host(xo)
+    ref = oracle.rms_norm(y, 1e-6)
+    err = np.abs(xg.astype(np.float64) - ref)
+    assert (err <= REL * np.abs(ref) + ABS).all()
+    assert (xq == oracle.q8_1_quantize(xg)).all()
