@@ -2,7 +2,9 @@
 
     python -m block_quantized_gemv_q8_amd.build
 
-Flags: -O3 for gfx950 only; correctly rounded binary32 division and square
+Flags: -O3 for gfx950 only; no floating-point contraction (a product rounded
+to binary32 and then to fp16 must not become one fused rounding); correctly
+rounded binary32 division and square
 root and no denormal flushing (the Q8_1 quants are decided by a binary32
 division that must match an IEEE implementation bit for bit); packed-FP32
 instructions disabled.
@@ -29,7 +31,7 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     "-shared",
     "-fno-fast-math",
-    "-ffp-contract=fast",
+    "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -73,7 +73,12 @@ __device__ __forceinline__ void q8_1_block_store(float v, int lane32, bool valid
     if (valid) {
         blk[4 + lane32] = (uint8_t)(int8_t)q;
         if (lane32 == 0) {
-            const float sf = d * (float)s;
+            float sf = d * (float)s;
+            // s is the binary32 product rounded to fp16.  Without this
+            // barrier the compiler turns multiply-then-convert into one
+            // v_fma_mixlo_f16, which rounds the exact product to fp16 once
+            // and differs from the twice-rounded value in rare ties.
+            __asm__ volatile("" : "+v"(sf));
             *reinterpret_cast<uint32_t *>(blk) = f2h(d) | (f2h(sf) << 16);
         }
     }

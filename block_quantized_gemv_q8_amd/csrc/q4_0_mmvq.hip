@@ -39,7 +39,10 @@ __device__ __forceinline__ uint32_t word_at(const uint32_t *w)
 }
 
 // Accumulate one Q4_0 block (scale bits `dbits`, nibble words qs[0..3])
-// against block `b` of every activation row.
+// against block `b` of every activation row.  Each nibble q is placed in the
+// high half of a byte with its top bit flipped, which is the signed byte
+// 16*(q - 8); the int32 dot is therefore 16x the exact block dot, and the
+// caller scales the finished sums by 1/16 (exact: a power of two).
 template <int M>
 __device__ __forceinline__ void block_dot(uint32_t dbits, const uint32_t qs[4],
                                           const uint8_t *__restrict__ xq, int nb, int b,
@@ -48,8 +51,8 @@ __device__ __forceinline__ void block_dot(uint32_t dbits, const uint32_t qs[4],
     int lo[4], hi[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        lo[i] = nib_minus8(qs[i] & 0x0F0F0F0Fu);        // elements 4i .. 4i+3
-        hi[i] = nib_minus8((qs[i] >> 4) & 0x0F0F0F0Fu); // elements 16+4i .. 16+4i+3
+        lo[i] = (int)(((qs[i] << 4) & 0xF0F0F0F0u) ^ 0x80808080u); // elements 4i .. 4i+3
+        hi[i] = (int)((qs[i] & 0xF0F0F0F0u) ^ 0x80808080u);        // elements 16+4i .. 16+4i+3
     }
     const float dw = h2f(dbits);
 #pragma unroll
@@ -91,24 +94,40 @@ __device__ __forceinline__ void chunk_all(const uint32_t *wd, const uint8_t *__r
     (chunk_block<J, M>(wd, xq, nb, b0 + J, acc), ...);
 }
 
-// ALIGNED: K % 256 == 0 and w 16-byte aligned, so every 8-block chunk of a
-// row is a 16-byte-aligned 144-byte run read with nine 128-bit loads.
-// Otherwise every block is read with 16-bit loads (always aligned).
+// Order this wave's LDS writes before its reads of other lanes' data (a
+// wave's LDS operations complete in order; the fences stop the compiler from
+// moving accesses across).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int CHUNK_BYTES = 8 * Q4_0_BYTES;           // 144: eight blocks, 16-byte aligned
+constexpr int CHUNK_PIECES = CHUNK_BYTES / 16;         // 9 x 16 bytes
+constexpr int STAGE_BYTES = WAVE * CHUNK_BYTES;        // 64 rows x 144 bytes per wave
+
+// ALIGNED (K % 256 == 0, w 16-byte aligned): a wave stages the 144-byte
+// chunk c of its 64 rows through LDS.  The 576 16-byte pieces are loaded
+// with nine 128-bit loads in which nine consecutive lanes read one row's
+// contiguous 144 bytes (each load instruction touches ~7 rows instead of
+// 64), written to LDS in the same order (so LDS holds [row][144 bytes]),
+// then every lane reads back its own row.
+// Otherwise (any K % 32 == 0) each lane reads its row's blocks directly
+// with 16-bit loads (always aligned).
 template <int M, bool ALIGNED>
 __global__ __launch_bounds__(1024) void q4_0_mmvq_dot4_kernel(const uint8_t *__restrict__ w,
                                                               int N, int nb,
                                                               const uint8_t *__restrict__ xq,
                                                               float *__restrict__ y)
 {
-    extern __shared__ float partial[]; // [S][M][64]
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
-    int n = blockIdx.x * WAVE + lane;
-    const bool active = n < N;
-    if (!active)
-        n = N - 1; // keep every load in bounds; the store is skipped
-    const uint8_t *row = w + (size_t)n * nb * Q4_0_BYTES;
+    const int n0 = blockIdx.x * WAVE;
+    const size_t row_bytes = (size_t)nb * Q4_0_BYTES;
 
     float acc[M];
 #pragma unroll
@@ -116,21 +135,45 @@ __global__ __launch_bounds__(1024) void q4_0_mmvq_dot4_kernel(const uint8_t *__r
         acc[m] = 0.0f;
 
     if constexpr (ALIGNED) {
+        uint8_t *stage = smem + (size_t)wave * STAGE_BYTES;
+        const uint8_t *tile = w + (size_t)n0 * row_bytes;
+        // per-lane byte offsets (within the tile) of the nine pieces it loads;
+        // rows past N repeat row N-1 so every load stays in bounds
+        uint32_t goff[CHUNK_PIECES];
+#pragma unroll
+        for (int j = 0; j < CHUNK_PIECES; ++j) {
+            const int p = j * WAVE + lane;
+            const int r = p / CHUNK_PIECES;
+            const int q = p - r * CHUNK_PIECES;
+            const int rr = (n0 + r < N) ? r : (N - 1 - n0);
+            goff[j] = (uint32_t)(rr * row_bytes) + 16u * (uint32_t)q;
+        }
         const int nchunks = nb >> 3;
         for (int c = wave; c < nchunks; c += S) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(row + (size_t)c * 144);
+            const uint8_t *src = tile + (size_t)c * CHUNK_BYTES;
+            u32x4 v[CHUNK_PIECES];
+#pragma unroll
+            for (int j = 0; j < CHUNK_PIECES; ++j)
+                v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + goff[j]));
+            wave_lds_sync();
+#pragma unroll
+            for (int j = 0; j < CHUNK_PIECES; ++j)
+                reinterpret_cast<u32x4 *>(stage)[j * WAVE + lane] = v[j];
+            wave_lds_sync();
             uint32_t wd[36];
 #pragma unroll
-            for (int i = 0; i < 9; ++i) {
-                const u32x4 v = __builtin_nontemporal_load(p + i);
-                wd[4 * i + 0] = v[0];
-                wd[4 * i + 1] = v[1];
-                wd[4 * i + 2] = v[2];
-                wd[4 * i + 3] = v[3];
+            for (int i = 0; i < CHUNK_PIECES; ++i) {
+                const u32x4 t = reinterpret_cast<const u32x4 *>(stage + lane * CHUNK_BYTES)[i];
+                wd[4 * i + 0] = t[0];
+                wd[4 * i + 1] = t[1];
+                wd[4 * i + 2] = t[2];
+                wd[4 * i + 3] = t[3];
             }
             chunk_all<M>(wd, xq, nb, c * 8, acc, std::make_integer_sequence<int, 8>{});
         }
     } else {
+        const int n = (n0 + lane < N) ? n0 + lane : N - 1;
+        const uint8_t *row = w + (size_t)n * row_bytes;
         for (int b = wave; b < nb; b += S) {
             const uint16_t *p = reinterpret_cast<const uint16_t *>(row + (size_t)b * Q4_0_BYTES);
             uint32_t qs[4];
@@ -141,6 +184,9 @@ __global__ __launch_bounds__(1024) void q4_0_mmvq_dot4_kernel(const uint8_t *__r
         }
     }
 
+    // partial sums of the S waves meet in LDS (reusing the staging area)
+    __syncthreads();
+    float *partial = reinterpret_cast<float *>(smem); // [S][M][64]
 #pragma unroll
     for (int m = 0; m < M; ++m)
         partial[(wave * M + m) * WAVE + lane] = acc[m];
@@ -151,16 +197,265 @@ __global__ __launch_bounds__(1024) void q4_0_mmvq_dot4_kernel(const uint8_t *__r
         float s = 0.0f;
         for (int v = 0; v < S; ++v)
             s += partial[(v * M + m) * WAVE + l];
-        const int nn = blockIdx.x * WAVE + l;
+        const int nn = n0 + l;
         if (nn < N)
-            y[(size_t)m * N + nn] = s;
+            y[(size_t)m * N + nn] = s * 0.0625f;
     }
 }
 
-// Waves per workgroup: enough workgroups x waves to give every CU several
-// waves, never more waves than K-units, at most 16 waves (1024 threads), and
+// ---------------------------------------------------------------- MFMA
+// Padded int8 MFMA, v_mfma_i32_16x16x64_i8 (D[16][16] += A[16][64] *
+// B[64][16]), used block-diagonally so one instruction produces the exact
+// integer dots of 16 weight rows x 2 blocks x 8 activation rows:
+//   B column n = weight row n of the 16-row tile; k in [0,32) is block
+//     8G+j of the chunk, k in [32,64) is block 8G+j+4 (same 2-byte alignment);
+//   A row i = (blk, m) = (i/8, i%8) holds activation row 8s+m of block
+//     8G+j+4*blk in its own half of k and zeros in the other half (and zeros
+//     past M); s = 0..ceil(M/8)-1 selects a set of eight activation rows,
+//     each set one MFMA sharing the same B.
+// Lane l (c = l%16, g = l/16) supplies B column c, k-group g: 16 signed bytes
+// 16*(q-8) made from qs[8h..8h+7] (h = g%2) of block 8G+j+4*(g/2) -- eight
+// low nibbles, then eight high nibbles -- and A row c, k-group g: the
+// matching activation bytes q[8h..8h+7], q[16+8h..16+8h+7] (or zeros).  The k
+// order inside a block is the same on both sides, so D[(blk,m)][n] = 16 * I.
+// Output lane l holds D rows 4g..4g+3 = block 8G+j+4*(g/2), m = 4h..4h+3 of
+// column c: exactly the block whose weight scale the lane read, so each of
+// its sums is scaled by d_w * d_x[m] and accumulated in binary32.  Lanes l
+// and l+32 hold the two halves of the chunk and are added at the end; then
+// the S waves' sums meet in LDS in wave order.
+//
+// Streaming: the S waves of a workgroup share one 16-row tile and take its
+// CB-block chunks round-robin.  A chunk is 16 rows x CB*18 contiguous bytes
+// (CB = 32: 576-byte runs, the longest that divide the usual K) plus the
+// chunk's CB Q8_1 blocks of every activation row; both are loaded as 16-byte
+// pieces (consecutive lanes along each contiguous run), written to the
+// wave's LDS stage, and read back in MFMA operand order.  The next chunk's
+// loads are issued before the current chunk is computed, and compute reads
+// only LDS, so the wait for one chunk never waits for the next.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+template <int M, int CB, int NST>
+struct MfmaShape {
+    static constexpr int MS = (M + 7) / 8;                   // MFMAs per block pair
+    static constexpr int RUN = CB * Q4_0_BYTES;              // weight bytes per row per chunk
+    static constexpr int XRUN = CB * Q8_1_BYTES;             // activation bytes per row per chunk
+    static constexpr int WPIECES = 16 * RUN / 16;            // 16 rows of weights
+    static constexpr int XPIECES = M * XRUN / 16;            // M rows of activations
+    static constexpr int PIECES = WPIECES + XPIECES;
+    static constexpr int LOADS = (PIECES + WAVE - 1) / WAVE; // DMA instructions per chunk
+    static constexpr int DXOFF = LOADS * WAVE * 16;          // f32 d_x [CB][8*MS] after the pieces
+    static constexpr int STAGE = DXOFF + CB * 8 * MS * 4;    // bytes per stage
+    static constexpr int WAVE_LDS = NST * STAGE;             // bytes per wave
+};
+
+// One workgroup owns a 16-row tile; its S waves take the tile's CB-block
+// chunks round-robin.  A chunk is staged in LDS as a list of 16-byte pieces:
+// first the tile's 16 rows x CB*18 contiguous weight bytes (consecutive lanes
+// along each row run), then the chunk's CB Q8_1 blocks of each activation
+// row.  The pieces travel by global_load_lds_dwordx4 -- global memory straight
+// into LDS, 64 lanes x 16 bytes per instruction -- into an NST-stage ring per
+// wave, so NST-1 chunks are in flight while one is computed and no VGPRs hold
+// data in transit.  Every load is issued unconditionally (past the wave's
+// last chunk it repeats the last chunk's addresses: cache hits, never used)
+// so the wait counts stay exact.
+template <int M, int CB, int NST>
+__global__ __launch_bounds__(512) void q4_0_mmvq_mfma_kernel(const uint8_t *__restrict__ w,
+                                                              int N, int nb,
+                                                              const uint8_t *__restrict__ xq,
+                                                              float *__restrict__ y)
+{
+    using SH = MfmaShape<M, CB, NST>;
+    constexpr int MS = SH::MS, LOADS = SH::LOADS;
+    static_assert(CB % 8 == 0 && (SH::RUN % 16) == 0 && (SH::XRUN % 16) == 0, "chunk shape");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+    const int n0 = blockIdx.x * 16;
+    const size_t row_bytes = (size_t)nb * Q4_0_BYTES;
+    uint8_t *ring = smem + (size_t)wave * SH::WAVE_LDS;
+
+    const int c16 = lane & 15;
+    const int g = lane >> 4;
+    const int h = g & 1;
+    const int hb = g >> 1;
+    bool a_on[MS];
+    uint32_t aoff[MS]; // offset of this lane's A row (activation row 8s + c16%8) in a stage
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+        const int m = 8 * s + (c16 & 7);
+        a_on[s] = ((c16 >> 3) == hb) && (m < M);
+        aoff[s] = (uint32_t)SH::WPIECES * 16 + (uint32_t)(a_on[s] ? m : 0) * SH::XRUN;
+    }
+    // per-lane source of piece p = 64j + lane at chunk c: base[j] + c * step[j]
+    const uint8_t *base[LOADS];
+    uint32_t step[LOADS];
+    {
+        const uint8_t *tile = w + (size_t)n0 * row_bytes;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int p = j * WAVE + lane;
+            if (p < SH::WPIECES) {
+                const int r = p / (SH::RUN / 16);
+                const int q = p - r * (SH::RUN / 16);
+                const int rr = (n0 + r < N) ? r : (N - 1 - n0);
+                base[j] = tile + (size_t)rr * row_bytes + 16 * q;
+                step[j] = SH::RUN;
+            } else if (p < SH::PIECES) {
+                const int px = p - SH::WPIECES;
+                const int m = px / (SH::XRUN / 16);
+                const int q = px - m * (SH::XRUN / 16);
+                base[j] = xq + (size_t)m * nb * Q8_1_BYTES + 16 * q;
+                step[j] = SH::XRUN;
+            } else {
+                base[j] = tile; // padding slot: a valid address, never read back
+                step[j] = SH::RUN;
+            }
+        }
+    }
+    auto issue = [&](int c, int st) {
+        uint8_t *dst = ring + st * SH::STAGE;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j)
+            __builtin_amdgcn_global_load_lds((global_void_t *)(base[j] + (size_t)c * step[j]),
+                                             (lds_void_t *)(dst + j * WAVE * 16), 16, 0, 0);
+    };
+
+    float acc[MS][4];
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            acc[s][r] = 0.0f;
+
+    auto compute = [&](int st) {
+        const uint8_t *stage = ring + st * SH::STAGE;
+        float *dxs = reinterpret_cast<float *>(ring + st * SH::STAGE + SH::DXOFF);
+        // d_x of the chunk's blocks as f32: dxs[b*8*MS + m], 0 past M
+#pragma unroll
+        for (int i = lane; i < CB * 8 * MS; i += WAVE) {
+            const int b = i / (8 * MS), m = i - (i / (8 * MS)) * (8 * MS);
+            const uint16_t bits = *reinterpret_cast<const uint16_t *>(
+                stage + SH::WPIECES * 16 + (m < M ? m : 0) * SH::XRUN + b * Q8_1_BYTES);
+            dxs[i] = (m < M) ? h2f(bits) : 0.0f;
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int G = 0; G < CB / 8; ++G) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int bl = 8 * G + j + 4 * hb; // this lane's block within the chunk
+                i32x4 A[MS];
+                float dx[MS][4];
+#pragma unroll
+                for (int s = 0; s < MS; ++s) {
+                    const uint32_t *xb =
+                        reinterpret_cast<const uint32_t *>(stage + aoff[s] + bl * Q8_1_BYTES);
+                    const int a0 = (int)xb[1 + 2 * h], a1 = (int)xb[2 + 2 * h];
+                    const int a2 = (int)xb[5 + 2 * h], a3 = (int)xb[6 + 2 * h];
+                    A[s][0] = a_on[s] ? a0 : 0;
+                    A[s][1] = a_on[s] ? a1 : 0;
+                    A[s][2] = a_on[s] ? a2 : 0;
+                    A[s][3] = a_on[s] ? a3 : 0;
+                    const float *dxp = dxs + bl * 8 * MS + 8 * s + 4 * h;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        dx[s][r] = dxp[r];
+                }
+                // block bl of staged row c16: d at byte o = 18*bl, qs at o + 2
+                const uint8_t *bp = stage + c16 * SH::RUN + Q4_0_BYTES * bl;
+                uint32_t x0, x1, dbits;
+                if (j & 1) { // o = 2 mod 4: qs 4-byte aligned, d in the high half before it
+                    const uint32_t *pw = reinterpret_cast<const uint32_t *>(bp - 2);
+                    dbits = pw[0] >> 16;
+                    x0 = pw[1 + 2 * h];
+                    x1 = pw[2 + 2 * h];
+                } else {     // o = 0 mod 4: d in the low half, qs start 2 bytes in
+                    const uint32_t *pw = reinterpret_cast<const uint32_t *>(bp);
+                    dbits = pw[0];
+                    const uint32_t a0 = pw[2 * h], a1 = pw[2 * h + 1], a2 = pw[2 * h + 2];
+                    x0 = __builtin_amdgcn_alignbyte(a1, a0, 2);
+                    x1 = __builtin_amdgcn_alignbyte(a2, a1, 2);
+                }
+                i32x4 B;
+                B[0] = (int)(((x0 << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
+                B[1] = (int)(((x1 << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
+                B[2] = (int)((x0 & 0xF0F0F0F0u) ^ 0x80808080u);
+                B[3] = (int)((x1 & 0xF0F0F0F0u) ^ 0x80808080u);
+                const float dw = h2f(dbits);
+#pragma unroll
+                for (int s = 0; s < MS; ++s) {
+                    const i32x4 D = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        A[s], B, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[s][r] = fmaf((float)D[r], dw * dx[s][r], acc[s][r]);
+                }
+            }
+        }
+        wave_lds_sync();
+    };
+
+    // Chunks wave, wave+S, ...; the wave's k-th chunk lives in stage k % NST.
+    // The compiler does not order LDS reads after these DMA loads, so the
+    // wait is explicit: before computing chunk k, exactly (NST-1)*LOADS
+    // younger DMA instructions (chunks k+1 .. k+NST-1) may still be
+    // outstanding and every older one -- chunk k's -- must have landed.
+    constexpr int YOUNGER = (NST - 1) * LOADS;
+    static_assert(YOUNGER <= 63, "vmcnt field");
+    constexpr int WAIT_IMM = (YOUNGER & 0xF) | (0x7 << 4) | (0xF << 8) | ((YOUNGER >> 4) << 14);
+    const int nchunks = nb / CB;
+    if (wave < nchunks) {
+        const int mine = (nchunks - wave + S - 1) / S; // this wave's chunk count
+#pragma unroll
+        for (int k = 0; k < NST - 1; ++k)
+            issue(wave + S * (k < mine ? k : mine - 1), k);
+        for (int k = 0; k < mine; ++k) {
+            const int kn = k + NST - 1;
+            issue(wave + S * (kn < mine ? kn : mine - 1), kn % NST);
+            __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+            compute(k % NST);
+        }
+    }
+
+    // the two chunk halves (lanes l and l+32), then the S waves in order
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            acc[s][r] += __shfl_xor(acc[s][r], 32, 64);
+    __builtin_amdgcn_s_waitcnt(0); // no load may still be writing the LDS reused below
+    __syncthreads();
+    constexpr int SLOTS = MS * 4;
+    float *partial = reinterpret_cast<float *>(smem); // [S][SLOTS][32]
+    if (lane < 32) {
+#pragma unroll
+        for (int s = 0; s < MS; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                partial[(wave * SLOTS + s * 4 + r) * 32 + lane] = acc[s][r];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x) {
+        const int slot = idx >> 5, l = idx & 31;
+        const int s = slot >> 2, r = slot & 3;
+        const int m = 8 * s + 4 * (l >> 4) + r;
+        const int nn = n0 + (l & 15);
+        float sacc = 0.0f;
+        for (int v = 0; v < S; ++v)
+            sacc += partial[(v * SLOTS + slot) * 32 + l];
+        if (m < M && nn < N)
+            y[(size_t)m * N + nn] = sacc * 0.0625f;
+    }
+}
+
+// Waves per workgroup of the dot4 kernel: enough workgroups x waves to give
+// every CU several waves, never more waves than K-units, at most 16 waves
+// (1024 threads: 16 x 9216 bytes of staging fit gfx950's 160 KB of LDS), and
 // at most 128 partial rows of LDS (S * M <= 128).
-static int pick_splits(int64_t N, int64_t units, int M)
+static int pick_splits(int64_t N, int64_t units, int M, int64_t lds_limit, bool staged)
 {
     const int64_t tiles = (N + WAVE - 1) / WAVE;
     const int64_t target_waves = 256 * 8;
@@ -171,7 +466,62 @@ static int pick_splits(int64_t N, int64_t units, int M)
         s = units;
     if (s > 128 / M)
         s = 128 / M;
+    if (staged && s > lds_limit / STAGE_BYTES)
+        s = lds_limit / STAGE_BYTES;
     return (int)(s < 1 ? 1 : s);
+}
+
+// Largest dynamic LDS a workgroup may use on the current device (queried
+// once; 160 KB on gfx950).
+static int64_t lds_limit()
+{
+    static int64_t cached = -1;
+    if (cached < 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            v <= 0)
+            v = 65536;
+        cached = v;
+    }
+    return cached;
+}
+
+// Waves per workgroup for the MFMA kernel: four (measured best on the
+// ffn_up and down shapes for every M, against 1..8), fewer when the row has
+// fewer chunks or LDS cannot hold four rings.
+template <int M, int CB, int NST>
+static int mfma_waves(int64_t N, int nb, int64_t limit)
+{
+    (void)N;
+    int64_t s = 4;
+    if (s > nb / CB)
+        s = nb / CB;
+    while (s > 1 && s * MfmaShape<M, CB, NST>::WAVE_LDS > limit)
+        --s;
+    return (int)(s < 1 ? 1 : s);
+}
+
+template <int M, int CB, int NST>
+static bq8_status launch_mfma(const void *w, int64_t N, int nb, const void *xq, float *y,
+                              hipStream_t stream, int64_t limit, int waves)
+{
+    using SH = MfmaShape<M, CB, NST>;
+    const int64_t tiles = (N + 15) / 16;
+    const int s = waves > 0 ? waves : mfma_waves<M, CB, NST>(N, nb, limit);
+    const int64_t ring = (int64_t)s * SH::WAVE_LDS;
+    const int64_t partial = (int64_t)s * SH::MS * 4 * 32 * (int64_t)sizeof(float);
+    const int64_t lds = ring > partial ? ring : partial;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)q4_0_mmvq_mfma_kernel<M, CB, NST>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit) != hipSuccess)
+            return BQ8_ERR_HIP;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((q4_0_mmvq_mfma_kernel<M, CB, NST>), dim3((unsigned)tiles), dim3(WAVE * s),
+                       (size_t)lds, stream, (const uint8_t *)w, (int)N, nb, (const uint8_t *)xq, y);
+    return launch_status();
 }
 
 template <int M>
@@ -181,23 +531,45 @@ static bq8_status mmvq_launch(const void *w, int64_t N, int64_t K, const void *x
     if (!w || !xq || !y)
         return BQ8_ERR_NULL;
     if (N < 1 || N >= (int64_t(1) << 31) || K < QK || K % QK != 0 ||
-        N * (K / QK) * Q4_0_BYTES >= (int64_t(1) << 40) || K / QK >= (int64_t(1) << 31) ||
+        N * (K / QK) * Q4_0_BYTES >= (int64_t(1) << 40) || K > (int64_t(1) << 26) ||
         (int64_t)M * K >= (int64_t(1) << 31))
         return BQ8_ERR_SHAPE;
     if (!aligned(w, 16) || !aligned(xq, 4) || !aligned(y, 4))
         return BQ8_ERR_ALIGN;
     const int nb = (int)(K / QK);
     const bool al = (K % 256 == 0);
-    const int S = pick_splits(N, al ? nb / 8 : nb, M);
+    const int64_t limit = lds_limit();
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    {
+        // MFMA path for K a multiple of 256: the longest chunk (32, 16 or 8
+        // blocks) that divides the row
+        // 8-block chunks; a ring of two stages up to M = 6, three above
+        // (measured on the ffn_up and down shapes)
+        constexpr int NST = M <= 6 ? 2 : 3;
+        if (al && MfmaShape<M, 8, NST>::WAVE_LDS <= limit)
+            return launch_mfma<M, 8, NST>(w, N, nb, xq, y, s, limit, 0);
+    }
+    const int64_t dlimit = al ? limit : 65536;
+    const int S = pick_splits(N, al ? nb / 8 : nb, M, dlimit, al);
     const dim3 grid((unsigned)((N + WAVE - 1) / WAVE));
     const dim3 block(WAVE * S);
-    const size_t lds = (size_t)S * M * WAVE * sizeof(float);
-    (void)hipGetLastError();
-    if (al)
-        hipLaunchKernelGGL((q4_0_mmvq_dot4_kernel<M, true>), grid, block, lds, (hipStream_t)stream,
+    const size_t partial_bytes = (size_t)S * M * WAVE * sizeof(float);
+    const size_t stage_bytes = al ? (size_t)S * STAGE_BYTES : 0;
+    const size_t lds = partial_bytes > stage_bytes ? partial_bytes : stage_bytes;
+    if (al) {
+        static bool attr_set = false;
+        if (!attr_set) {
+            if (hipFuncSetAttribute((const void *)q4_0_mmvq_dot4_kernel<M, true>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)limit) != hipSuccess)
+                return BQ8_ERR_HIP;
+            attr_set = true;
+        }
+        hipLaunchKernelGGL((q4_0_mmvq_dot4_kernel<M, true>), grid, block, lds, s,
                            (const uint8_t *)w, (int)N, nb, (const uint8_t *)xq, y);
-    else
-        hipLaunchKernelGGL((q4_0_mmvq_dot4_kernel<M, false>), grid, block, lds, (hipStream_t)stream,
+    } else
+        hipLaunchKernelGGL((q4_0_mmvq_dot4_kernel<M, false>), grid, block, lds, s,
                            (const uint8_t *)w, (int)N, nb, (const uint8_t *)xq, y);
     return launch_status();
 }

@@ -12,9 +12,11 @@
 // Formats: include/bq8.h.
 //
 // Top-1 mapping on gfx950: lane <-> vocabulary row n (64 rows per wave,
-// 4 waves per workgroup, grid-stride over 64-row tiles).  A lane streams its
-// row of the pack in 128-byte runs (eight 128-bit loads), and the R quantized
-// activation rows -- identical for every lane -- come through scalar loads.
+// 4 waves per workgroup, grid-stride over 64-row tiles).  The wave loads each
+// 128-byte run of its 64 rows' quants with whole-cache-line loads (eight
+// lanes per row), passes it through LDS, and every lane reads back its own
+// row; the R quantized activation rows -- identical for every lane -- come
+// through scalar loads.
 // Per 32 values and activation row: 8 x v_dot4 give the two 16-value integer
 // dots, which the two int8 subscales combine exactly in int32; the result is
 // scaled by d_w * d_x (exact in binary32) and accumulated in binary32, in the
@@ -117,16 +119,28 @@ __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restr
         *counter = 0u;
 }
 
+// Order this wave's LDS writes before its reads of other lanes' data.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int PIECE_ROW_STRIDE = 144; // 128 bytes of quants + 16 of padding per staged row
+
 template <int R>
 __global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_kernel(
     const int8_t *__restrict__ Q, const int8_t *__restrict__ SC, const uint16_t *__restrict__ D,
     int N, int K, const uint8_t *__restrict__ xq, uint64_t *__restrict__ slots,
     uint32_t *__restrict__ counter, int32_t *__restrict__ ids)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[TOP1_WAVES][WAVE * PIECE_ROW_STRIDE];
     __shared__ uint64_t wave_best[TOP1_WAVES][R];
     __shared__ uint32_t is_last;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint8_t *stage = stage_all[wave];
     const int nb = K / QK;
     const int nsb = K / QK_K;
     const int ntiles = (N + WAVE - 1) / WAVE;
@@ -137,55 +151,98 @@ __global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_kernel(
         best[r] = 0;
 
     for (int t = blockIdx.x * TOP1_WAVES + wave; t < ntiles; t += gridDim.x * TOP1_WAVES) {
-        const int n_raw = t * WAVE + lane;
+        const int n0 = t * WAVE;
+        const int n_raw = n0 + lane;
         const int n = n_raw < N ? n_raw : N - 1; // loads stay in bounds
-        const int8_t *qrow = Q + (size_t)n * K;
+        // A 128-byte run of the quant plane for the tile's 64 rows is 512
+        // pieces of 16 bytes; load j brings pieces 64j..64j+63, i.e. rows
+        // 8j..8j+7 with eight lanes per row: eight whole 128-byte lines.
+        const int8_t *tile = Q + (size_t)n0 * K;
+        uint32_t goff[8];
+        uint32_t soff[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * j + (lane >> 3);
+            const int rr = (n0 + r < N) ? r : (N - 1 - n0);
+            goff[j] = (uint32_t)rr * (uint32_t)K + 16u * (uint32_t)(lane & 7);
+            soff[j] = (uint32_t)r * PIECE_ROW_STRIDE + 16u * (uint32_t)(lane & 7);
+        }
         const int8_t *srow = SC + (size_t)n * (K / 16);
         const uint16_t *drow = D + (size_t)n * nsb;
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r)
             acc[r] = 0.0f;
-        for (int sb = 0; sb < nsb; ++sb) {
-            const u32x4 scw = *reinterpret_cast<const u32x4 *>(srow + sb * 16);
-            const float dw = h2f(drow[sb]);
+
+        auto load_half = [&](u32x4(&v)[8], int sb, int half) {
+            const int8_t *src = tile + sb * QK_K + half * 128;
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const u32x4 *p = reinterpret_cast<const u32x4 *>(qrow + sb * QK_K + half * 128);
-                uint32_t wq[32];
+            for (int j = 0; j < 8; ++j)
+                v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + goff[j]));
+        };
+        auto compute_half = [&](const u32x4(&v)[8], int sb, int half, const u32x4 &scw, float dw) {
+            wave_lds_sync();
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const u32x4 v = __builtin_nontemporal_load(p + i);
-                    wq[4 * i + 0] = v[0];
-                    wq[4 * i + 1] = v[1];
-                    wq[4 * i + 2] = v[2];
-                    wq[4 * i + 3] = v[3];
-                }
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<u32x4 *>(stage + soff[j]) = v[j];
+            wave_lds_sync();
+            uint32_t wq[32];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    // 32-block b = sb*8 + half*4 + j uses subscales 2*(half*4+j) and +1
-                    const int sbi = 2 * (half * 4 + j);
-                    const uint32_t scword = scw[sbi >> 2];
-                    const int sca = __builtin_amdgcn_sbfe(scword, 8 * (sbi & 3), 8);
-                    const int scb = __builtin_amdgcn_sbfe(scword, 8 * ((sbi & 3) + 1), 8);
-                    const int b = sb * 8 + half * 4 + j;
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 x4 =
+                    *reinterpret_cast<const u32x4 *>(stage + lane * PIECE_ROW_STRIDE + 16 * i);
+                wq[4 * i + 0] = x4[0];
+                wq[4 * i + 1] = x4[1];
+                wq[4 * i + 2] = x4[2];
+                wq[4 * i + 3] = x4[3];
+            }
 #pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const uint32_t *xb = reinterpret_cast<const uint32_t *>(
-                            xq + ((size_t)r * nb + b) * Q8_1_BYTES);
-                        int sa = dot4((int)wq[8 * j + 0], (int)xb[1], 0);
-                        sa = dot4((int)wq[8 * j + 1], (int)xb[2], sa);
-                        sa = dot4((int)wq[8 * j + 2], (int)xb[3], sa);
-                        sa = dot4((int)wq[8 * j + 3], (int)xb[4], sa);
-                        int sbv = dot4((int)wq[8 * j + 4], (int)xb[5], 0);
-                        sbv = dot4((int)wq[8 * j + 5], (int)xb[6], sbv);
-                        sbv = dot4((int)wq[8 * j + 6], (int)xb[7], sbv);
-                        sbv = dot4((int)wq[8 * j + 7], (int)xb[8], sbv);
-                        const int I = sa * sca + sbv * scb;
-                        acc[r] = fmaf((float)I, dw * h2f(xb[0]), acc[r]);
-                    }
+            for (int j = 0; j < 4; ++j) {
+                // 32-block b = sb*8 + half*4 + j uses subscales 2*(half*4+j) and +1
+                const int sbi = 2 * (half * 4 + j);
+                const uint32_t scword = scw[sbi >> 2];
+                const int sca = __builtin_amdgcn_sbfe(scword, 8 * (sbi & 3), 8);
+                const int scb = __builtin_amdgcn_sbfe(scword, 8 * ((sbi & 3) + 1), 8);
+                const int b = sb * 8 + half * 4 + j;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t *xb = reinterpret_cast<const uint32_t *>(
+                        xq + ((size_t)r * nb + b) * Q8_1_BYTES);
+                    int sa = dot4((int)wq[8 * j + 0], (int)xb[1], 0);
+                    sa = dot4((int)wq[8 * j + 1], (int)xb[2], sa);
+                    sa = dot4((int)wq[8 * j + 2], (int)xb[3], sa);
+                    sa = dot4((int)wq[8 * j + 3], (int)xb[4], sa);
+                    int sbv = dot4((int)wq[8 * j + 4], (int)xb[5], 0);
+                    sbv = dot4((int)wq[8 * j + 5], (int)xb[6], sbv);
+                    sbv = dot4((int)wq[8 * j + 6], (int)xb[7], sbv);
+                    sbv = dot4((int)wq[8 * j + 7], (int)xb[8], sbv);
+                    const int I = sa * sca + sbv * scb;
+                    acc[r] = fmaf((float)I, dw * h2f(xb[0]), acc[r]);
                 }
             }
+        };
+
+        // Both halves of the next superblock are in flight while one is
+        // computed.  Loads are issued without branches (a wait-count join
+        // after a skipped load would make later waits conservative): after
+        // the last superblock the prefetch repeats its addresses (cache hits,
+        // never used).
+        u32x4 va[8], vb[8];
+        load_half(va, 0, 0);
+        load_half(vb, 0, 1);
+        u32x4 scw = *reinterpret_cast<const u32x4 *>(srow);
+        uint32_t dbits = drow[0];
+        for (int sb = 0; sb < nsb; ++sb) {
+            const int sbn = (sb + 1 < nsb) ? sb + 1 : sb;
+            const u32x4 scw_next = *reinterpret_cast<const u32x4 *>(srow + sbn * 16);
+            const uint32_t dbits_next = drow[sbn];
+            const float dw = h2f(dbits);
+            compute_half(va, sb, 0, scw, dw);
+            load_half(va, sbn, 0);
+            compute_half(vb, sb, 1, scw, dw);
+            load_half(vb, sbn, 1);
+            scw = scw_next;
+            dbits = dbits_next;
         }
         if (n_raw < N) {
 #pragma unroll

@@ -94,7 +94,7 @@ bq8_status q8_1_quantize(const float *x, int64_t M, int64_t K, void *xq, void *s
  * w:  Q4_0 [N][K/32] blocks of 18 bytes, row-major, 16-byte aligned.
  * xq: Q8_1 [M][K/32] (from q8_1_quantize), 4-byte aligned.
  * y:  f32 [M][N] row-major, 4-byte aligned; fully overwritten.
- * Shape: 1 <= N < 2^31, K >= 32, K % 32 == 0, N*K/32*18 < 2^40.
+ * Shape: 1 <= N < 2^31, 32 <= K <= 2^26, K % 32 == 0, N*K/32*18 < 2^40.
  * Each weight byte is read from memory once per call whatever M is.
  * Accumulation is binary32 over exact per-block integer dots, in a fixed
  * order: results are bitwise reproducible run to run, and equal weight rows
@@ -125,8 +125,8 @@ bq8_status q4_0_mmvq(const void *w, int64_t N, int64_t K, const void *xq, int64_
 /* ------------------------------------------------------------------------
  * Q6_K expansion (run once, at load time).  The fused-head page expands the
  * output tensor once into signed int8 quants, int8 subscales and fp16
- * superblock scales ("Why this was slow") and requires "the exact expected
- * layout and byte count" of the pack ("Exactness and safety contracts").
+ * superblock scales ("Why this was slow") and accepts the pack only with its
+ * exact layout and size ("Exactness and safety contracts").
  * q6k_pack_bytes: host; N*K + N*K/16 + 2*N*K/256, or -1 if the shape is
  * invalid.  [248320 x 5120] gives 1,360,793,600 ("Memory and startup").
  * raw:  Q6_K [N][K/256] superblocks of 210 bytes, row-major, 2-byte aligned.

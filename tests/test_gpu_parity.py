@@ -93,8 +93,34 @@ def test_q8_1_quantize_bitexact(case):
     assert (xq == oracle.q8_1_quantize(x)).all()
 
 
+def test_q8_1_s_field_double_rounding_regression():
+    """s is d*sum(q) rounded to binary32 and then to fp16.  Blocks where a
+    single rounding of the exact product to fp16 would differ are rare; find
+    some on the CPU and check the GPU rounds them twice like the oracle."""
+    rng = np.random.default_rng(102)
+    x = (rng.standard_normal((8192, 1024)) * rng.uniform(0.01, 50, (8192, 1))).astype(np.float32)
+    xq = oracle.q8_1_quantize(x)
+    d, s, q = oracle.q8_1_fields(xq)
+    d32 = (np.abs(x.reshape(-1, 32)).max(axis=1) / np.float32(127)).astype(np.float32)
+    qs = q.astype(np.int64).sum(axis=1)
+    once = (d32.astype(np.float64) * qs).astype(np.float16).view(np.uint16)
+    hits = np.where(once != s)[0]
+    assert len(hits) >= 8, "expected some double-rounding blocks in the sample"
+    xs = np.ascontiguousarray(x.reshape(-1, 32)[hits].reshape(1, -1))
+    say(f"q8_1 double-rounding blocks: {len(hits)}")
+    got = host(bq.q8_1_quantize(dev(xs)))
+    assert (got == oracle.q8_1_quantize(xs)).all()
+    # the same blocks through the fused SiLU*up path: g large so SiLU(g) = g
+    g = np.full_like(xs, 100.0)
+    u = xs / np.float32(100.0)
+    h = torch.empty(xs.shape, dtype=torch.float32, device=DEV)
+    hq = host(bq.silu_mul_q8_1(dev(g), dev(u), h=h))
+    assert (hq == oracle.q8_1_quantize(host(h))).all()
+
+
 # ------------------------------------------------------------------ Q4_0
-SMALL_SHAPES = [(200, 512), (70, 96), (1, 32), (64, 256), (130, 1024), (333, 2304)]
+SMALL_SHAPES = [(200, 512), (70, 96), (1, 32), (64, 256), (130, 1024), (333, 2304),
+                (16390, 512), (33000, 256)]
 
 
 @pytest.mark.parametrize("N,K", SMALL_SHAPES)
