@@ -12,10 +12,11 @@ weight from HBM; inputs are resident in device memory before timing starts.
 Printed: one JSON line with the effective weight bandwidth of a step
 (value, GB/s), the mmvq kernel's roofline against the 8 TB/s HBM peak, the
 fused Q6_K LM-head top-1 time on the lm_head workload, the per-M times of the
-down_sweep workload, and the oracle's CPU throughput on a bounded sample.
+down_sweep workload, ms per full width-6 pass of the 64-layer verifier FFN
+stream (q4_0_ffn_stream), and the oracle's CPU throughput on a bounded sample.
 
 Profiling helpers (one kernel family per process, for rocprofv3):
-    python bench.py --profile-target mmvq_m6|lmhead_top1|down_sweep|copy [--reps R]
+    python bench.py --profile-target mmvq_m6|lmhead_top1|down_sweep|stream|copy [--reps R]
 """
 from __future__ import annotations
 
@@ -150,6 +151,31 @@ def time_down_sweep(torch, bq, synth, reps):
     return out
 
 
+def time_stream(torch, bq, synth, passes):
+    """ms per full width-6 pass of the 64-layer verifier FFN stream (weights
+    generated on the device, 9.6 GB, far beyond the caches); median, p10 and
+    p90 over `passes` passes, each bracketed by its own HIP events."""
+    cfg = synth.STREAM
+    L, M, H, F = cfg["layers"], cfg["M"], cfg["hidden"], cfg["ffn"]
+    wg, wu, wd = synth.stream_weights_device(L, H, F)
+    tables = tuple(bq.stream_weight_table(ws) for ws in (wg, wu, wd))
+    x0 = torch.from_numpy(synth.stream_x0()).to("cuda")
+    y, work = bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, tables=tables)
+    for _ in range(2):
+        bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, y=y, work=work, tables=tables)
+    ms = []
+    for _ in range(passes):
+        with Timer(torch) as t:
+            bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, y=y, work=work, tables=tables)
+        ms.append(t.ms)
+    wbytes = L * (2 * q4_0_bytes(F, H) + q4_0_bytes(H, F))
+    med = float(np.median(ms))
+    return {"layers": L, "M": M, "hidden": H, "ffn": F, "passes": passes,
+            "ms_median": round(med, 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
+            "ms_p90": round(float(np.percentile(ms, 90)), 4), "weight_bytes": wbytes,
+            "GBps": round(wbytes / med / 1e6, 1), "launches_per_pass": 5 * L}
+
+
 def cpu_baseline(synth, budget_s=10.0):
     """The oracle, as written, on the full ffn_up workload, repeated for
     about budget_s seconds of wall time on the host's cores."""
@@ -211,6 +237,8 @@ def profile_target(torch, bq, synth, target, reps):
                                s["scratch"])
     elif target == "down_sweep":
         time_down_sweep(torch, bq, synth, reps)
+    elif target == "stream":
+        time_stream(torch, bq, synth, reps)
     torch.cuda.synchronize()
     log(f"{target}: done")
 
@@ -270,6 +298,10 @@ def main():
     sweep = time_down_sweep(torch, bq, synth, 100)
     log(f"bench: sweep {sweep}")
 
+    log("bench: stream")
+    stream = time_stream(torch, bq, synth, 20)
+    log(f"bench: stream {stream['ms_median']:.3f} ms per pass, {stream['GBps']} GB/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
@@ -303,6 +335,7 @@ def main():
             "lmhead_pack_bytes": pack_bytes,
             "lmhead_GBps": round(pack_bytes / lm_us / 1e3, 1),
             "down_sweep": sweep,
+            "stream_64_layer_pass": stream,
             "device": torch.cuda.get_device_name(0),
         },
         "roofline": {

@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
         L.silu_mul_q8_1.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
         L.rms_norm_q8_1.restype = _ST
         L.rms_norm_q8_1.argtypes = [_P, _I64, _I64, ctypes.c_float, _P, _P, _P]
+        L.q4_0_ffn_stream_layout.restype = _ST
+        L.q4_0_ffn_stream_layout.argtypes = [_I64, _I64, _I64, ctypes.POINTER(_I64)]
+        L.q4_0_ffn_stream.restype = _ST
+        L.q4_0_ffn_stream.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_float, _P,
+                                      _P, _I64, _P]
         _lib = L
     return _lib
 
@@ -233,7 +238,65 @@ def rms_norm_q8_1(y: torch.Tensor, eps: float, xq: torch.Tensor | None = None,
     return xq
 
 
+# ------------------------------------------------------- verifier stream
+def q4_0_ffn_stream_layout(M: int, hidden: int, ffn: int) -> dict:
+    """Byte offsets of the stage buffers in the stream workspace and its size."""
+    off = (ctypes.c_int64 * 5)()
+    _check("q4_0_ffn_stream_layout", lib().q4_0_ffn_stream_layout(M, hidden, ffn, off))
+    return dict(xq=off[0], g=off[1], u=off[2], hq=off[3], total=off[4])
+
+
+def stream_weight_table(ws) -> ctypes.Array:
+    """Host array of the device addresses of a list of weight tensors."""
+    return (ctypes.c_void_p * len(ws))(*[_dev(w, "weight", torch.uint8) for w in ws])
+
+
+def q4_0_ffn_stream(w_gate, w_up, w_down, x0: torch.Tensor, eps: float,
+                    y: torch.Tensor | None = None, work: torch.Tensor | None = None,
+                    tables=None):
+    """Enqueue a whole verifier FFN pass over len(w_gate) layers.
+
+    w_gate/w_up: Q4_0 uint8 [ffn][hidden/32*18] per layer; w_down: Q4_0 uint8
+    [hidden][ffn/32*18]; x0: f32 [M][hidden].  Returns (y, work); the stage
+    buffers of the last layer are views of work (see stream_stages).
+    ``tables`` may hold the three prebuilt stream_weight_table arrays."""
+    M, hidden = x0.shape
+    layers = len(w_gate)
+    if layers < 1 or len(w_up) != layers or len(w_down) != layers:
+        raise ValueError("w_gate, w_up and w_down must list the same number of layers (>= 1)")
+    ffn, k = _q4_0_shape(w_gate[0])
+    if k != hidden:
+        raise ValueError("gate weights must have K = hidden")
+    for w in (*w_gate, *w_up):
+        if _q4_0_shape(w) != (ffn, hidden):
+            raise ValueError("every gate/up weight must be Q4_0 [ffn][hidden/32]")
+    for w in w_down:
+        if _q4_0_shape(w) != (hidden, ffn):
+            raise ValueError("every down weight must be Q4_0 [hidden][ffn/32]")
+    lay = q4_0_ffn_stream_layout(M, hidden, ffn)
+    y = _out(y, (M, hidden), torch.float32, x0.device, "y")
+    work = _out(work, (lay["total"],), torch.uint8, x0.device, "work")
+    tg, tu, td = tables if tables is not None else (
+        stream_weight_table(w_gate), stream_weight_table(w_up), stream_weight_table(w_down))
+    _check("q4_0_ffn_stream", lib().q4_0_ffn_stream(
+        tg, tu, td, layers, M, hidden, ffn, _dev(x0, "x0", torch.float32), float(eps),
+        _dev(y, "y", torch.float32), _dev(work, "work", torch.uint8), work.numel(), _stream()))
+    return y, work
+
+
+def stream_stages(work: torch.Tensor, M: int, hidden: int, ffn: int) -> dict:
+    """Views of the last layer's stage buffers inside a stream workspace."""
+    lay = q4_0_ffn_stream_layout(M, hidden, ffn)
+    nq_h, nq_f = hidden // QK * Q8_1_BYTES, ffn // QK * Q8_1_BYTES
+    return dict(
+        xq=work[lay["xq"]:lay["xq"] + M * nq_h].view(M, nq_h),
+        g=work[lay["g"]:lay["g"] + 4 * M * ffn].view(torch.float32).view(M, ffn),
+        u=work[lay["u"]:lay["u"] + 4 * M * ffn].view(torch.float32).view(M, ffn),
+        hq=work[lay["hq"]:lay["hq"] + M * nq_f].view(M, nq_f))
+
+
 __all__ = ["Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "q4_0_mmvq",
            *[f"q4_0_mmvq_m{m}" for m in range(1, MAX_M + 1)], "q6k_pack_bytes",
            "q6k_pack_expand", "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1",
-           "silu_mul_q8_1", "rms_norm_q8_1", "synth"]
+           "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_ffn_stream_layout", "q4_0_ffn_stream",
+           "stream_weight_table", "stream_stages", "synth"]

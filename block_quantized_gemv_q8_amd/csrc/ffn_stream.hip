@@ -1,0 +1,106 @@
+// Width-6 verifier FFN stream: a chain of layers, each a Q4_0 gate and up
+// projection sharing one Q8_1 activation, SiLU(gate)*up requantized to Q8_1
+// on the device, and a Q4_0 down projection whose output becomes the next
+// layer's input through an RMS step and a Q8_1 quantize.
+//
+// "Qwen3.6 27B Q4_0 DFlash/SYCL closure": offline-packed width-6 gate/up and
+// down projections carry the target verifier ("What materially worked");
+// the down-to-next-RMS/Q8 boundary ("Closed or negative paths").
+// "Qwen3.6 27B B70 follow-up: Q8 activation cache, FP8 artifacts, MTP
+// blocker", "Q8_1 activation cache prototype": gate and up read the same
+// quantized activation.
+//
+// The whole pass is enqueued from native code: five launches per layer on
+// the caller's stream, no host synchronization, no allocation.  Every shape
+// and every layer's pointers are validated before the first launch, so a
+// rejected call enqueues nothing.
+#include "bq8_dev.h"
+
+namespace bq8 {
+
+static int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+// Offsets of the stage buffers inside the caller's workspace.
+struct StreamLayout {
+    int64_t xq, g, u, hq, total;
+};
+
+static bool stream_layout(int64_t M, int64_t hidden, int64_t ffn, StreamLayout *L)
+{
+    if (M < 1 || M > 17 || hidden < QK || hidden % QK != 0 || ffn < QK || ffn % QK != 0 ||
+        hidden > 32768 || ffn > (int64_t(1) << 26) ||
+        M * hidden >= (int64_t(1) << 31) || M * ffn >= (int64_t(1) << 31))
+        return false;
+    L->xq = 0;
+    L->g = align256(M * (hidden / QK) * Q8_1_BYTES);
+    L->u = L->g + align256(M * ffn * 4);
+    L->hq = L->u + align256(M * ffn * 4);
+    L->total = L->hq + align256(M * (ffn / QK) * Q8_1_BYTES);
+    return true;
+}
+
+} // namespace bq8
+
+using namespace bq8;
+
+BQ8_EXPORT bq8_status q4_0_ffn_stream_layout(int64_t M, int64_t hidden, int64_t ffn,
+                                             int64_t *offsets)
+{
+    if (!offsets)
+        return BQ8_ERR_NULL;
+    StreamLayout L;
+    if (!stream_layout(M, hidden, ffn, &L))
+        return BQ8_ERR_SHAPE;
+    offsets[0] = L.xq;
+    offsets[1] = L.g;
+    offsets[2] = L.u;
+    offsets[3] = L.hq;
+    offsets[4] = L.total;
+    return BQ8_OK;
+}
+
+BQ8_EXPORT bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *const *w_up,
+                                      const void *const *w_down, int64_t layers, int64_t M,
+                                      int64_t hidden, int64_t ffn, const float *x0, float eps,
+                                      float *y, void *work, int64_t work_bytes, void *stream)
+{
+    if (!w_gate || !w_up || !w_down || !x0 || !y || !work)
+        return BQ8_ERR_NULL;
+    StreamLayout L;
+    if (layers < 1 || layers > (int64_t(1) << 20) || !stream_layout(M, hidden, ffn, &L) ||
+        !(eps > 0.0f) || ffn * (hidden / QK) * Q4_0_BYTES >= (int64_t(1) << 40))
+        return BQ8_ERR_SHAPE;
+    for (int64_t l = 0; l < layers; ++l) {
+        if (!w_gate[l] || !w_up[l] || !w_down[l])
+            return BQ8_ERR_NULL;
+        if (!aligned(w_gate[l], 16) || !aligned(w_up[l], 16) || !aligned(w_down[l], 16))
+            return BQ8_ERR_ALIGN;
+    }
+    if (!aligned(x0, 4) || !aligned(y, 4) || !aligned(work, 256))
+        return BQ8_ERR_ALIGN;
+    if (work_bytes < L.total)
+        return BQ8_ERR_SIZE;
+
+    uint8_t *base = static_cast<uint8_t *>(work);
+    void *xq = base + L.xq;
+    float *g = reinterpret_cast<float *>(base + L.g);
+    float *u = reinterpret_cast<float *>(base + L.u);
+    void *hq = base + L.hq;
+
+    // Everything below was validated above; a nonzero status can only be a
+    // launch failure, reported as is.
+    bq8_status st = q8_1_quantize(x0, M, hidden, xq, stream);
+    for (int64_t l = 0; l < layers && st == BQ8_OK; ++l) {
+        if (l > 0)
+            st = rms_norm_q8_1(y, M, hidden, eps, nullptr, xq, stream);
+        if (st == BQ8_OK)
+            st = q4_0_mmvq(w_gate[l], ffn, hidden, xq, M, g, stream);
+        if (st == BQ8_OK)
+            st = q4_0_mmvq(w_up[l], ffn, hidden, xq, M, u, stream);
+        if (st == BQ8_OK)
+            st = silu_mul_q8_1(g, u, M, ffn, nullptr, hq, stream);
+        if (st == BQ8_OK)
+            st = q4_0_mmvq(w_down[l], hidden, ffn, hq, M, y, stream);
+    }
+    return st;
+}

@@ -48,11 +48,18 @@ __global__ __launch_bounds__(256) void silu_mul_q8_1_kernel(const float *__restr
     q8_1_block_store(v, j, valid, hq + (size_t)blk * Q8_1_BYTES);
 }
 
-// One workgroup per row: sum of squares with a fixed reduction tree
-// (per-thread strided partials, then a wave butterfly, then the waves in
-// index order), so the result does not depend on scheduling.
-constexpr int RMS_THREADS = 256;
+// One workgroup of 1024 threads per row.  The 32 groups of 32 lanes own
+// blocks g, g + 32, g + 64, ... (VPT blocks each); every thread loads its
+// VPT values once, up front, into registers, so the row costs one memory
+// round trip.  Sum of squares with a fixed reduction tree (per-thread
+// partials in block order, a wave butterfly, the 16 waves in index order),
+// so the result does not depend on scheduling; then each group quantizes its
+// blocks from the registers.
+constexpr int RMS_THREADS = 1024;
+constexpr int RMS_GROUPS = RMS_THREADS / QK;
+constexpr int RMS_MAX_K = RMS_GROUPS * 32 * QK; // 32 blocks per group
 
+template <int VPT>
 __global__ __launch_bounds__(RMS_THREADS) void rms_norm_q8_1_kernel(const float *__restrict__ y,
                                                                     int K, float eps,
                                                                     float *__restrict__ x,
@@ -60,12 +67,20 @@ __global__ __launch_bounds__(RMS_THREADS) void rms_norm_q8_1_kernel(const float 
 {
     __shared__ float wave_sums[RMS_THREADS / WAVE];
     const int m = blockIdx.x;
+    const int nb = K / QK;
+    const int grp = threadIdx.x >> 5;
+    const int j = threadIdx.x & 31;
     const float *row = y + (size_t)m * K;
-    float ss = 0.0f;
-    for (int k = threadIdx.x; k < K; k += RMS_THREADS) {
-        const float v = row[k];
-        ss = fmaf(v, v, ss);
+    float v[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int b = grp + RMS_GROUPS * i;
+        v[i] = b < nb ? row[b * QK + j] : 0.0f;
     }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+        ss = fmaf(v[i], v[i], ss);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         ss += __shfl_xor(ss, off, 64);
@@ -78,22 +93,26 @@ __global__ __launch_bounds__(RMS_THREADS) void rms_norm_q8_1_kernel(const float 
         tot += wave_sums[w];
     const float inv = 1.0f / sqrtf(tot / (float)K + eps);
 
-    const int nb = K / QK;
     uint8_t *out = xq + (size_t)m * nb * Q8_1_BYTES;
-    // 256 threads = 8 groups of 32 lanes; group g handles blocks g, g+8, ...
-    const int grp = threadIdx.x >> 5;
-    const int j = threadIdx.x & 31;
-    for (int b0 = 0; b0 < nb; b0 += RMS_THREADS / QK) {
-        const int b = b0 + grp;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int b = grp + RMS_GROUPS * i;
+        if (b - grp >= nb) // no group has a block this far (uniform per workgroup)
+            break;
         const bool valid = b < nb;
-        float v = 0.0f;
-        if (valid) {
-            v = row[b * QK + j] * inv;
-            if (x)
-                x[(size_t)m * K + b * QK + j] = v;
-        }
-        q8_1_block_store(v, j, valid, out + (size_t)b * Q8_1_BYTES);
+        const float val = v[i] * inv;
+        if (valid && x)
+            x[(size_t)m * K + b * QK + j] = val;
+        q8_1_block_store(val, j, valid, out + (size_t)b * Q8_1_BYTES);
     }
+}
+
+template <int VPT>
+static void launch_rms(const float *y, int64_t M, int64_t K, float eps, float *x, void *xq,
+                       hipStream_t s)
+{
+    hipLaunchKernelGGL(rms_norm_q8_1_kernel<VPT>, dim3((unsigned)M), dim3(RMS_THREADS), 0, s, y,
+                       (int)K, eps, x, (uint8_t *)xq);
 }
 
 } // namespace bq8
@@ -140,12 +159,22 @@ BQ8_EXPORT bq8_status rms_norm_q8_1(const float *y, int64_t M, int64_t K, float 
 {
     if (!y || !xq)
         return BQ8_ERR_NULL;
-    if (M < 1 || M > 64 || K < QK || K % QK != 0 || M * K >= (int64_t(1) << 31) || !(eps > 0.0f))
+    if (M < 1 || M > 64 || K < QK || K % QK != 0 || K > RMS_MAX_K || !(eps > 0.0f))
         return BQ8_ERR_SHAPE;
     if (!aligned(y, 4) || !aligned(xq, 4) || (x && !aligned(x, 4)))
         return BQ8_ERR_ALIGN;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(rms_norm_q8_1_kernel, dim3((unsigned)M), dim3(RMS_THREADS), 0,
-                       (hipStream_t)stream, y, (int)K, eps, x, (uint8_t *)xq);
+    const int64_t per_group = (K / QK + RMS_GROUPS - 1) / RMS_GROUPS;
+    hipStream_t s = (hipStream_t)stream;
+    if (per_group <= 2)
+        launch_rms<2>(y, M, K, eps, x, xq, s);
+    else if (per_group <= 4)
+        launch_rms<4>(y, M, K, eps, x, xq, s);
+    else if (per_group <= 8)
+        launch_rms<8>(y, M, K, eps, x, xq, s);
+    else if (per_group <= 16)
+        launch_rms<16>(y, M, K, eps, x, xq, s);
+    else
+        launch_rms<32>(y, M, K, eps, x, xq, s);
     return launch_status();
 }

@@ -185,3 +185,22 @@ def q6k_raw_weights_device(seed: int, N: int, K: int, device="cuda", d_range=Q6_
     d.uniform_(d_range[0], d_range[1], generator=g)
     dbytes = d.to(torch.float16).view(torch.uint8).reshape(N, ns, 2)
     return torch.cat([qbytes, sc, dbytes], dim=2).reshape(N, ns * Q6_K_BYTES).contiguous()
+
+
+def stream_weights_device(layers: int = STREAM["layers"], hidden: int = STREAM["hidden"],
+                          ffn: int = STREAM["ffn"], device="cuda"):
+    """Gate, up ([ffn][hidden/32] Q4_0) and down ([hidden][ffn/32] Q4_0)
+    weights of every stream layer, generated on the device from the
+    per-layer sub-seeds.  Returns three lists of uint8 tensors."""
+    gate = [q4_0_weights_device(stream_layer_seed(l, "gate"), ffn, hidden, device)
+            for l in range(layers)]
+    up = [q4_0_weights_device(stream_layer_seed(l, "up"), ffn, hidden, device)
+          for l in range(layers)]
+    down = [q4_0_weights_device(stream_layer_seed(l, "down"), hidden, ffn, device)
+            for l in range(layers)]
+    return gate, up, down
+
+
+def stream_x0(M: int = STREAM["M"], hidden: int = STREAM["hidden"], seed: int = STREAM["seed"]):
+    """Layer-0 input of the stream: f32 [M][hidden] ~ N(0, 1)."""
+    return normal_rows(np.random.default_rng(seed), M, hidden)

@@ -176,13 +176,47 @@ bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, const float *
  *   M*N < 2^31.  4-byte alignment.
  * rms_norm_q8_1: x = y / sqrt(mean_k(y^2) + eps) per row, then xq = Q8_1(x).
  *   y: f32 [M][K]; x: optional f32 [M][K] copy (NULL to skip); xq: Q8_1
- *   [M][K/32].  Shape: 1 <= M <= 64, K >= 32, K % 32 == 0, M*K < 2^31;
+ *   [M][K/32].  Shape: 1 <= M <= 64, 32 <= K <= 32768, K % 32 == 0;
  *   eps > 0.  4-byte alignment.
  * ---------------------------------------------------------------------- */
 bq8_status silu_mul_q8_1(const float *g, const float *u, int64_t M, int64_t N, float *h, void *hq,
                          void *stream);
 bq8_status rms_norm_q8_1(const float *y, int64_t M, int64_t K, float eps, float *x, void *xq,
                          void *stream);
+
+/* ------------------------------------------------------------------------
+ * Width-M verifier FFN stream over `layers` layers, enqueued from native
+ * code (five launches per layer, no host synchronization; the closure page's
+ * width-6 gate/up and down projections and down-to-next-RMS/Q8 boundary, and
+ * the follow-up page's shared Q8_1 activation for sibling matmuls).
+ * Per layer l:
+ *   xq = Q8_1(x0)                        if l == 0   (q8_1_quantize)
+ *   xq = rms_norm_q8_1(y, eps)           otherwise
+ *   g  = q4_0_mmvq(w_gate[l], xq)        f32 [M][ffn]
+ *   u  = q4_0_mmvq(w_up[l],   xq)        f32 [M][ffn]
+ *   hq = silu_mul_q8_1(g, u)             Q8_1 [M][ffn/32]
+ *   y  = q4_0_mmvq(w_down[l], hq)        f32 [M][hidden]
+ * w_gate, w_up, w_down: HOST arrays of `layers` DEVICE pointers; gate and up
+ *   are Q4_0 [ffn][hidden/32], down is Q4_0 [hidden][ffn/32]; 16-byte
+ *   aligned.
+ * x0: f32 [M][hidden] input of layer 0, 4-byte aligned (read only).
+ * y:  f32 [M][hidden], 4-byte aligned; on completion the down output of the
+ *   last layer (it is also each layer's intermediate).
+ * work: device workspace of at least offsets[4] bytes from
+ *   q4_0_ffn_stream_layout, 256-byte aligned.  On completion it holds the
+ *   last layer's stage buffers: xq at offsets[0], g at offsets[1], u at
+ *   offsets[2], hq at offsets[3].
+ * Shape: 1 <= M <= 17, hidden and ffn multiples of 32, 32 <= hidden <= 32768,
+ *   32 <= ffn <= 2^26, M*ffn < 2^31, 1 <= layers <= 2^20, eps > 0.
+ * Every layer's pointers are checked before anything is enqueued.
+ * q4_0_ffn_stream_layout: host; writes the four stage offsets and the total
+ *   workspace size to offsets[0..4].
+ * ---------------------------------------------------------------------- */
+bq8_status q4_0_ffn_stream_layout(int64_t M, int64_t hidden, int64_t ffn, int64_t *offsets);
+bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *const *w_up,
+                           const void *const *w_down, int64_t layers, int64_t M, int64_t hidden,
+                           int64_t ffn, const float *x0, float eps, float *y, void *work,
+                           int64_t work_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,8 @@ def test_header_declares_expected_entry_points():
         assert f"q4_0_mmvq_m{m}" in names
     for n in ["q8_1_quantize", "q4_0_mmvq", "q6k_pack_bytes", "q6k_pack_expand",
               "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1", "bq8_status_string",
-              "bq8_abi_version", "silu_mul_q8_1", "rms_norm_q8_1"]:
+              "bq8_abi_version", "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_ffn_stream_layout",
+              "q4_0_ffn_stream"]:
         assert n in names
 
 
@@ -158,4 +159,53 @@ def test_layer_glue_validation(L):
     assert L.rms_norm_q8_1(None, 6, 64, ctypes.c_float(1e-6), None, A, None) == NULL
     assert L.rms_norm_q8_1(A, 65, 64, ctypes.c_float(1e-6), None, A, None) == SHAPE
     assert L.rms_norm_q8_1(A, 6, 64, ctypes.c_float(0.0), None, A, None) == SHAPE
+    assert L.rms_norm_q8_1(A, 1, 32768 + 32, ctypes.c_float(1e-6), None, A, None) == SHAPE
     assert L.rms_norm_q8_1(A, 6, 64, ctypes.c_float(1e-6), None, A + 1, None) == ALIGN
+
+
+def test_stream_layout(L):
+    import block_quantized_gemv_q8_amd as b
+
+    lay = b.q4_0_ffn_stream_layout(6, 5120, 17408)
+    assert lay["xq"] == 0
+    assert lay["g"] >= 6 * 160 * 36 and lay["g"] % 256 == 0
+    assert lay["u"] >= lay["g"] + 6 * 17408 * 4 and lay["u"] % 256 == 0
+    assert lay["hq"] >= lay["u"] + 6 * 17408 * 4 and lay["hq"] % 256 == 0
+    assert lay["total"] >= lay["hq"] + 6 * 544 * 36
+    off = (ctypes.c_int64 * 5)()
+    assert L.q4_0_ffn_stream_layout(0, 5120, 17408, off) == SHAPE
+    assert L.q4_0_ffn_stream_layout(18, 5120, 17408, off) == SHAPE
+    assert L.q4_0_ffn_stream_layout(6, 5000, 17408, off) == SHAPE
+    assert L.q4_0_ffn_stream_layout(6, 5120, 17400, off) == SHAPE
+    assert L.q4_0_ffn_stream_layout(6, 32768 + 32, 17408, off) == SHAPE
+    assert L.q4_0_ffn_stream_layout(6, 32768, 17408, off) == OK
+    assert L.q4_0_ffn_stream_layout(6, 5120, 17408, None) == NULL
+
+
+def test_stream_validation(L):
+    import block_quantized_gemv_q8_amd as b
+
+    total = b.q4_0_ffn_stream_layout(6, 5120, 17408)["total"]
+    layers = 3
+    good = (ctypes.c_void_p * layers)(A, A + 0x100, A + 0x200)
+    args = dict(g=good, u=good, d=good, layers=layers, M=6, hidden=5120, ffn=17408, x0=A,
+                eps=1e-6, y=A, work=A, wb=total)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.q4_0_ffn_stream(a["g"], a["u"], a["d"], a["layers"], a["M"], a["hidden"],
+                                 a["ffn"], a["x0"], ctypes.c_float(a["eps"]), a["y"], a["work"],
+                                 a["wb"], None)
+
+    assert call(g=None) == NULL
+    assert call(x0=None) == NULL
+    assert call(work=None) == NULL
+    assert call(u=(ctypes.c_void_p * layers)(A, None, A)) == NULL       # a null layer
+    assert call(layers=0) == SHAPE
+    assert call(M=18) == SHAPE
+    assert call(hidden=5000) == SHAPE
+    assert call(eps=0.0) == SHAPE
+    assert call(d=(ctypes.c_void_p * layers)(A, A, A + 8)) == ALIGN    # last layer misaligned
+    assert call(x0=A + 2) == ALIGN
+    assert call(work=A + 16) == ALIGN
+    assert call(wb=total - 1) == SIZE

@@ -359,11 +359,13 @@ def test_silu_mul_q8_1_stage():
     assert (hq2 == hq).all()
 
 
-def test_rms_norm_q8_1_stage():
-    rng = np.random.default_rng(401)
-    M, K = 6, 5120
+@pytest.mark.parametrize("M,K", [(6, 5120), (1, 32), (3, 2048), (2, 4096), (17, 8192),
+                                 (6, 16384), (6, 17408), (2, 32768), (64, 1056)])
+def test_rms_norm_q8_1_stage(M, K):
+    say(f"rms_norm_q8_1 M={M} K={K}")
+    rng = np.random.default_rng(401 + K + M)
     y = (rng.standard_normal((M, K)) * 40).astype(np.float32)
-    y[5] = 0.0
+    y[M - 1] = 0.0 if M > 1 else y[M - 1]
     xo = torch.empty((M, K), dtype=torch.float32, device=DEV)
     xq = host(bq.rms_norm_q8_1(dev(y), 1e-6, x=xo))
     xg = host(xo)
@@ -371,3 +373,5 @@ def test_rms_norm_q8_1_stage():
     err = np.abs(xg.astype(np.float64) - ref)
     assert (err <= REL * np.abs(ref) + ABS).all()
     assert (xq == oracle.q8_1_quantize(xg)).all()
+    xq2 = host(bq.rms_norm_q8_1(dev(y), 1e-6))
+    assert (xq2 == xq).all()
