@@ -52,20 +52,30 @@ __device__ __forceinline__ int nib_minus8(uint32_t nibbles)
 // lanes (lane32 = lane index within the group).  Arithmetic in binary32:
 // amax over the block, d = amax / 127 (correctly rounded division),
 // q = x / d rounded half away from zero and clamped to +-127 (d == 0 gives
-// q = 0), s = d * sum(q).  Lane 0 of the group writes d and s; every lane
-// writes its quant.  `blk` points at the block's 36 output bytes.
-__device__ __forceinline__ void q8_1_block_store(float v, int lane32, bool valid, uint8_t *blk)
+// q = 0).  Returns this lane's quant; `d` receives the binary32 scale (the
+// block stores it rounded to fp16).
+__device__ __forceinline__ int q8_1_block_quant(float v, float &d)
 {
     float a = fabsf(v);
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1)
         a = fmaxf(a, __shfl_xor(a, off, 32));
-    const float d = a / 127.0f;
+    d = a / 127.0f;
     int q = 0;
     if (d != 0.0f) {
         q = (int)roundf(v / d);
         q = q > 127 ? 127 : (q < -127 ? -127 : q);
     }
+    return q;
+}
+
+// The Q8_1 block of q8_1_block_quant: every lane writes its quant, lane 0
+// of the group writes d and s = d * sum(q) (binary32 product, then fp16).
+// `blk` points at the block's 36 output bytes.
+__device__ __forceinline__ void q8_1_block_store(float v, int lane32, bool valid, uint8_t *blk)
+{
+    float d;
+    const int q = q8_1_block_quant(v, d);
     int s = q;
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1)

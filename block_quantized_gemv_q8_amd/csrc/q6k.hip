@@ -11,40 +11,62 @@
 //   "Memory and startup" -- the pack size for [5120, 248320].
 // Formats: include/bq8.h.
 //
-// Top-1 mapping on gfx950: lane <-> vocabulary row n (64 rows per wave,
-// 4 waves per workgroup, grid-stride over 64-row tiles).  The wave loads each
-// 128-byte run of its 64 rows' quants with whole-cache-line loads (eight
-// lanes per row), passes it through LDS, and every lane reads back its own
-// row; the R quantized activation rows -- identical for every lane -- come
-// through scalar loads.
+// Pack layout (Q, SC and D planes split into tiles of 64 consecutive rows,
+// the last tile ragged; include/bq8.h gives the offsets): within a tile the
+// Q plane stores 16-value piece c of every row, row after row, then piece
+// c + 1, so the 64 rows' piece c is one contiguous kilobyte.
+//
+// Top-1 mapping on gfx950: one wave per 64-row tile, lane <-> row.  Lane r
+// loads its own 16-byte pieces; each load instruction of the wave reads one
+// contiguous kilobyte, and the values land directly in the registers where
+// they are used (no LDS staging).  The R quantized activation rows --
+// identical for every lane -- come through scalar loads as v_dot4 operands.
 // Per 32 values and activation row: 8 x v_dot4 give the two 16-value integer
-// dots, which the two int8 subscales combine exactly in int32; the result is
-// scaled by d_w * d_x (exact in binary32) and accumulated in binary32, in the
-// same order for every row, so equal weight rows give bitwise equal logits.
-// Each lane keeps, per activation row, a 64-bit key
+// dots, which the two int8 subscales combine exactly in int32 (24-bit
+// multiplies); the result, widened to binary32, is scaled by the row's d_x
+// into a per-superblock sum, and d_w scales that sum once per superblock.
+// The order of operations is the same for every row, so equal weight rows
+// give bitwise equal logits.  Each lane keeps, per activation row, a 64-bit
+// key
 //     (order-preserving bits of the logit) << 32 | (0xFFFFFFFF - id)
 // whose maximum is the largest logit with the lowest id among ties.  Keys
 // meet by wave butterflies, then in LDS, then in one slot per workgroup in
-// the caller's scratch; the last workgroup to finish (atomic counter) reduces
-// the slots and writes the ids.  No logit ever reaches memory, and max over
-// integers makes the result independent of scheduling.
+// the caller's scratch; a one-workgroup kernel on the same stream reduces
+// the slots and writes the ids.  Stream order, not a device-wide fence,
+// publishes the slots: a per-workgroup release fence at device scope costs
+// an L2 write-back on this multi-XCD part and doubled the kernel time.  No
+// logit ever reaches memory, and max over integers makes the result
+// independent of scheduling.
 #include "bq8_dev.h"
 
 namespace bq8 {
 
 // ------------------------------------------------------------- expansion
-// One wave per superblock (grid-stride).  Lane l produces the four codes
-// 4l..4l+3: value e of the superblock lies in half h = e/128; within it,
-// c = (e%128)/32 picks the low (c < 2) or high nibble of ql[64h + 32(c&1) + l']
-// and bits 2c..2c+1 of qh[32h + l'], with l' = e%32.
-__global__ __launch_bounds__(256) void q6k_expand_kernel(const uint8_t *__restrict__ raw,
-                                                         int64_t nsb, int8_t *__restrict__ Q,
+constexpr int PACK_TILE = 64;
+
+// Tile of row n: first row n0, rows in the tile, index of n in the tile.
+__device__ __forceinline__ int tile_of(int n, int N, int &n0, int &r)
+{
+    n0 = n / PACK_TILE * PACK_TILE;
+    r = n - n0;
+    return (N - n0 < PACK_TILE) ? N - n0 : PACK_TILE;
+}
+
+// One wave per (superblock s, row n), rows fastest, so neighbouring waves
+// fill neighbouring 16-byte pieces of the tiled planes.  Lane l produces the
+// four codes 4l..4l+3 of the superblock: value e lies in half h = e/128;
+// within it, c = (e%128)/32 picks the low (c < 2) or high nibble of
+// ql[64h + 32(c&1) + l'] and bits 2c..2c+1 of qh[32h + l'], with l' = e%32.
+__global__ __launch_bounds__(256) void q6k_expand_kernel(const uint8_t *__restrict__ raw, int N,
+                                                         int K, int8_t *__restrict__ Q,
                                                          int8_t *__restrict__ SC,
                                                          uint16_t *__restrict__ D)
 {
     const int lane = threadIdx.x & 63;
     const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int ns = K / QK_K;
+    const int64_t total = (int64_t)N * ns;
     const int e = 4 * lane;
     const int h = e >> 7;
     const int c = (e & 127) >> 5;
@@ -53,8 +75,12 @@ __global__ __launch_bounds__(256) void q6k_expand_kernel(const uint8_t *__restri
     const int qh_off = 128 + 32 * h + l0;
     const int lo_shift = (c < 2) ? 0 : 4;
     const int hi_shift = 2 * c;
-    for (int64_t i = wave_id; i < nsb; i += nwaves) {
-        const uint8_t *blk = raw + i * Q6_K_BYTES;
+    for (int64_t i = wave_id; i < total; i += nwaves) {
+        const int s = (int)(i / N);
+        const int n = (int)(i - (int64_t)s * N);
+        int n0, r;
+        const int rows_t = tile_of(n, N, n0, r);
+        const uint8_t *blk = raw + ((int64_t)n * ns + s) * Q6_K_BYTES;
         uint32_t packed = 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -63,15 +89,19 @@ __global__ __launch_bounds__(256) void q6k_expand_kernel(const uint8_t *__restri
             const uint32_t code = lo | (hi << 4);
             packed |= ((code - 32u) & 0xFFu) << (8 * t);
         }
-        reinterpret_cast<uint32_t *>(Q + i * QK_K)[lane] = packed;
+        // value e of superblock s is in piece 16 s + e/16 at byte e%16
+        const int64_t piece = (int64_t)s * 16 + (e >> 4);
+        *reinterpret_cast<uint32_t *>(Q + (int64_t)n0 * K + (piece * rows_t + r) * 16 + (e & 15)) =
+            packed;
         if (lane < 4) {
-            const uint8_t *s = blk + 192 + 4 * lane;
-            reinterpret_cast<uint32_t *>(SC + i * 16)[lane] =
-                (uint32_t)s[0] | ((uint32_t)s[1] << 8) | ((uint32_t)s[2] << 16) |
-                ((uint32_t)s[3] << 24);
+            const uint8_t *sc = blk + 192 + 4 * lane;
+            *reinterpret_cast<uint32_t *>(SC + (int64_t)n0 * (K / 16) +
+                                          ((int64_t)s * rows_t + r) * 16 + 4 * lane) =
+                (uint32_t)sc[0] | ((uint32_t)sc[1] << 8) | ((uint32_t)sc[2] << 16) |
+                ((uint32_t)sc[3] << 24);
         }
         if (lane == 4)
-            D[i] = (uint16_t)(blk[208] | (blk[209] << 8));
+            D[(int64_t)n0 * ns + (int64_t)s * rows_t + r] = (uint16_t)(blk[208] | (blk[209] << 8));
     }
 }
 
@@ -80,7 +110,6 @@ constexpr int TOP1_THREADS = 256;
 constexpr int TOP1_WAVES = TOP1_THREADS / WAVE;
 constexpr int TOP1_MAX_GRID = 1024;
 constexpr int TOP1_MAX_ROWS = 8;
-constexpr int64_t SCRATCH_HEADER = 256; // [0,4): completion counter
 
 __device__ __forceinline__ uint64_t make_key(float v, uint32_t id)
 {
@@ -103,121 +132,90 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k)
     return k;
 }
 
-// Rows 0..R-1 of x starting at row0 -> Q8_1 in scratch; reset the counter.
-__global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restrict__ x,
-                                                            int nblocks,
-                                                            uint8_t *__restrict__ xq,
-                                                            uint32_t *__restrict__ counter)
+// Rows 0..R-1 of x (starting at row0) -> the Q8_1 quants and scales in
+// scratch, block-major so that one superblock's activations for every row
+// are contiguous: quants int8 [nb][R][32], scales f32 [nb][R] (the fp16 d of
+// the block, widened exactly).
+__global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restrict__ x, int R,
+                                                            int nb, int8_t *__restrict__ xq8,
+                                                            float *__restrict__ dx)
 {
     const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-    const int blk = gid >> 5;
+    const int blk = gid >> 5; // row-major (r, b) over the R rows of x
     const int j = gid & 31;
-    const bool valid = blk < nblocks;
+    const bool valid = blk < R * nb;
     const float v = valid ? x[(size_t)blk * QK + j] : 0.0f;
-    q8_1_block_store(v, j, valid, xq + (size_t)blk * Q8_1_BYTES);
-    if (gid == 0)
-        *counter = 0u;
+    float d;
+    const int q = q8_1_block_quant(v, d);
+    if (valid) {
+        const int r = blk / nb, b = blk - r * nb;
+        xq8[((size_t)b * R + r) * QK + j] = (int8_t)q;
+        if (j == 0)
+            dx[(size_t)b * R + r] = h2f(f2h(d));
+    }
 }
-
-// Order this wave's LDS writes before its reads of other lanes' data.
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-constexpr int PIECE_ROW_STRIDE = 144; // 128 bytes of quants + 16 of padding per staged row
 
 template <int R>
-__global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_kernel(
-    const int8_t *__restrict__ Q, const int8_t *__restrict__ SC, const uint16_t *__restrict__ D,
-    int N, int K, const uint8_t *__restrict__ xq, uint64_t *__restrict__ slots,
-    uint32_t *__restrict__ counter, int32_t *__restrict__ ids)
+__global__ __launch_bounds__(TOP1_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
+q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ SC,
+                const uint16_t *__restrict__ D, int N, int K, const int8_t *__restrict__ xq8,
+                const float *__restrict__ dx, uint64_t *__restrict__ slots)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t stage_all[TOP1_WAVES][WAVE * PIECE_ROW_STRIDE];
     __shared__ uint64_t wave_best[TOP1_WAVES][R];
-    __shared__ uint32_t is_last;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    uint8_t *stage = stage_all[wave];
-    const int nb = K / QK;
     const int nsb = K / QK_K;
-    const int ntiles = (N + WAVE - 1) / WAVE;
+    const int ntiles = (N + PACK_TILE - 1) / PACK_TILE;
 
     uint64_t best[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        best[r] = 0;
+    for (int i = 0; i < R; ++i)
+        best[i] = 0;
 
     for (int t = blockIdx.x * TOP1_WAVES + wave; t < ntiles; t += gridDim.x * TOP1_WAVES) {
-        const int n0 = t * WAVE;
+        const int n0 = t * PACK_TILE;
+        const int rows_t = (N - n0 < PACK_TILE) ? N - n0 : PACK_TILE;
+        const int r = lane < rows_t ? lane : rows_t - 1; // ragged tile: repeat the last row
         const int n_raw = n0 + lane;
-        const int n = n_raw < N ? n_raw : N - 1; // loads stay in bounds
-        // A 128-byte run of the quant plane for the tile's 64 rows is 512
-        // pieces of 16 bytes; load j brings pieces 64j..64j+63, i.e. rows
-        // 8j..8j+7 with eight lanes per row: eight whole 128-byte lines.
-        const int8_t *tile = Q + (size_t)n0 * K;
-        uint32_t goff[8];
-        uint32_t soff[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = 8 * j + (lane >> 3);
-            const int rr = (n0 + r < N) ? r : (N - 1 - n0);
-            goff[j] = (uint32_t)rr * (uint32_t)K + 16u * (uint32_t)(lane & 7);
-            soff[j] = (uint32_t)r * PIECE_ROW_STRIDE + 16u * (uint32_t)(lane & 7);
-        }
-        const int8_t *srow = SC + (size_t)n * (K / 16);
-        const uint16_t *drow = D + (size_t)n * nsb;
+        const int8_t *qt = Q + (size_t)n0 * K;
+        const int8_t *st = SC + (size_t)n0 * (K / 16);
+        const uint16_t *dt = D + (size_t)n0 * nsb;
         float acc[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            acc[r] = 0.0f;
+        for (int i = 0; i < R; ++i)
+            acc[i] = 0.0f;
 
+        // pieces 16 sb + 8 half .. +7 of this lane's row: 128 quants
         auto load_half = [&](u32x4(&v)[8], int sb, int half) {
-            const int8_t *src = tile + sb * QK_K + half * 128;
+            const int c0 = sb * 16 + half * 8;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + goff[j]));
+                v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    qt + ((size_t)(c0 + j) * rows_t + r) * 16));
         };
-        auto compute_half = [&](const u32x4(&v)[8], int sb, int half, const u32x4 &scw, float dw) {
-            wave_lds_sync();
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<u32x4 *>(stage + soff[j]) = v[j];
-            wave_lds_sync();
-            uint32_t wq[32];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const u32x4 x4 =
-                    *reinterpret_cast<const u32x4 *>(stage + lane * PIECE_ROW_STRIDE + 16 * i);
-                wq[4 * i + 0] = x4[0];
-                wq[4 * i + 1] = x4[1];
-                wq[4 * i + 2] = x4[2];
-                wq[4 * i + 3] = x4[3];
-            }
+        // 32-blocks 4 half .. 4 half + 3 of the superblock, every activation row
+        auto compute_half = [&](const u32x4(&v)[8], int half, const u32x4 &scw,
+                                const int8_t *xs, const float *ds, float(&accsb)[R]) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                // 32-block b = sb*8 + half*4 + j uses subscales 2*(half*4+j) and +1
-                const int sbi = 2 * (half * 4 + j);
-                const uint32_t scword = scw[sbi >> 2];
-                const int sca = __builtin_amdgcn_sbfe(scword, 8 * (sbi & 3), 8);
-                const int scb = __builtin_amdgcn_sbfe(scword, 8 * ((sbi & 3) + 1), 8);
-                const int b = sb * 8 + half * 4 + j;
+                const int bl = half * 4 + j;
+                const uint32_t scword = scw[bl >> 1];
+                const int sca = __builtin_amdgcn_sbfe(scword, 16 * (bl & 1), 8);
+                const int scb = __builtin_amdgcn_sbfe(scword, 16 * (bl & 1) + 8, 8);
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const uint32_t *xb = reinterpret_cast<const uint32_t *>(
-                        xq + ((size_t)r * nb + b) * Q8_1_BYTES);
-                    int sa = dot4((int)wq[8 * j + 0], (int)xb[1], 0);
-                    sa = dot4((int)wq[8 * j + 1], (int)xb[2], sa);
-                    sa = dot4((int)wq[8 * j + 2], (int)xb[3], sa);
-                    sa = dot4((int)wq[8 * j + 3], (int)xb[4], sa);
-                    int sbv = dot4((int)wq[8 * j + 4], (int)xb[5], 0);
-                    sbv = dot4((int)wq[8 * j + 5], (int)xb[6], sbv);
-                    sbv = dot4((int)wq[8 * j + 6], (int)xb[7], sbv);
-                    sbv = dot4((int)wq[8 * j + 7], (int)xb[8], sbv);
-                    const int I = sa * sca + sbv * scb;
-                    acc[r] = fmaf((float)I, dw * h2f(xb[0]), acc[r]);
+                for (int i = 0; i < R; ++i) {
+                    const int *xb = reinterpret_cast<const int *>(xs + (bl * R + i) * QK);
+                    int sa = dot4((int)v[2 * j][0], xb[0], 0);
+                    sa = dot4((int)v[2 * j][1], xb[1], sa);
+                    sa = dot4((int)v[2 * j][2], xb[2], sa);
+                    sa = dot4((int)v[2 * j][3], xb[3], sa);
+                    int sbv = dot4((int)v[2 * j + 1][0], xb[4], 0);
+                    sbv = dot4((int)v[2 * j + 1][1], xb[5], sbv);
+                    sbv = dot4((int)v[2 * j + 1][2], xb[6], sbv);
+                    sbv = dot4((int)v[2 * j + 1][3], xb[7], sbv);
+                    // |sa|, |sbv| <= 16 * 32 * 127 < 2^23: exact 24-bit products
+                    const int I = __mul24(sa, sca) + __mul24(sbv, scb);
+                    accsb[i] = fmaf((float)I, ds[bl * R + i], accsb[i]);
                 }
             }
         };
@@ -230,37 +228,47 @@ __global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_kernel(
         u32x4 va[8], vb[8];
         load_half(va, 0, 0);
         load_half(vb, 0, 1);
-        u32x4 scw = *reinterpret_cast<const u32x4 *>(srow);
-        uint32_t dbits = drow[0];
+        u32x4 scw = *reinterpret_cast<const u32x4 *>(st + (size_t)r * 16);
+        uint32_t dbits = dt[r];
         for (int sb = 0; sb < nsb; ++sb) {
             const int sbn = (sb + 1 < nsb) ? sb + 1 : sb;
-            const u32x4 scw_next = *reinterpret_cast<const u32x4 *>(srow + sbn * 16);
-            const uint32_t dbits_next = drow[sbn];
-            const float dw = h2f(dbits);
-            compute_half(va, sb, 0, scw, dw);
+            const u32x4 scw_next =
+                *reinterpret_cast<const u32x4 *>(st + ((size_t)sbn * rows_t + r) * 16);
+            const uint32_t dbits_next = dt[(size_t)sbn * rows_t + r];
+            const int8_t *xs = xq8 + (size_t)sb * 8 * R * QK;
+            const float *ds = dx + (size_t)sb * 8 * R;
+            float accsb[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                accsb[i] = 0.0f;
+            compute_half(va, 0, scw, xs, ds, accsb);
             load_half(va, sbn, 0);
-            compute_half(vb, sb, 1, scw, dw);
+            compute_half(vb, 1, scw, xs, ds, accsb);
             load_half(vb, sbn, 1);
+            const float dw = h2f(dbits);
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                acc[i] = fmaf(accsb[i], dw, acc[i]);
             scw = scw_next;
             dbits = dbits_next;
         }
         if (n_raw < N) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float v = acc[r];
+            for (int i = 0; i < R; ++i) {
+                const float v = acc[i];
                 if (!__builtin_isnan(v)) {
                     const uint64_t k = make_key(v, (uint32_t)n_raw);
-                    best[r] = k > best[r] ? k : best[r];
+                    best[i] = k > best[i] ? k : best[i];
                 }
             }
         }
     }
 
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint64_t k = wave_max_u64(best[r]);
+    for (int i = 0; i < R; ++i) {
+        const uint64_t k = wave_max_u64(best[i]);
         if (lane == 0)
-            wave_best[wave][r] = k;
+            wave_best[wave][i] = k;
     }
     __syncthreads();
     if (threadIdx.x < R) {
@@ -270,26 +278,24 @@ __global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_kernel(
             k = wave_best[w][threadIdx.x] > k ? wave_best[w][threadIdx.x] : k;
         slots[(size_t)blockIdx.x * R + threadIdx.x] = k;
     }
-    // publish this workgroup's slot, then count it
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0)
-        is_last = (atomicAdd(counter, 1u) == gridDim.x - 1) ? 1u : 0u;
-    __syncthreads();
-    if (!is_last)
-        return;
-    __threadfence();
-    // the last workgroup reduces every slot; thread r*32+i handles row r
-    for (int r = 0; r < R; ++r) {
+}
+
+// One workgroup: the maximum key of each row over every slot -> ids.
+__global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_final_kernel(
+    const uint64_t *__restrict__ slots, int nslots, int R, int32_t *__restrict__ ids)
+{
+    __shared__ uint64_t wave_best[TOP1_WAVES][TOP1_MAX_ROWS];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    for (int i = 0; i < R; ++i) {
         uint64_t k = 0;
-        for (int g = threadIdx.x; g < (int)gridDim.x; g += TOP1_THREADS) {
-            const uint64_t s = __hip_atomic_load(&slots[(size_t)g * R + r], __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+        for (int g = threadIdx.x; g < nslots; g += TOP1_THREADS) {
+            const uint64_t s = slots[(size_t)g * R + i];
             k = s > k ? s : k;
         }
         k = wave_max_u64(k);
         if (lane == 0)
-            wave_best[wave][r] = k;
+            wave_best[wave][i] = k;
     }
     __syncthreads();
     if (threadIdx.x < R) {
@@ -315,19 +321,20 @@ static bool top1_shape_ok(int64_t N, int64_t K)
            N * K < (int64_t(1) << 40) && K < (int64_t(1) << 24);
 }
 
-static int64_t xq_area(int64_t K, int64_t rows)
-{
-    const int64_t b = rows * (K / QK) * Q8_1_BYTES;
-    return (b + 255) / 256 * 256;
-}
+static int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
+
+// Scratch: quants int8 [nb][rows][32] | scales f32 [nb][rows] | one u64 key
+// per (workgroup, row); each area starts on a 256-byte boundary.
+static int64_t xq8_area(int64_t K, int64_t rows) { return round256(rows * K); }
+static int64_t dx_area(int64_t K, int64_t rows) { return round256(rows * (K / QK) * 4); }
 
 template <int R>
 static void launch_top1(const int8_t *Q, const int8_t *SC, const uint16_t *D, int N, int K,
-                        const uint8_t *xq, uint64_t *slots, uint32_t *counter, int32_t *ids,
-                        int grid, hipStream_t s)
+                        const int8_t *xq8, const float *dx, uint64_t *slots, int grid,
+                        hipStream_t s)
 {
     hipLaunchKernelGGL(q6k_top1_kernel<R>, dim3(grid), dim3(TOP1_THREADS), 0, s, Q, SC, D, N, K,
-                       xq, slots, counter, ids);
+                       xq8, dx, slots);
 }
 
 } // namespace bq8
@@ -361,7 +368,7 @@ BQ8_EXPORT bq8_status q6k_pack_expand(const void *raw, int64_t N, int64_t K, voi
         grid = 65536;
     (void)hipGetLastError();
     hipLaunchKernelGGL(q6k_expand_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
-                       (const uint8_t *)raw, nsb, Q, SC, D);
+                       (const uint8_t *)raw, (int)N, (int)K, Q, SC, D);
     return launch_status();
 }
 
@@ -369,7 +376,7 @@ BQ8_EXPORT int64_t q6k_lmhead_top1_scratch_bytes(int64_t N, int64_t K, int64_t r
 {
     if (!top1_shape_ok(N, K) || rows < 1 || rows > TOP1_MAX_ROWS)
         return -1;
-    return SCRATCH_HEADER + xq_area(K, rows) + top1_grid(N) * rows * (int64_t)sizeof(uint64_t);
+    return xq8_area(K, rows) + dx_area(K, rows) + top1_grid(N) * rows * (int64_t)sizeof(uint64_t);
 }
 
 BQ8_EXPORT bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, const float *x,
@@ -389,28 +396,33 @@ BQ8_EXPORT bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, co
     const int8_t *SC = Q + N * K;
     const uint16_t *D = (const uint16_t *)(SC + N * (K / 16));
     uint8_t *base = (uint8_t *)scratch;
-    uint32_t *counter = (uint32_t *)base;
-    uint8_t *xq = base + SCRATCH_HEADER;
-    uint64_t *slots = (uint64_t *)(xq + xq_area(K, rows));
-    const int nblocks = (int)(rows * (K / QK));
+    int8_t *xq8 = (int8_t *)base;
+    float *dx = (float *)(base + xq8_area(K, rows));
+    uint64_t *slots = (uint64_t *)(base + xq8_area(K, rows) + dx_area(K, rows));
+    const int nb = (int)(K / QK);
+    const int nblocks = (int)rows * nb;
     const int grid = (int)top1_grid(N);
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     hipLaunchKernelGGL(q6k_top1_prep_kernel, dim3((nblocks * 32 + 255) / 256), dim3(256), 0, s,
-                       x + row0 * K, nblocks, xq, counter);
+                       x + row0 * K, (int)rows, nb, xq8, dx);
     if (hipGetLastError() != hipSuccess)
         return BQ8_ERR_HIP;
     const int n = (int)N, k = (int)K;
     switch (rows) {
-    case 1: launch_top1<1>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
-    case 2: launch_top1<2>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
-    case 3: launch_top1<3>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
-    case 4: launch_top1<4>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
-    case 5: launch_top1<5>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
-    case 6: launch_top1<6>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
-    case 7: launch_top1<7>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
-    case 8: launch_top1<8>(Q, SC, D, n, k, xq, slots, counter, ids, grid, s); break;
+    case 1: launch_top1<1>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
+    case 2: launch_top1<2>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
+    case 3: launch_top1<3>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
+    case 4: launch_top1<4>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
+    case 5: launch_top1<5>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
+    case 6: launch_top1<6>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
+    case 7: launch_top1<7>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
+    case 8: launch_top1<8>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
     }
+    if (hipGetLastError() != hipSuccess)
+        return BQ8_ERR_HIP;
+    hipLaunchKernelGGL(q6k_top1_final_kernel, dim3(1), dim3(TOP1_THREADS), 0, s, slots, grid,
+                       (int)rows, ids);
     return launch_status();
 }
 

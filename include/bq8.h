@@ -40,9 +40,18 @@
  *         low nibble of qs[j], element j+16 the high nibble; value d*(q-8).
  *   Q6_K  256 weights in 210 bytes: ql[128], qh[64], scales[16] (int8),
  *         d (fp16); value d * scales[e/16] * (u - 32) for a 6-bit code u.
- *   Expanded Q6_K pack: three planar row-major arrays,
- *         Q int8 [N][K] at 0, SC int8 [N][K/16] at N*K,
- *         D fp16 [N][K/256] at N*K + N*K/16  (total q6k_pack_bytes(N, K)).
+ *   Expanded Q6_K pack: three planes -- Q int8 quants at 0, SC int8
+ *         subscales (one per 16 values) at N*K, D fp16 superblock scales at
+ *         N*K + N*K/16 (total q6k_pack_bytes(N, K)) -- each split into tiles
+ *         of 64 consecutive rows (the last tile holds the remaining N % 64
+ *         rows).  For row n: n0 = 64*(n/64), r = n - n0, rows_t =
+ *         min(64, N - n0).
+ *           quant k      at byte    n0*K + ((k/16)*rows_t + r)*16 + k%16
+ *           subscale j   at byte    N*K + n0*(K/16) + ((j/16)*rows_t + r)*16 + j%16
+ *           scale s      at element (N*K + N*K/16)/2 + n0*(K/256) + s*rows_t + r
+ *         i.e. a tile stores 16-value piece c of all its rows, row after
+ *         row, then piece c + 1: lane r of a wave reads its row's piece c
+ *         while the wave reads one contiguous kilobyte.
  */
 #ifndef BQ8_H
 #define BQ8_H
@@ -151,8 +160,10 @@ bq8_status q6k_pack_expand(const void *raw, int64_t N, int64_t K, void *pack, in
  *          M = 6, row0 = 1, rows = 5); 1 <= rows <= 8, row0 + rows <= M.
  * ids:     int32 [rows]; ids[r] is the greedy token id of row row0 + r.
  * scratch: device workspace of at least q6k_lmhead_top1_scratch_bytes(N, K,
- *          rows) bytes, 16-byte aligned (quantized rows and per-row keys);
- *          its contents on entry do not matter.
+ *          rows) bytes, 16-byte aligned (quantized rows and one key per
+ *          workgroup and row); its contents on entry do not matter.  Three
+ *          kernels run in stream order: quantize, fused projection + per-
+ *          workgroup reduction, final reduction.
  * Shape: 1 <= N < 2^31 - 1, K >= 256, K % 256 == 0, N*K < 2^40.
  * Tie rule: among equal maximal logits the lowest id wins; -0 equals +0.
  * Equal weight rows give bitwise equal logits, so planted duplicate rows

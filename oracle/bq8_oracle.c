@@ -277,12 +277,50 @@ void orc_q4_0_q8_1_gemv(const uint8_t *w, int64_t N, int64_t K, const uint8_t *x
 /* d * scales[e/16] * (u - 32) for element e.                                */
 /*                                                                           */
 /* READING (pack layout; the pages give only "exact expected layout and byte */
-/* count" and the total): three planar row-major arrays,                     */
-/*   Q  int8 [N][K]        at offset 0,                                      */
-/*   SC int8 [N][K/16]     at offset N*K,                                    */
-/*   D  fp16 [N][K/256]    at offset N*K + N*K/16,                           */
-/* so the size is N*K + N*K/16 + 2*N*K/256 bytes.                            */
+/* count" and the total).  Three planes, each split into tiles of 64         */
+/* consecutive rows (the last tile holds the N % 64 remaining rows, if any); */
+/* for row n, t = n / 64, n0 = 64 t, rows_t = min(64, N - n0), r = n - n0:   */
+/*   Q  int8, plane at 0:            quant k of row n at                      */
+/*        n0*K + ((k/16)*rows_t + r)*16 + k%16                                */
+/*      (a tile stores the 16-value piece c of all its rows, row after row,  */
+/*      then piece c + 1, ...);                                              */
+/*   SC int8, plane at N*K:          subscale j (= k/16) of row n at          */
+/*        n0*(K/16) + ((j/16)*rows_t + r)*16 + j%16                           */
+/*      (per superblock s, the 16 subscales of every row of the tile);       */
+/*   D  fp16, plane at N*K + N*K/16: scale of superblock s of row n at        */
+/*        element n0*(K/256) + s*rows_t + r.                                  */
+/* The size is N*K + N*K/16 + 2*N*K/256 bytes.                               */
 /* ------------------------------------------------------------------------ */
+
+#define PACK_TILE 64
+
+static int64_t tile_rows(int64_t n, int64_t N, int64_t *n0, int64_t *r)
+{
+    *n0 = n / PACK_TILE * PACK_TILE;
+    *r = n - *n0;
+    return (N - *n0 < PACK_TILE) ? N - *n0 : PACK_TILE;
+}
+
+/* byte offset of quant (n, k) in the Q plane */
+static int64_t pack_q_at(int64_t n, int64_t k, int64_t N, int64_t K)
+{
+    int64_t n0, r, rows_t = tile_rows(n, N, &n0, &r);
+    return n0 * K + ((k / 16) * rows_t + r) * 16 + k % 16;
+}
+
+/* byte offset of subscale (n, j) in the SC plane, j = k / 16 */
+static int64_t pack_sc_at(int64_t n, int64_t j, int64_t N, int64_t K)
+{
+    int64_t n0, r, rows_t = tile_rows(n, N, &n0, &r);
+    return n0 * (K / 16) + ((j / 16) * rows_t + r) * 16 + j % 16;
+}
+
+/* element index of superblock scale (n, s) in the D plane */
+static int64_t pack_d_at(int64_t n, int64_t s, int64_t N, int64_t K)
+{
+    int64_t n0, r, rows_t = tile_rows(n, N, &n0, &r);
+    return n0 * (K / QK_K) + s * rows_t + r;
+}
 
 void orc_q6k_decode(const uint8_t *raw, int64_t N, int64_t K, int8_t *q, int8_t *sc, uint16_t *d)
 {
@@ -336,19 +374,27 @@ void orc_q6k_pack_expand(const uint8_t *raw, int64_t N, int64_t K, uint8_t *pack
     int8_t *Q = (int8_t *)pack;
     int8_t *SC = (int8_t *)(pack + N * K);
     uint8_t *D = pack + N * K + N * (K / 16);
-    const int64_t nsb = N * (K / QK_K);
+    const int64_t ns = K / QK_K;
 #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < nsb; ++i) {
-        uint16_t dbits;
-        orc_q6k_decode(raw + i * Q6_K_BYTES, 1, QK_K, Q + i * QK_K, SC + i * 16, &dbits);
-        wr16(D + 2 * i, dbits);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t s = 0; s < ns; ++s) {
+            int8_t q[QK_K], sc[16];
+            uint16_t dbits;
+            orc_q6k_decode(raw + (n * ns + s) * Q6_K_BYTES, 1, QK_K, q, sc, &dbits);
+            for (int e = 0; e < QK_K; ++e)
+                Q[pack_q_at(n, s * QK_K + e, N, K)] = q[e];
+            for (int j = 0; j < 16; ++j)
+                SC[pack_sc_at(n, s * 16 + j, N, K)] = sc[j];
+            wr16(D + 2 * pack_d_at(n, s, N, K), dbits);
+        }
     }
 }
 
 /* logits[r][n] = sum_k Wq6[n][k] * X[r][k] over the pack's dequantized
  * values d * sc * q and the Q8_1 rows' values d_x * q_x, in binary64.
  * bound[r][n] = sum over 32-blocks of |block contribution|.
- * pack: expanded Q6_K [N][K]; xq: Q8_1 [rows][K/32]; logits, bound: [rows][N]. */
+ * pack: expanded Q6_K of an [N][K] weight (layout above); xq: Q8_1
+ * [rows][K/32]; logits, bound: [rows][N]. */
 void orc_q6k_pack_logits(const uint8_t *pack, int64_t N, int64_t K, const uint8_t *xq,
                          int64_t rows, double *logits, double *bound)
 {
@@ -364,11 +410,12 @@ void orc_q6k_pack_logits(const uint8_t *pack, int64_t N, int64_t K, const uint8_
                 const uint8_t *xb = xq + (r * nb + b) * Q8_1_BYTES;
                 const int64_t k0 = b * QK;
                 double dx = (double)orc_f16_to_f32(rd16(xb));
-                double dw = (double)orc_f16_to_f32(rd16(D + 2 * (n * (K / QK_K) + k0 / QK_K)));
+                double dw = (double)orc_f16_to_f32(rd16(D + 2 * pack_d_at(n, k0 / QK_K, N, K)));
                 double tb = 0.0;
                 for (int j = 0; j < QK; ++j) {
                     int64_t k = k0 + j;
-                    double wv = dw * (double)SC[n * (K / 16) + k / 16] * (double)Q[n * K + k];
+                    double wv = dw * (double)SC[pack_sc_at(n, k / 16, N, K)] *
+                                (double)Q[pack_q_at(n, k, N, K)];
                     double xv = dx * (double)(int8_t)xb[4 + j];
                     tb += wv * xv;
                 }

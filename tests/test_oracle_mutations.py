@@ -43,8 +43,12 @@ MUTATIONS = {
         "int hi = (qh[32 * h + l] >> (2 * (3 - c))) & 3;",
         ["test_oracle_q6k.py"]),
     "q6k_subscale_index_per_32": (
-        "double wv = dw * (double)SC[n * (K / 16) + k / 16] * (double)Q[n * K + k];",
-        "double wv = dw * (double)SC[n * (K / 16) + k / 32] * (double)Q[n * K + k];",
+        "double wv = dw * (double)SC[pack_sc_at(n, k / 16, N, K)] *",
+        "double wv = dw * (double)SC[pack_sc_at(n, k / 32, N, K)] *",
+        ["test_oracle_q6k.py"]),
+    "pack_tile_row_major": (
+        "return n0 * K + ((k / 16) * rows_t + r) * 16 + k % 16;",
+        "return n0 * K + r * K + k;",
         ["test_oracle_q6k.py"]),
     "top1_last_of_ties": (
         "if (best < 0 || v > bv) {",

@@ -78,16 +78,29 @@ def test_decode_worked_example(orc):
 
 
 def test_pack_planes(orc):
+    """The pack's layout, checked value by value from the decoded raw blocks:
+    tiles of 64 rows (the last one ragged), each tile storing 16-value pieces
+    of all its rows piece after piece (Q), the 16 subscales of each
+    superblock row after row (SC), and the superblock scales (D)."""
     rng = np.random.default_rng(23)
-    N, K = 6, 768
+    N, K = 70, 768            # one full tile and a ragged tile of 6 rows; 3 superblocks
     raw = synth.q6k_raw_weights(rng, N, K)
     pack = orc.q6k_pack_expand(raw, N, K)
     q, sc, d = orc.q6k_decode(raw, N, K)
     assert pack.size == orc.q6k_pack_bytes(N, K)
-    assert (pack[:N * K].view(np.int8).reshape(N, K) == q).all()
-    assert (pack[N * K:N * K + N * K // 16].view(np.int8).reshape(N, K // 16) == sc).all()
-    tail = pack[N * K + N * K // 16:]
-    assert (tail.view("<u2").reshape(N, K // 256) == d).all()
+    Qp = pack[:N * K].view(np.int8)
+    SCp = pack[N * K:N * K + N * K // 16].view(np.int8)
+    Dp = pack[N * K + N * K // 16:].view("<u2")
+    for t0, rows_t in [(0, 64), (64, 6)]:
+        tq = Qp[t0 * K:(t0 + rows_t) * K].reshape(K // 16, rows_t, 16)
+        assert (tq.transpose(1, 0, 2).reshape(rows_t, K) == q[t0:t0 + rows_t]).all()
+        ts = SCp[t0 * K // 16:(t0 + rows_t) * K // 16].reshape(K // 256, rows_t, 16)
+        assert (ts.transpose(1, 0, 2).reshape(rows_t, K // 16) == sc[t0:t0 + rows_t]).all()
+        td = Dp[t0 * K // 256:(t0 + rows_t) * K // 256].reshape(K // 256, rows_t)
+        assert (td.T == d[t0:t0 + rows_t]).all()
+    # a tile's piece c of its 64 rows is one contiguous kilobyte
+    c, r = 5, 17
+    assert (Qp[(c * 64 + r) * 16:(c * 64 + r) * 16 + 16] == q[r, 16 * c:16 * c + 16]).all()
 
 
 def _xq(orc, rows, K, seed):
@@ -115,7 +128,7 @@ def test_constant_closed_form(orc, qv, scv, qx):
 
 def test_exact_rational_bruteforce(orc):
     rng = np.random.default_rng(24)
-    N, K, rows = 3, 512, 2       # two superblocks, 16 subscales each
+    N, K, rows = 3, 512, 2       # two superblocks, 16 subscales each (one ragged tile)
     raw = synth.q6k_raw_weights(rng, N, K)
     pack = orc.q6k_pack_expand(raw, N, K)
     xq = _xq(orc, rows, K, 25)
@@ -142,7 +155,7 @@ def test_exact_rational_bruteforce(orc):
 
 def test_numpy_dequantize_matmul(orc):
     rng = np.random.default_rng(26)
-    N, K, rows = 300, 1024, 5
+    N, K, rows = 300, 1024, 5    # four full 64-row tiles and a ragged one of 44 rows
     raw = synth.q6k_raw_weights(rng, N, K)
     pack = orc.q6k_pack_expand(raw, N, K)
     xq = _xq(orc, rows, K, 27)
