@@ -69,6 +69,11 @@ def _declare(L):
     L.orc_q4_0_decode.argtypes = [_P, _I64, _I64, _P, _P]
     L.orc_q4_0_encode.argtypes = [_P, _P, _I64, _I64, _P]
     L.orc_q4_0_q8_1_gemv.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
+    L.orc_q4_0_pack_bytes.restype = _I64
+    L.orc_q4_0_pack_bytes.argtypes = [_I64, _I64]
+    L.orc_q4_0_pack.argtypes = [_P, _I64, _I64, _P]
+    L.orc_q4_0_unpack.argtypes = [_P, _I64, _I64, _P]
+    L.orc_q4_0p_q8_1_gemv.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
     L.orc_q6k_decode.argtypes = [_P, _I64, _I64, _P, _P, _P]
     L.orc_q6k_encode.argtypes = [_P, _P, _P, _I64, _I64, _P]
     L.orc_q6k_pack_bytes.restype = _I64
@@ -156,6 +161,37 @@ def q4_0_gemv(w, N: int, K: int, xq, M: int):
     y = np.empty((M, N), np.float64)
     bound = np.empty((M, N), np.float64)
     lib().orc_q4_0_q8_1_gemv(_ptr(w), N, K, _ptr(xq), M, _ptr(y), _ptr(bound))
+    return y, bound
+
+
+# ------------------------------------------------------------ packed Q4_0
+def q4_0_pack(w, N: int, K: int) -> np.ndarray:
+    """Q4_0 [N][K/32] blocks -> the offline-packed layout (K % 512 == 0)."""
+    assert K % 512 == 0
+    w = _c(w, np.uint8)
+    assert w.size == N * K // QK * Q4_0_BYTES
+    out = np.empty(int(lib().orc_q4_0_pack_bytes(N, K)), np.uint8)
+    lib().orc_q4_0_pack(_ptr(w), N, K, _ptr(out))
+    return out
+
+
+def q4_0_unpack(wp, N: int, K: int) -> np.ndarray:
+    """The inverse of q4_0_pack: Q4_0 bytes [N][K/32*18]."""
+    wp = _c(wp, np.uint8)
+    out = np.empty((N, K // QK * Q4_0_BYTES), np.uint8)
+    lib().orc_q4_0_unpack(_ptr(wp), N, K, _ptr(out))
+    return out
+
+
+def q4_0p_gemv(wp, N: int, K: int, xq, M: int):
+    """(y, bound) as q4_0_gemv, reading the packed layout."""
+    wp = _c(wp, np.uint8)
+    xq = _c(xq, np.uint8)
+    assert wp.size == N * K // QK * Q4_0_BYTES
+    assert xq.size == M * K // QK * Q8_1_BYTES
+    y = np.empty((M, N), np.float64)
+    bound = np.empty((M, N), np.float64)
+    lib().orc_q4_0p_q8_1_gemv(_ptr(wp), N, K, _ptr(xq), M, _ptr(y), _ptr(bound))
     return y, bound
 
 

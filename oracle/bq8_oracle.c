@@ -264,6 +264,126 @@ void orc_q4_0_q8_1_gemv(const uint8_t *w, int64_t N, int64_t K, const uint8_t *x
 }
 
 /* ------------------------------------------------------------------------ */
+/* Offline-packed Q4_0 ([CLOSURE] "What materially worked": the verifier's   */
+/* width-6 gate/up and down projections ran on offline-packed weights).      */
+/*                                                                           */
+/* READING (the pages name the packing, not a format): the same 18 bytes per */
+/* 32 weights, regrouped.  Requires K % 512 == 0 (nb = K/32 a multiple of    */
+/* 16).  Rows form tiles of 16 (the last one ragged): for row n,             */
+/* n0 = 16*(n/16), r = n - n0, rows_t = min(16, N - n0).  Two planes:        */
+/*   QS, N*nb*16 bytes at 0: element j of block b of row n, with half        */
+/*     h = j/16 and jj = j%16, is nibble (jj >= 8 ? high : low) of byte      */
+/*       n0*nb*16 + u*(4*rows_t*16) + (g*rows_t + r)*16 + 8*v + (jj % 8)     */
+/*     where u = b/4, v = (b%4)/2, g = 2*(b%2) + h;                           */
+/*   D, N*nb*2 bytes at N*nb*16: the fp16 scale of block b of row n is       */
+/*     element n0*nb + ((b/16)*2 + b%2)*rows_t*8 + r*8 + (b%16)/2.           */
+/* The nibble codes are the Q4_0 codes (value d*(q - 8)).                    */
+/* ------------------------------------------------------------------------ */
+
+#define Q4P_TILE 16
+
+static int64_t q4p_tile(int64_t n, int64_t N, int64_t *n0, int64_t *r)
+{
+    *n0 = n / Q4P_TILE * Q4P_TILE;
+    *r = n - *n0;
+    return (N - *n0 < Q4P_TILE) ? N - *n0 : Q4P_TILE;
+}
+
+/* byte of the QS plane holding element j of block b of row n; *hi = nibble */
+static int64_t q4p_qs_at(int64_t n, int64_t b, int j, int64_t N, int64_t nb, int *hi)
+{
+    int64_t n0, r, rows_t = q4p_tile(n, N, &n0, &r);
+    const int h = j / 16, jj = j % 16;
+    const int64_t u = b / 4, v = (b % 4) / 2, g = 2 * (b % 2) + h;
+    *hi = (jj >= 8);
+    return n0 * nb * 16 + u * (4 * rows_t * 16) + (g * rows_t + r) * 16 + 8 * v + (jj % 8);
+}
+
+/* element of the D plane holding the scale of block b of row n */
+static int64_t q4p_d_at(int64_t n, int64_t b, int64_t N, int64_t nb)
+{
+    int64_t n0, r, rows_t = q4p_tile(n, N, &n0, &r);
+    return n0 * nb + ((b / 16) * 2 + b % 2) * rows_t * 8 + r * 8 + (b % 16) / 2;
+}
+
+int64_t orc_q4_0_pack_bytes(int64_t N, int64_t K)
+{
+    return N * (K / QK) * Q4_0_BYTES;
+}
+
+void orc_q4_0_pack(const uint8_t *w, int64_t N, int64_t K, uint8_t *wp)
+{
+    const int64_t nb = K / QK;
+    uint8_t *QS = wp;
+    uint8_t *D = wp + N * nb * 16;
+    memset(wp, 0, (size_t)(N * nb * Q4_0_BYTES));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *wb = w + (n * nb + b) * Q4_0_BYTES;
+            for (int j = 0; j < QK; ++j) {
+                int nib = (j < 16) ? (wb[2 + j] & 0x0F) : (wb[2 + j - 16] >> 4);
+                int hi;
+                int64_t at = q4p_qs_at(n, b, j, N, nb, &hi);
+                QS[at] |= (uint8_t)(hi ? nib << 4 : nib);
+            }
+            wr16(D + 2 * q4p_d_at(n, b, N, nb), rd16(wb));
+        }
+}
+
+void orc_q4_0_unpack(const uint8_t *wp, int64_t N, int64_t K, uint8_t *w)
+{
+    const int64_t nb = K / QK;
+    const uint8_t *QS = wp;
+    const uint8_t *D = wp + N * nb * 16;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < nb; ++b) {
+            uint8_t *wb = w + (n * nb + b) * Q4_0_BYTES;
+            memset(wb, 0, Q4_0_BYTES);
+            wr16(wb, rd16(D + 2 * q4p_d_at(n, b, N, nb)));
+            for (int j = 0; j < QK; ++j) {
+                int hi;
+                int64_t at = q4p_qs_at(n, b, j, N, nb, &hi);
+                int nib = hi ? (QS[at] >> 4) : (QS[at] & 0x0F);
+                wb[2 + (j % 16)] |= (uint8_t)((j < 16) ? nib : nib << 4);
+            }
+        }
+}
+
+/* The Q4_0 x Q8_1 product of orc_q4_0_q8_1_gemv, reading the packed layout:
+ * same dequantized values, same order of summation. */
+void orc_q4_0p_q8_1_gemv(const uint8_t *wp, int64_t N, int64_t K, const uint8_t *xq, int64_t M,
+                         double *y, double *bound)
+{
+    const int64_t nb = K / QK;
+    const uint8_t *QS = wp;
+    const uint8_t *D = wp + N * nb * 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t *xb = xq + (m * nb + b) * Q8_1_BYTES;
+                double dw = (double)orc_f16_to_f32(rd16(D + 2 * q4p_d_at(n, b, N, nb)));
+                double dx = (double)orc_f16_to_f32(rd16(xb));
+                double tb = 0.0;
+                for (int j = 0; j < QK; ++j) {
+                    int hi;
+                    int64_t at = q4p_qs_at(n, b, j, N, nb, &hi);
+                    int nib = hi ? (QS[at] >> 4) : (QS[at] & 0x0F);
+                    double wv = dw * (double)(nib - 8);
+                    double xv = dx * (double)(int8_t)xb[4 + j];
+                    tb += wv * xv;
+                }
+                acc += tb;
+                mag += fabs(tb);
+            }
+            y[m * N + n] = acc;
+            bound[m * N + n] = mag;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Q6_K weights and the expanded pack ([TOP1] "Why this was slow": the       */
 /* output tensor is expanded once into signed int8 quants, int8 subscales    */
 /* and fp16 superblock scales; "Memory and startup": pack byte count).       */

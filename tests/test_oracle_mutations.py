@@ -19,12 +19,16 @@ SRC = os.path.join(ROOT, "oracle", "bq8_oracle.c")
 # name: (original text, planted mistake, pin files expected to catch it)
 MUTATIONS = {
     "q4_0_drops_minus8": (
-        "double wv = dw * (double)(nib - 8);",
-        "double wv = dw * (double)(nib);",
+        "int nib = (j < 16) ? (wb[2 + j] & 0x0F) : (wb[2 + j - 16] >> 4);\n"
+        "                    double wv = dw * (double)(nib - 8);",
+        "int nib = (j < 16) ? (wb[2 + j] & 0x0F) : (wb[2 + j - 16] >> 4);\n"
+        "                    double wv = dw * (double)(nib);",
         ["test_oracle_q4_0.py"]),
     "q4_0_nibbles_swapped": (
-        "int nib = (j < 16) ? (wb[2 + j] & 0x0F) : (wb[2 + j - 16] >> 4);",
-        "int nib = (j < 16) ? (wb[2 + j] >> 4) : (wb[2 + j - 16] & 0x0F);",
+        "int nib = (j < 16) ? (wb[2 + j] & 0x0F) : (wb[2 + j - 16] >> 4);\n"
+        "                    double wv = dw * (double)(nib - 8);",
+        "int nib = (j < 16) ? (wb[2 + j] >> 4) : (wb[2 + j - 16] & 0x0F);\n"
+        "                    double wv = dw * (double)(nib - 8);",
         ["test_oracle_q4_0.py"]),
     "q8_1_rounds_half_even": (
         "double a = floor(fabs((double)t) + 0.5); /* exact in binary64 */",
@@ -46,6 +50,14 @@ MUTATIONS = {
         "double wv = dw * (double)SC[pack_sc_at(n, k / 16, N, K)] *",
         "double wv = dw * (double)SC[pack_sc_at(n, k / 32, N, K)] *",
         ["test_oracle_q6k.py"]),
+    "q4_0_packed_nibble_choice": (
+        "*hi = (jj >= 8);",
+        "*hi = (jj % 2);",
+        ["test_oracle_q4_0_packed.py"]),
+    "q4_0_packed_scale_parity": (
+        "return n0 * nb + ((b / 16) * 2 + b % 2) * rows_t * 8 + r * 8 + (b % 16) / 2;",
+        "return n0 * nb + ((b / 16) * 2 + (b / 2) % 2) * rows_t * 8 + r * 8 + (b % 16) / 2;",
+        ["test_oracle_q4_0_packed.py"]),
     "pack_tile_row_major": (
         "return n0 * K + ((k / 16) * rows_t + r) * 16 + k % 16;",
         "return n0 * K + r * K + k;",
