@@ -4,19 +4,26 @@
 
 A step is one verifier projection of the ffn_up workload: Q8_1 quantization
 of the six f32 activation rows [6][5120] followed by the Q4_0 x Q8_1
-product against an [17408][5120] Q4_0 weight (q8_1_quantize +
-q4_0_mmvq_m6).  Twelve copies of the weight (601 MB, more than twice the
-256 MB last-level cache) are used round-robin so every step streams its
-weight from HBM; inputs are resident in device memory before timing starts.
+product against an [17408][5120] Q4_0 weight held in the library's
+offline-packed layout (q8_1_quantize + q4_0_mmvq_packed, M = 6).  The
+packing -- the same 18 bytes per 32 weights, regrouped once at load time,
+as the pages' verifier did with its offline-packed width-6 projections --
+is not timed, like the Q6_K expansion of the LM head.  Twelve copies of the
+weight (601 MB, more than twice the 256 MB last-level cache) are used
+round-robin so every step streams its weight from HBM; inputs are resident
+in device memory before timing starts.
 
 Printed: one JSON line with the effective weight bandwidth of a step
-(value, GB/s), the mmvq kernel's roofline against the 8 TB/s HBM peak, the
-fused Q6_K LM-head top-1 time on the lm_head workload, the per-M times of the
-down_sweep workload, ms per full width-6 pass of the 64-layer verifier FFN
-stream (q4_0_ffn_stream), and the oracle's CPU throughput on a bounded sample.
+(value, GB/s), the product kernel's roofline against the 8 TB/s HBM peak,
+the same projection on the weight's plain GGUF block layout
+(q4_0_mmvq_m6), the fused Q6_K LM-head top-1 time on the lm_head workload,
+the per-M times of the down_sweep workload on both layouts, ms per full
+width-6 pass of the 64-layer verifier FFN stream (both layouts), and the
+oracle's CPU throughput on a bounded sample.
 
 Profiling helpers (one kernel family per process, for rocprofv3):
-    python bench.py --profile-target mmvq_m6|lmhead_top1|down_sweep|stream|copy [--reps R]
+    python bench.py --profile-target \\
+        packed_m6|mmvq_m6|lmhead_top1|down_sweep|stream|stream_packed|copy [--reps R]
 """
 from __future__ import annotations
 
@@ -34,8 +41,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROTATE = 12
-PMC_RECORD = os.path.join(ROOT, "profiles", "pmc_q4_0_mmvq_m6_ffn_up.json")
-KERNEL_SOURCES = ["block_quantized_gemv_q8_amd/csrc/q4_0_mmvq.hip",
+PMC_RECORD = os.path.join(ROOT, "profiles", "pmc_q4_0_mmvq_packed_m6_ffn_up.json")
+KERNEL_SOURCES = ["block_quantized_gemv_q8_amd/csrc/q4_0_packed.hip",
                   "block_quantized_gemv_q8_amd/csrc/bq8_dev.h"]
 
 METRIC = "µs + effective weight GB/s (% of HBM peak) per Q4_0 M=6 proj; LM-head top-1 µs"
@@ -76,31 +83,51 @@ class Timer:
         self.ms = self.a.elapsed_time(self.b)
 
 
+def time_calls(torch, fn, reps, warm=10):
+    """µs per call of fn(i), i = call index, after `warm` untimed calls."""
+    for i in range(warm):
+        fn(i)
+    with Timer(torch) as t:
+        for i in range(reps):
+            fn(i)
+    return t.ms * 1000.0 / reps
+
+
+def capture(torch, fn, n):
+    """A HIP graph of the calls fn(0) .. fn(n-1), captured on torch's capture
+    stream (every library call enqueues on torch's current stream).  fn(0)
+    runs once eagerly first, so one-time set-up stays outside the graph."""
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
 def setup_ffn_up(torch, bq, synth):
     cfg = synth.FFN_UP
     N, K, M = cfg["N"], cfg["K"], cfg["M"]
     w, x = synth.ffn_up()
     w0 = torch.from_numpy(w).to("cuda")
     ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+    wps = [bq.q4_0_pack(wi) for wi in ws]
     xd = torch.from_numpy(x).to("cuda")
     xq = torch.empty((M, K // 32 * 36), dtype=torch.uint8, device="cuda")
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    return dict(N=N, K=K, M=M, ws=ws, x=xd, xq=xq, y=y, w_host=w, x_host=x)
+    return dict(N=N, K=K, M=M, ws=ws, wps=wps, x=xd, xq=xq, y=y)
 
 
-def step_ffn_up(bq, s, i):
+def step_packed(bq, s, i):
+    bq.q8_1_quantize(s["x"], s["xq"])
+    bq.q4_0_mmvq_packed(s["wps"][i % ROTATE], s["N"], s["K"], s["xq"], s["M"], s["y"])
+
+
+def step_standard(bq, s, i):
     bq.q8_1_quantize(s["x"], s["xq"])
     bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
-
-
-def time_mmvq_only(torch, bq, s, reps):
-    bq.q8_1_quantize(s["x"], s["xq"])
-    for i in range(20):
-        bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
-    with Timer(torch) as t:
-        for i in range(reps):
-            bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
-    return t.ms * 1000.0 / reps
 
 
 def setup_lm_head(torch, bq, synth):
@@ -118,16 +145,9 @@ def setup_lm_head(torch, bq, synth):
                 rows=cfg["rows"])
 
 
-def time_lm_head(torch, bq, s, reps):
-    def call():
-        bq.q6k_lmhead_top1(s["pack"], s["N"], s["K"], s["x"], s["row0"], s["rows"], s["ids"],
-                           s["scratch"])
-    for _ in range(5):
-        call()
-    with Timer(torch) as t:
-        for _ in range(reps):
-            call()
-    return t.ms * 1000.0 / reps
+def lm_head_call(bq, s):
+    bq.q6k_lmhead_top1(s["pack"], s["N"], s["K"], s["x"], s["row0"], s["rows"], s["ids"],
+                       s["scratch"])
 
 
 def time_down_sweep(torch, bq, synth, reps):
@@ -136,44 +156,63 @@ def time_down_sweep(torch, bq, synth, reps):
     w, x = synth.down_sweep()
     w0 = torch.from_numpy(w).to("cuda")
     ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+    wps = [bq.q4_0_pack(wi) for wi in ws]
     xq = bq.q8_1_quantize(torch.from_numpy(x).to("cuda"))
+    wb = q4_0_bytes(N, K)
     out = {}
     for m in cfg["Ms"]:
         f = getattr(bq, f"q4_0_mmvq_m{m}")
+        xm = xq[:m]
         y = torch.empty((m, N), dtype=torch.float32, device="cuda")
-        for i in range(10):
-            f(ws[i % ROTATE], xq, y)
-        with Timer(torch) as t:
-            for i in range(reps):
-                f(ws[i % ROTATE], xq, y)
-        us = t.ms * 1000.0 / reps
-        out[str(m)] = {"us": round(us, 3), "GBps": round(q4_0_bytes(N, K) / us / 1e3, 1)}
+        usp = time_calls(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % ROTATE], N, K, xm, m, y),
+                         reps)
+        us = time_calls(torch, lambda i: f(ws[i % ROTATE], xm, y), reps)
+        out[str(m)] = {"packed_us": round(usp, 3), "packed_GBps": round(wb / usp / 1e3, 1),
+                       "gguf_us": round(us, 3), "gguf_GBps": round(wb / us / 1e3, 1)}
     return out
 
 
-def time_stream(torch, bq, synth, passes):
+def time_stream(torch, bq, synth, passes, packed):
     """ms per full width-6 pass of the 64-layer verifier FFN stream (weights
     generated on the device, 9.6 GB, far beyond the caches); median, p10 and
     p90 over `passes` passes, each bracketed by its own HIP events."""
     cfg = synth.STREAM
     L, M, H, F = cfg["layers"], cfg["M"], cfg["hidden"], cfg["ffn"]
     wg, wu, wd = synth.stream_weights_device(L, H, F)
+    if packed:
+        for ws in (wg, wu, wd):
+            for i in range(L):
+                ws[i] = bq.q4_0_pack(ws[i])
     tables = tuple(bq.stream_weight_table(ws) for ws in (wg, wu, wd))
     x0 = torch.from_numpy(synth.stream_x0()).to("cuda")
-    y, work = bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, tables=tables)
+    kw = dict(tables=tables, packed=packed, ffn=F)
+    y, work = bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, **kw)
     for _ in range(2):
-        bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, y=y, work=work, tables=tables)
+        bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, y=y, work=work, **kw)
     ms = []
     for _ in range(passes):
         with Timer(torch) as t:
-            bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, y=y, work=work, tables=tables)
+            bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, y=y, work=work, **kw)
         ms.append(t.ms)
+    # the same pass captured once as a HIP graph and replayed
+    g = capture(torch, lambda i: bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, y=y, work=work, **kw), 1)
+    gms = []
+    for _ in range(passes):
+        with Timer(torch) as t:
+            g.replay()
+        gms.append(t.ms)
     wbytes = L * (2 * q4_0_bytes(F, H) + q4_0_bytes(H, F))
     med = float(np.median(ms))
+    gmed = float(np.median(gms))
     return {"layers": L, "M": M, "hidden": H, "ffn": F, "passes": passes,
+            "layout": "packed" if packed else "gguf",
             "ms_median": round(med, 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
             "ms_p90": round(float(np.percentile(ms, 90)), 4), "weight_bytes": wbytes,
-            "GBps": round(wbytes / med / 1e6, 1), "launches_per_pass": 5 * L}
+            "GBps": round(wbytes / med / 1e6, 1), "launches_per_pass": 5 * L,
+            "graph_ms_median": round(gmed, 4),
+            "graph_ms_p10": round(float(np.percentile(gms, 10)), 4),
+            "graph_ms_p90": round(float(np.percentile(gms, 90)), 4),
+            "graph_GBps": round(wbytes / gmed / 1e6, 1)}
 
 
 def cpu_baseline(synth, budget_s=10.0):
@@ -200,7 +239,7 @@ def cpu_baseline(synth, budget_s=10.0):
                       f"[17408x5120], M=6) in {el:.1f} s"}
 
 
-def pmc_traffic(per_launch_algo_bytes):
+def pmc_traffic():
     """HBM bytes per launch from the committed rocprofv3 counter record,
     if it was taken on the current kernel source; else None."""
     try:
@@ -225,20 +264,21 @@ def profile_target(torch, bq, synth, target, reps):
         torch.cuda.synchronize()
         log(f"copy: {reps} x {n} bytes")
         return
-    if target == "mmvq_m6":
+    if target in ("packed_m6", "mmvq_m6"):
         s = setup_ffn_up(torch, bq, synth)
-        bq.q8_1_quantize(s["x"], s["xq"])
+        step = step_packed if target == "packed_m6" else step_standard
         for i in range(reps):
-            bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
+            step(bq, s, i)
     elif target == "lmhead_top1":
         s = setup_lm_head(torch, bq, synth)
         for _ in range(reps):
-            bq.q6k_lmhead_top1(s["pack"], s["N"], s["K"], s["x"], s["row0"], s["rows"], s["ids"],
-                               s["scratch"])
+            lm_head_call(bq, s)
     elif target == "down_sweep":
         time_down_sweep(torch, bq, synth, reps)
-    elif target == "stream":
-        time_stream(torch, bq, synth, reps)
+    elif target in ("stream", "stream_packed"):
+        time_stream(torch, bq, synth, reps, target == "stream_packed")
+    else:
+        raise SystemExit(f"unknown profile target {target}")
     torch.cuda.synchronize()
     log(f"{target}: done")
 
@@ -270,26 +310,45 @@ def main():
         profile_target(torch, bq, synth, args.profile_target, args.reps)
         return
 
-    log("bench: ffn_up setup")
+    log("bench: ffn_up setup (12 weight copies, packed once)")
     s = setup_ffn_up(torch, bq, synth)
     N, K, M = s["N"], s["K"], s["M"]
     wbytes = q4_0_bytes(N, K)
+    # The timed steps run as one captured HIP graph of `steps` consecutive
+    # steps (each step: its own quantize and product launches), so Python's
+    # per-call launch cost does not set the pace; warm-up steps run eagerly.
     for i in range(args.warmup):
-        step_ffn_up(bq, s, i)
+        step_packed(bq, s, i)
+    g = capture(torch, lambda i: step_packed(bq, s, i), args.steps)
+    g.replay()
     with Timer(torch) as t:
-        for i in range(args.steps):
-            step_ffn_up(bq, s, i)
+        g.replay()
     step_us = t.ms * 1000.0 / args.steps
     value = wbytes / step_us / 1e3  # GB/s
-    log(f"bench: step {step_us:.3f} us, {value:.1f} GB/s")
+    log(f"bench: step (quantize + packed M=6, graph) {step_us:.3f} us, {value:.1f} GB/s")
+    with Timer(torch) as t:
+        for i in range(args.steps):
+            step_packed(bq, s, i)
+    eager_step_us = t.ms * 1000.0 / args.steps
+    log(f"bench: step eager {eager_step_us:.3f} us")
+    del g
 
-    mmvq_us = time_mmvq_only(torch, bq, s, max(args.steps, 100))
-    achieved = wbytes / mmvq_us / 1e3
-    log(f"bench: mmvq_m6 {mmvq_us:.3f} us, {achieved:.1f} GB/s")
+    bq.q8_1_quantize(s["x"], s["xq"])
+    reps = max(args.steps, 100)
+    packed_us = time_calls(torch, lambda i: bq.q4_0_mmvq_packed(
+        s["wps"][i % ROTATE], N, K, s["xq"], M, s["y"]), reps, warm=20)
+    achieved = wbytes / packed_us / 1e3
+    log(f"bench: q4_0_mmvq_packed M=6 {packed_us:.3f} us, {achieved:.1f} GB/s")
+    std_us = time_calls(torch, lambda i: bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"]),
+                        reps, warm=20)
+    std_step_us = time_calls(torch, lambda i: step_standard(bq, s, i), reps, warm=20)
+    log(f"bench: q4_0_mmvq_m6 (GGUF layout) {std_us:.3f} us; step {std_step_us:.3f} us")
+    quant_us = time_calls(torch, lambda i: bq.q8_1_quantize(s["x"], s["xq"]), reps, warm=20)
+    del s
 
     log("bench: lm_head setup")
     lm = setup_lm_head(torch, bq, synth)
-    lm_us = time_lm_head(torch, bq, lm, 50)
+    lm_us = time_calls(torch, lambda i: lm_head_call(bq, lm), 50, warm=5)
     pack_bytes = lm["pack"].numel()
     log(f"bench: lmhead_top1 {lm_us:.2f} us, {pack_bytes / lm_us / 1e3:.1f} GB/s")
     del lm
@@ -298,16 +357,19 @@ def main():
     sweep = time_down_sweep(torch, bq, synth, 100)
     log(f"bench: sweep {sweep}")
 
-    log("bench: stream")
-    stream = time_stream(torch, bq, synth, 20)
-    log(f"bench: stream {stream['ms_median']:.3f} ms per pass, {stream['GBps']} GB/s")
+    log("bench: stream (packed)")
+    stream_p = time_stream(torch, bq, synth, 20, packed=True)
+    log(f"bench: stream packed {stream_p['ms_median']:.3f} ms per pass, {stream_p['GBps']} GB/s")
+    log("bench: stream (GGUF layout)")
+    stream_s = time_stream(torch, bq, synth, 10, packed=False)
+    log(f"bench: stream gguf {stream_s['ms_median']:.3f} ms per pass")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         cpu = cpu_baseline(synth)
 
-    traffic = pmc_traffic(wbytes)
+    traffic = pmc_traffic()
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -319,23 +381,31 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_0 x q8_1 (int8 dot, f32 accumulate)",
+        "dtype": "q4_0 x q8_1 (int8 MFMA dot, f32 accumulate)",
         "data": "synthetic (seeded; weights and activations resident in HBM, 12 rotating "
                 "weight copies)",
         "config": {
             "workload": "ffn_up: Q8_1 quantize of [6][5120] f32 + Q4_0 [17408x5120] M=6 "
-                        "projection",
+                        "projection (weight in the offline-packed layout, packed once, untimed)",
             "N": N, "K": K, "M": M,
             "weight_bytes": wbytes,
             "step_us": round(step_us, 3),
-            "mmvq_us": round(mmvq_us, 3),
+            "step_timing": "HIP graph of all timed steps, replayed once",
+            "step_eager_us": round(eager_step_us, 3),
+            "packed_mmvq_us": round(packed_us, 3),
+            "quantize_us": round(quant_us, 3),
             "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
             "pct_hbm_peak_mmvq": round(100 * achieved / HBM_PEAK_GBS, 2),
+            "gguf_layout": {"q4_0_mmvq_m6_us": round(std_us, 3),
+                            "GBps": round(wbytes / std_us / 1e3, 1),
+                            "step_us": round(std_step_us, 3)},
             "lmhead_top1_us": round(lm_us, 2),
             "lmhead_pack_bytes": pack_bytes,
             "lmhead_GBps": round(pack_bytes / lm_us / 1e3, 1),
+            "lmhead_pct_hbm_peak": round(100 * pack_bytes / lm_us / 1e3 / HBM_PEAK_GBS, 2),
             "down_sweep": sweep,
-            "stream_64_layer_pass": stream,
+            "stream_64_layer_pass": stream_p,
+            "stream_64_layer_pass_gguf_layout": stream_s,
             "device": torch.cuda.get_device_name(0),
         },
         "roofline": {
@@ -345,7 +415,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "q4_0_mmvq_m6 (ffn_up, 50,135,040 algorithmic bytes per launch)",
+            "kernel": "q4_0_mmvq_packed M=6 (ffn_up, 50,135,040 algorithmic weight bytes per "
+                      "launch)",
         },
         "cpu_baseline": cpu,
     }

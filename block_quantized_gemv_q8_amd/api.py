@@ -74,11 +74,17 @@ def lib() -> ctypes.CDLL:
         L.silu_mul_q8_1.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
         L.rms_norm_q8_1.restype = _ST
         L.rms_norm_q8_1.argtypes = [_P, _I64, _I64, ctypes.c_float, _P, _P, _P]
+        L.q4_0_pack_bytes.restype = _I64
+        L.q4_0_pack_bytes.argtypes = [_I64, _I64]
+        L.q4_0_pack.restype = _ST
+        L.q4_0_pack.argtypes = [_P, _I64, _I64, _P, _I64, _P]
+        L.q4_0_mmvq_packed.restype = _ST
+        L.q4_0_mmvq_packed.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
         L.q4_0_ffn_stream_layout.restype = _ST
         L.q4_0_ffn_stream_layout.argtypes = [_I64, _I64, _I64, ctypes.POINTER(_I64)]
-        L.q4_0_ffn_stream.restype = _ST
-        L.q4_0_ffn_stream.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_float, _P,
-                                      _P, _I64, _P]
+        for f in (L.q4_0_ffn_stream, L.q4_0_ffn_stream_packed):
+            f.restype = _ST
+            f.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_float, _P, _P, _I64, _P]
         _lib = L
     return _lib
 
@@ -89,8 +95,15 @@ def _check(fn: str, status: int):
         raise Bq8Error(fn, status, msg)
 
 
+try:  # the raw handle of the current stream without building a Stream object
+    _raw_stream = torch._C._cuda_getCurrentRawStream
+except AttributeError:  # pragma: no cover - older torch
+    def _raw_stream(device):
+        return torch.cuda.current_stream(device).cuda_stream
+
+
 def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return _raw_stream(torch.cuda.current_device())
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
@@ -238,6 +251,33 @@ def rms_norm_q8_1(y: torch.Tensor, eps: float, xq: torch.Tensor | None = None,
     return xq
 
 
+# ------------------------------------------------------------ packed Q4_0
+def q4_0_pack_bytes(N: int, K: int) -> int:
+    return int(lib().q4_0_pack_bytes(N, K))
+
+
+def q4_0_pack(w: torch.Tensor, wp: torch.Tensor | None = None) -> torch.Tensor:
+    """Q4_0 uint8 [N][K/32*18] -> the offline-packed layout, uint8 [bytes]."""
+    N, K = _q4_0_shape(w)
+    nbytes = q4_0_pack_bytes(N, K)
+    if nbytes < 0:
+        raise Bq8Error("q4_0_pack", 2, status_string(2))
+    wp = _out(wp, (nbytes,), torch.uint8, w.device, "wp")
+    _check("q4_0_pack", lib().q4_0_pack(_dev(w, "w", torch.uint8), N, K,
+                                        _dev(wp, "wp", torch.uint8), wp.numel(), _stream()))
+    return wp
+
+
+def q4_0_mmvq_packed(wp: torch.Tensor, N: int, K: int, xq: torch.Tensor, M: int,
+                     y: torch.Tensor | None = None) -> torch.Tensor:
+    """y f32 [M][N] = packed Q4_0 weight times the M Q8_1 rows of xq."""
+    y = _out(y, (M, N), torch.float32, wp.device, "y")
+    _check("q4_0_mmvq_packed", lib().q4_0_mmvq_packed(
+        _dev(wp, "wp", torch.uint8), N, K, _dev(xq, "xq", torch.uint8), M,
+        _dev(y, "y", torch.float32), _stream()))
+    return y
+
+
 # ------------------------------------------------------- verifier stream
 def q4_0_ffn_stream_layout(M: int, hidden: int, ffn: int) -> dict:
     """Byte offsets of the stage buffers in the stream workspace and its size."""
@@ -253,33 +293,45 @@ def stream_weight_table(ws) -> ctypes.Array:
 
 def q4_0_ffn_stream(w_gate, w_up, w_down, x0: torch.Tensor, eps: float,
                     y: torch.Tensor | None = None, work: torch.Tensor | None = None,
-                    tables=None):
+                    tables=None, packed: bool = False, hidden: int | None = None,
+                    ffn: int | None = None):
     """Enqueue a whole verifier FFN pass over len(w_gate) layers.
 
-    w_gate/w_up: Q4_0 uint8 [ffn][hidden/32*18] per layer; w_down: Q4_0 uint8
-    [hidden][ffn/32*18]; x0: f32 [M][hidden].  Returns (y, work); the stage
-    buffers of the last layer are views of work (see stream_stages).
-    ``tables`` may hold the three prebuilt stream_weight_table arrays."""
-    M, hidden = x0.shape
+    Standard weights: w_gate/w_up Q4_0 uint8 [ffn][hidden/32*18] per layer,
+    w_down Q4_0 uint8 [hidden][ffn/32*18].  packed=True: the q4_0_pack of each
+    matrix (uint8 vectors of the same byte count).  x0: f32 [M][hidden].
+    Returns (y, work); the stage buffers of the last layer are views of work
+    (see stream_stages).  ``tables`` may hold the three prebuilt
+    stream_weight_table arrays."""
+    M, hid = x0.shape
     layers = len(w_gate)
     if layers < 1 or len(w_up) != layers or len(w_down) != layers:
         raise ValueError("w_gate, w_up and w_down must list the same number of layers (>= 1)")
-    ffn, k = _q4_0_shape(w_gate[0])
-    if k != hidden:
-        raise ValueError("gate weights must have K = hidden")
-    for w in (*w_gate, *w_up):
-        if _q4_0_shape(w) != (ffn, hidden):
-            raise ValueError("every gate/up weight must be Q4_0 [ffn][hidden/32]")
-    for w in w_down:
-        if _q4_0_shape(w) != (hidden, ffn):
-            raise ValueError("every down weight must be Q4_0 [hidden][ffn/32]")
-    lay = q4_0_ffn_stream_layout(M, hidden, ffn)
-    y = _out(y, (M, hidden), torch.float32, x0.device, "y")
+    if packed:
+        if ffn is None:
+            raise ValueError("packed weights need ffn")
+        nbytes = q4_0_pack_bytes(ffn, hid)
+        for w in (*w_gate, *w_up, *w_down):
+            if w.dim() != 1 or w.numel() != nbytes:
+                raise ValueError("every packed weight must be a uint8 vector of q4_0_pack_bytes")
+    else:
+        ffn, k = _q4_0_shape(w_gate[0])
+        if k != hid:
+            raise ValueError("gate weights must have K = hidden")
+        for w in (*w_gate, *w_up):
+            if _q4_0_shape(w) != (ffn, hid):
+                raise ValueError("every gate/up weight must be Q4_0 [ffn][hidden/32]")
+        for w in w_down:
+            if _q4_0_shape(w) != (hid, ffn):
+                raise ValueError("every down weight must be Q4_0 [hidden][ffn/32]")
+    lay = q4_0_ffn_stream_layout(M, hid, ffn)
+    y = _out(y, (M, hid), torch.float32, x0.device, "y")
     work = _out(work, (lay["total"],), torch.uint8, x0.device, "work")
     tg, tu, td = tables if tables is not None else (
         stream_weight_table(w_gate), stream_weight_table(w_up), stream_weight_table(w_down))
-    _check("q4_0_ffn_stream", lib().q4_0_ffn_stream(
-        tg, tu, td, layers, M, hidden, ffn, _dev(x0, "x0", torch.float32), float(eps),
+    fn = lib().q4_0_ffn_stream_packed if packed else lib().q4_0_ffn_stream
+    _check("q4_0_ffn_stream" + ("_packed" if packed else ""), fn(
+        tg, tu, td, layers, M, hid, ffn, _dev(x0, "x0", torch.float32), float(eps),
         _dev(y, "y", torch.float32), _dev(work, "work", torch.uint8), work.numel(), _stream()))
     return y, work
 
@@ -298,5 +350,6 @@ def stream_stages(work: torch.Tensor, M: int, hidden: int, ffn: int) -> dict:
 __all__ = ["Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "q4_0_mmvq",
            *[f"q4_0_mmvq_m{m}" for m in range(1, MAX_M + 1)], "q6k_pack_bytes",
            "q6k_pack_expand", "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1",
-           "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_ffn_stream_layout", "q4_0_ffn_stream",
+           "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed",
+           "q4_0_ffn_stream_layout", "q4_0_ffn_stream",
            "stream_weight_table", "stream_stages", "synth"]

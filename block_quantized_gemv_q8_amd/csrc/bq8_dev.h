@@ -19,6 +19,27 @@ constexpr int Q6_K_BYTES = 210; // ql[128] qh[64] scales[16] fp16 d
 constexpr int WAVE = 64;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+// Order this wave's LDS writes before its reads of other lanes' data (a
+// wave's LDS operations complete in order; the fences stop the compiler from
+// moving accesses across).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// s_waitcnt immediate for gfx9-family encodings: vmcnt = `vm` (6 bits split
+// across two fields), expcnt and lgkmcnt left at their maximum (no wait).
+constexpr int waitcnt_vmcnt(int vm)
+{
+    return (vm & 0xF) | (0x7 << 4) | (0xF << 8) | ((vm >> 4) << 14);
+}
 
 // Exact binary16 -> binary32 of raw bits (v_cvt_f32_f16).
 __device__ __forceinline__ float h2f(uint32_t bits)

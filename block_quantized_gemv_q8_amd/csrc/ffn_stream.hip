@@ -59,16 +59,20 @@ BQ8_EXPORT bq8_status q4_0_ffn_stream_layout(int64_t M, int64_t hidden, int64_t 
     return BQ8_OK;
 }
 
-BQ8_EXPORT bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *const *w_up,
-                                      const void *const *w_down, int64_t layers, int64_t M,
-                                      int64_t hidden, int64_t ffn, const float *x0, float eps,
-                                      float *y, void *work, int64_t work_bytes, void *stream)
+typedef bq8_status (*proj_fn)(const void *w, int64_t N, int64_t K, const void *xq, int64_t M,
+                              float *y, void *stream);
+
+static bq8_status ffn_stream(proj_fn proj, int64_t align_k, const void *const *w_gate,
+                             const void *const *w_up, const void *const *w_down, int64_t layers,
+                             int64_t M, int64_t hidden, int64_t ffn, const float *x0, float eps,
+                             float *y, void *work, int64_t work_bytes, void *stream)
 {
     if (!w_gate || !w_up || !w_down || !x0 || !y || !work)
         return BQ8_ERR_NULL;
     StreamLayout L;
     if (layers < 1 || layers > (int64_t(1) << 20) || !stream_layout(M, hidden, ffn, &L) ||
-        !(eps > 0.0f) || ffn * (hidden / QK) * Q4_0_BYTES >= (int64_t(1) << 40))
+        !(eps > 0.0f) || ffn * (hidden / QK) * Q4_0_BYTES >= (int64_t(1) << 40) ||
+        hidden % align_k != 0 || ffn % align_k != 0)
         return BQ8_ERR_SHAPE;
     for (int64_t l = 0; l < layers; ++l) {
         if (!w_gate[l] || !w_up[l] || !w_down[l])
@@ -94,13 +98,44 @@ BQ8_EXPORT bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *con
         if (l > 0)
             st = rms_norm_q8_1(y, M, hidden, eps, nullptr, xq, stream);
         if (st == BQ8_OK)
-            st = q4_0_mmvq(w_gate[l], ffn, hidden, xq, M, g, stream);
+            st = proj(w_gate[l], ffn, hidden, xq, M, g, stream);
         if (st == BQ8_OK)
-            st = q4_0_mmvq(w_up[l], ffn, hidden, xq, M, u, stream);
+            st = proj(w_up[l], ffn, hidden, xq, M, u, stream);
         if (st == BQ8_OK)
             st = silu_mul_q8_1(g, u, M, ffn, nullptr, hq, stream);
         if (st == BQ8_OK)
-            st = q4_0_mmvq(w_down[l], hidden, ffn, hq, M, y, stream);
+            st = proj(w_down[l], hidden, ffn, hq, M, y, stream);
     }
     return st;
+}
+
+static bq8_status proj_standard(const void *w, int64_t N, int64_t K, const void *xq, int64_t M,
+                                float *y, void *stream)
+{
+    return q4_0_mmvq(w, N, K, xq, M, y, stream);
+}
+
+static bq8_status proj_packed(const void *w, int64_t N, int64_t K, const void *xq, int64_t M,
+                              float *y, void *stream)
+{
+    return q4_0_mmvq_packed(w, N, K, xq, M, y, stream);
+}
+
+BQ8_EXPORT bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *const *w_up,
+                                      const void *const *w_down, int64_t layers, int64_t M,
+                                      int64_t hidden, int64_t ffn, const float *x0, float eps,
+                                      float *y, void *work, int64_t work_bytes, void *stream)
+{
+    return ffn_stream(proj_standard, QK, w_gate, w_up, w_down, layers, M, hidden, ffn, x0, eps, y,
+                      work, work_bytes, stream);
+}
+
+BQ8_EXPORT bq8_status q4_0_ffn_stream_packed(const void *const *w_gate, const void *const *w_up,
+                                             const void *const *w_down, int64_t layers,
+                                             int64_t M, int64_t hidden, int64_t ffn,
+                                             const float *x0, float eps, float *y, void *work,
+                                             int64_t work_bytes, void *stream)
+{
+    return ffn_stream(proj_packed, 512, w_gate, w_up, w_down, layers, M, hidden, ffn, x0, eps, y,
+                      work, work_bytes, stream);
 }

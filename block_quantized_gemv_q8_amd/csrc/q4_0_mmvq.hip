@@ -94,15 +94,6 @@ __device__ __forceinline__ void chunk_all(const uint32_t *wd, const uint8_t *__r
     (chunk_block<J, M>(wd, xq, nb, b0 + J, acc), ...);
 }
 
-// Order this wave's LDS writes before its reads of other lanes' data (a
-// wave's LDS operations complete in order; the fences stop the compiler from
-// moving accesses across).
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 constexpr int CHUNK_BYTES = 8 * Q4_0_BYTES;           // 144: eight blocks, 16-byte aligned
 constexpr int CHUNK_PIECES = CHUNK_BYTES / 16;         // 9 x 16 bytes
@@ -232,9 +223,6 @@ __global__ __launch_bounds__(1024) void q4_0_mmvq_dot4_kernel(const uint8_t *__r
 // wave's LDS stage, and read back in MFMA operand order.  The next chunk's
 // loads are issued before the current chunk is computed, and compute reads
 // only LDS, so the wait for one chunk never waits for the next.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void global_void_t;
 
 template <int M, int CB, int NST>
 struct MfmaShape {
@@ -405,7 +393,7 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_mfma_kernel(const uint8_t *__re
     // outstanding and every older one -- chunk k's -- must have landed.
     constexpr int YOUNGER = (NST - 1) * LOADS;
     static_assert(YOUNGER <= 63, "vmcnt field");
-    constexpr int WAIT_IMM = (YOUNGER & 0xF) | (0x7 << 4) | (0xF << 8) | ((YOUNGER >> 4) << 14);
+    constexpr int WAIT_IMM = waitcnt_vmcnt(YOUNGER);
     const int nchunks = nb / CB;
     if (wave < nchunks) {
         const int mine = (nchunks - wave + S - 1) / S; // this wave's chunk count

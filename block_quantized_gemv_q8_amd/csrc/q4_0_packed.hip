@@ -1,0 +1,420 @@
+// Offline-packed Q4_0 and its M = 1..17 matrix-vector product.
+//
+// "Qwen3.6 27B Q4_0 DFlash/SYCL closure", "What materially worked": the
+// verifier's width-6 gate/up and down projections ran on offline-packed
+// weights.  This pack keeps the 18 bytes per 32 weights and regroups them so
+// that the MFMA kernel's weight operand arrives straight from memory into
+// registers: in each 16-row tile, the 16 rows' nibbles for one (4-block
+// group, lane group) are 256 contiguous bytes, so one wave load instruction
+// (16 bytes per lane) reads one contiguous kilobyte and every lane receives
+// exactly the nibbles of its MFMA B operand -- no LDS staging, no byte
+// realignment of the 18-byte blocks.  Layout (K % 512 == 0; include/bq8.h):
+//
+//   tile of row n: n0 = 16*(n/16), r = n - n0, rows_t = min(16, N - n0)
+//   QS plane (N*nb*16 bytes at 0): element j of block b of row n, with
+//     h = j/16, jj = j%16, is nibble (jj >= 8 ? high : low) of byte
+//       n0*nb*16 + u*(4*rows_t*16) + (g*rows_t + r)*16 + 8*v + jj%8
+//     where u = b/4, v = (b%4)/2, g = 2*(b%2) + h;
+//   D plane (N*nb*2 bytes at N*nb*16): scale of block b of row n at element
+//       n0*nb + ((b/16)*2 + b%2)*rows_t*8 + r*8 + (b%16)/2.
+//
+// The product is the one of q4_0_mmvq.hip (block-diagonal int8 MFMA, exact
+// per-block integer dots, d_w * d_x scaling and binary32 accumulation in a
+// fixed order); only where the operands come from differs.
+#include "bq8_dev.h"
+
+namespace bq8 {
+
+constexpr int PK_TILE = 16;
+constexpr int PK_CB = 8; // blocks per chunk: two 4-block groups
+
+__device__ __forceinline__ int pk_tile(int n, int N, int &n0, int &r)
+{
+    n0 = n / PK_TILE * PK_TILE;
+    r = n - n0;
+    return (N - n0 < PK_TILE) ? N - n0 : PK_TILE;
+}
+
+// ------------------------------------------------------------- packing
+// One thread per (row, block): the block's 32 codes go to two 8-byte pieces
+// (one per half), its scale to the D plane.
+__global__ __launch_bounds__(256) void q4_0_pack_kernel(const uint8_t *__restrict__ w, int N,
+                                                        int nb, uint8_t *__restrict__ QS,
+                                                        uint16_t *__restrict__ D)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)N * nb)
+        return;
+    const int n = (int)(i / nb), b = (int)(i - (int64_t)n * nb);
+    int n0, r;
+    const int rows_t = pk_tile(n, N, n0, r);
+    const uint8_t *blk = w + i * Q4_0_BYTES;
+    uint8_t qs[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        qs[j] = blk[2 + j];
+    const int u = b / 4, v = (b % 4) / 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        // element 16h + jj: code of qs[jj] (low nibble, h = 0) or (high, h = 1)
+        uint32_t word[2] = {0u, 0u};
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const uint32_t code = h ? (qs[jj] >> 4) : (qs[jj] & 0x0Fu);
+            const int byte = jj % 8;
+            const int shift = 8 * (byte % 4) + (jj >= 8 ? 4 : 0);
+            word[byte / 4] |= code << shift;
+        }
+        const int g = 2 * (b % 2) + h;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(
+            QS + (int64_t)n0 * nb * 16 + (int64_t)u * (4 * rows_t * 16) + (g * rows_t + r) * 16 +
+            8 * v);
+        dst[0] = word[0];
+        dst[1] = word[1];
+    }
+    D[(int64_t)n0 * nb + ((b / 16) * 2 + b % 2) * rows_t * 8 + r * 8 + (b % 16) / 2] =
+        (uint16_t)(blk[0] | (blk[1] << 8));
+}
+
+// --------------------------------------------------------------- product
+// One workgroup owns a 16-row tile; its S waves take the tile's 8-block
+// chunks round-robin.  Per chunk a wave loads, straight into registers, its
+// lane's 2 x 16 bytes of packed nibbles and 8 bytes of scales, and stages the
+// chunk's M Q8_1 activation blocks in LDS (global_load_lds, 16 bytes per
+// lane) together with their scales as binary32.  The registers are double
+// buffered: chunk k+1 is issued before chunk k is computed, and the only
+// wait in the loop is for chunk k itself.
+//
+// MFMA mapping (v_mfma_i32_16x16x64_i8, one per block pair (2t, 2t+1) of the
+// chunk): B lane l holds weight row c16 = l%16, k range 16*(l/16) .. +15,
+// i.e. half h = (l/16)%2 of block 2t + hb, hb = l/32 -- exactly the lane's
+// 8 packed bytes, unpacked to 16 signed bytes 16*(q - 8); A row c16 holds
+// activation row m = c16%8 (+8s) for block c16/8, zero outside its block's k
+// range (lanes outside it read a zeroed LDS row).  Results are 16x the exact
+// dots (scaled by 1/16 at the end, exact).
+template <int M>
+struct PkShape {
+    static constexpr int MS = (M + 7) / 8;
+    static constexpr int XRUN = PK_CB * Q8_1_BYTES;          // activation bytes per row per chunk
+    static constexpr int XPIECES = M * XRUN / 16;
+    static constexpr int LOADS = (XPIECES + WAVE - 1) / WAVE; // DMA instructions per chunk
+    static constexpr int DXOFF = LOADS * WAVE * 16;           // f32 d_x [PK_CB][8*MS]
+    static constexpr int STAGE = DXOFF + PK_CB * 8 * MS * 4;
+    static constexpr int ZOFF = 2 * STAGE;                    // XRUN zero bytes after the ring
+    static constexpr int WAVE_LDS = ZOFF + XRUN;
+};
+
+template <int M>
+__global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__restrict__ QS,
+                                                                const uint16_t *__restrict__ D,
+                                                                int N, int nb,
+                                                                const uint8_t *__restrict__ xq,
+                                                                float *__restrict__ y)
+{
+    using SH = PkShape<M>;
+    constexpr int MS = SH::MS, LOADS = SH::LOADS;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+    const int n0 = blockIdx.x * PK_TILE;
+    const int rows_t = (N - n0 < PK_TILE) ? N - n0 : PK_TILE;
+    uint8_t *ring = smem + (size_t)wave * SH::WAVE_LDS;
+    uint8_t *zero = ring + SH::ZOFF;
+    for (int i = lane; i < SH::XRUN / 4; i += WAVE)
+        reinterpret_cast<uint32_t *>(zero)[i] = 0u;
+
+    const int c16 = lane & 15;
+    const int g = lane >> 4;
+    const int h = g & 1;
+    const int hb = g >> 1;
+    const int r = c16 < rows_t ? c16 : rows_t - 1; // ragged tile: repeat the last row
+    bool a_on[MS];
+    uint32_t aoff[MS];
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+        const int m = 8 * s + (c16 & 7);
+        a_on[s] = ((c16 >> 3) == hb) && (m < M);
+        aoff[s] = (uint32_t)(a_on[s] ? m : 0) * SH::XRUN;
+    }
+    // activation pieces: piece p = 64j + lane of a chunk is 16 bytes of row m
+    const uint8_t *xbase[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int p = j * WAVE + lane;
+        if (p < SH::XPIECES) {
+            const int m = p / (SH::XRUN / 16);
+            const int q = p - m * (SH::XRUN / 16);
+            xbase[j] = xq + (size_t)m * nb * Q8_1_BYTES + 16 * q;
+        } else {
+            xbase[j] = xq; // padding slot: a valid address, never read back
+        }
+    }
+    // this lane's weight piece of 4-block group u: wt + u * group_bytes
+    const uint8_t *wt = QS + (size_t)n0 * nb * 16 + (size_t)(g * rows_t + r) * 16;
+    const size_t group_bytes = (size_t)4 * rows_t * 16;
+    // scales of this lane's blocks (parity hb) of 16-block group q: dt + q * (2 rows_t 8)
+    const uint16_t *dt = D + (size_t)n0 * nb + (size_t)hb * rows_t * 8 + (size_t)r * 8;
+    const size_t dgroup = (size_t)2 * rows_t * 8;
+
+    auto issue = [&](int c, int st, u32x4(&wv)[2], uint32_t(&dv)[2]) {
+        uint8_t *dst = ring + st * SH::STAGE;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j)
+            __builtin_amdgcn_global_load_lds((global_void_t *)(xbase[j] + (size_t)c * SH::XRUN),
+                                             (lds_void_t *)(dst + j * WAVE * 16), 16, 0, 0);
+        wv[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(wt + (size_t)(2 * c) * group_bytes));
+        wv[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(wt + (size_t)(2 * c + 1) * group_bytes));
+        // blocks 8c + 2i + hb, i = 0..3: elements 4*(c%2) .. +3 of group c/2
+        const uint32_t *dq = reinterpret_cast<const uint32_t *>(dt + (size_t)(c >> 1) * dgroup +
+                                                                (c & 1) * 4);
+        dv[0] = dq[0];
+        dv[1] = dq[1];
+    };
+
+    float acc[MS][4];
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            acc[s][x] = 0.0f;
+
+    auto compute = [&](int st, const u32x4(&wv)[2], const uint32_t(&dv)[2]) {
+        const uint8_t *stage = ring + st * SH::STAGE;
+        float *dxs = reinterpret_cast<float *>(ring + st * SH::STAGE + SH::DXOFF);
+        // d_x of the chunk's blocks as f32: dxs[b*8*MS + m], 0 past M
+#pragma unroll
+        for (int i = lane; i < PK_CB * 8 * MS; i += WAVE) {
+            const int b = i / (8 * MS), m = i - (i / (8 * MS)) * (8 * MS);
+            const uint16_t bits = *reinterpret_cast<const uint16_t *>(
+                stage + (m < M ? m : 0) * SH::XRUN + b * Q8_1_BYTES);
+            dxs[i] = (m < M) ? h2f(bits) : 0.0f;
+        }
+        const uint8_t *abase[MS];
+#pragma unroll
+        for (int s = 0; s < MS; ++s)
+            abase[s] = a_on[s] ? stage + aoff[s] : zero;
+        wave_lds_sync();
+#pragma unroll
+        for (int t = 0; t < PK_CB / 2; ++t) {
+            const int bl = 2 * t + hb; // this lane's block within the chunk
+            i32x4 A[MS];
+            f32x4 dx[MS];
+#pragma unroll
+            for (int s = 0; s < MS; ++s) {
+                const uint32_t *xb =
+                    reinterpret_cast<const uint32_t *>(abase[s] + bl * Q8_1_BYTES);
+                A[s][0] = (int)xb[1 + 4 * h];
+                A[s][1] = (int)xb[2 + 4 * h];
+                A[s][2] = (int)xb[3 + 4 * h];
+                A[s][3] = (int)xb[4 + 4 * h];
+                dx[s] = *reinterpret_cast<const f32x4 *>(dxs + bl * 8 * MS + 8 * s + 4 * h);
+            }
+            // 8 packed bytes: byte i < 4 holds elements i (low) and 8+i (high),
+            // byte 4+i elements 4+i and 12+i, of the lane's 16-element range
+            const uint32_t w0 = wv[t >> 1][2 * (t & 1)], w1 = wv[t >> 1][2 * (t & 1) + 1];
+            i32x4 B;
+            B[0] = (int)(((w0 << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
+            B[1] = (int)(((w1 << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
+            B[2] = (int)((w0 & 0xF0F0F0F0u) ^ 0x80808080u);
+            B[3] = (int)((w1 & 0xF0F0F0F0u) ^ 0x80808080u);
+            const float dw = h2f(dv[t >> 1] >> (16 * (t & 1)));
+#pragma unroll
+            for (int s = 0; s < MS; ++s) {
+                const i32x4 Dm =
+                    __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s], B, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    acc[s][x] = fmaf((float)Dm[x], dw * dx[s][x], acc[s][x]);
+            }
+        }
+        wave_lds_sync();
+    };
+
+    const int nchunks = nb / PK_CB;
+    if (wave < nchunks) {
+        const int mine = (nchunks - wave + S - 1) / S;
+        u32x4 wn[2], wc[2];
+        uint32_t dn[2], dc[2];
+        issue(wave, 0, wn, dn);
+        for (int k = 0; k < mine; ++k) {
+            // Taking chunk k out of the prefetch registers waits for exactly
+            // its loads (nothing younger is in flight yet); the explicit wait
+            // also covers its activation DMA, which the compiler does not track.
+            wc[0] = wn[0];
+            wc[1] = wn[1];
+            dc[0] = dn[0];
+            dc[1] = dn[1];
+            __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
+            // past the wave's last chunk the prefetch repeats it (cache hits, never used)
+            const int kn = k + 1 < mine ? k + 1 : mine - 1;
+            issue(wave + S * kn, (k + 1) & 1, wn, dn);
+            compute(k & 1, wc, dc);
+        }
+    }
+
+    // the two blocks of each pair (lanes l and l+32), then the S waves in order
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            acc[s][x] += __shfl_xor(acc[s][x], 32, 64);
+    __builtin_amdgcn_s_waitcnt(0); // no load may still be writing the LDS reused below
+    __syncthreads();
+    constexpr int SLOTS = MS * 4;
+    float *partial = reinterpret_cast<float *>(smem); // [S][SLOTS][32]
+    if (lane < 32) {
+#pragma unroll
+        for (int s = 0; s < MS; ++s)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                partial[(wave * SLOTS + s * 4 + x) * 32 + lane] = acc[s][x];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x) {
+        const int slot = idx >> 5, l = idx & 31;
+        const int s = slot >> 2, x = slot & 3;
+        const int m = 8 * s + 4 * (l >> 4) + x;
+        const int nn = n0 + (l & 15);
+        float sacc = 0.0f;
+        for (int v = 0; v < S; ++v)
+            sacc += partial[(v * SLOTS + slot) * 32 + l];
+        if (m < M && nn < N)
+            y[(size_t)m * N + nn] = sacc * 0.0625f;
+    }
+}
+
+// Largest dynamic LDS a workgroup may use on the current device (queried
+// once; 160 KB on gfx950).
+static int64_t packed_lds_limit()
+{
+    static int64_t cached = -1;
+    if (cached < 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            v <= 0)
+            v = 65536;
+        cached = v;
+    }
+    return cached;
+}
+
+// Waves per workgroup: enough for about 2048 waves in flight (two per tile
+// on the ffn_up shape, seven on the down shape), at most eight, never more
+// than the tile has chunks or the LDS holds.
+static int packed_waves(int64_t N, int nb, int64_t wave_lds, int64_t limit)
+{
+    const int64_t tiles = (N + PK_TILE - 1) / PK_TILE;
+    int64_t s = (2048 + tiles - 1) / tiles;
+    if (s < 2)
+        s = 2;
+    if (s > 8)
+        s = 8;
+    if (s > nb / PK_CB)
+        s = nb / PK_CB;
+    while (s > 1 && s * wave_lds > limit)
+        --s;
+    return (int)(s < 1 ? 1 : s);
+}
+
+template <int M>
+static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const void *xq, float *y,
+                                hipStream_t stream)
+{
+    using SH = PkShape<M>;
+    const int nb = (int)(K / QK);
+    const int64_t limit = packed_lds_limit();
+    const int s = packed_waves(N, nb, SH::WAVE_LDS, limit);
+    const int64_t ring = (int64_t)s * SH::WAVE_LDS;
+    const int64_t partial = (int64_t)s * SH::MS * 4 * 32 * (int64_t)sizeof(float);
+    const int64_t lds = ring > partial ? ring : partial;
+    if (lds > limit)
+        return BQ8_ERR_SHAPE;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)q4_0_mmvq_packed_kernel<M>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit) != hipSuccess)
+            return BQ8_ERR_HIP;
+        attr_set = true;
+    }
+    const uint8_t *QS = wp;
+    const uint16_t *D = reinterpret_cast<const uint16_t *>(wp + N * nb * 16);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((q4_0_mmvq_packed_kernel<M>), dim3((unsigned)((N + PK_TILE - 1) / PK_TILE)),
+                       dim3(WAVE * s), (size_t)lds, stream, QS, D, (int)N, nb,
+                       (const uint8_t *)xq, y);
+    return launch_status();
+}
+
+static bool packed_shape_ok(int64_t N, int64_t K)
+{
+    return N >= 1 && N < (int64_t(1) << 31) && K >= 512 && K % 512 == 0 &&
+           K <= (int64_t(1) << 26) && N * (K / QK) * Q4_0_BYTES < (int64_t(1) << 40);
+}
+
+} // namespace bq8
+
+using namespace bq8;
+
+BQ8_EXPORT int64_t q4_0_pack_bytes(int64_t N, int64_t K)
+{
+    if (!packed_shape_ok(N, K))
+        return -1;
+    return N * (K / QK) * Q4_0_BYTES;
+}
+
+BQ8_EXPORT bq8_status q4_0_pack(const void *w, int64_t N, int64_t K, void *wp, int64_t wp_bytes,
+                                void *stream)
+{
+    if (!w || !wp)
+        return BQ8_ERR_NULL;
+    if (!packed_shape_ok(N, K))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(w, 2) || !aligned(wp, 16))
+        return BQ8_ERR_ALIGN;
+    if (wp_bytes != q4_0_pack_bytes(N, K))
+        return BQ8_ERR_SIZE;
+    const int nb = (int)(K / QK);
+    const int64_t items = N * nb;
+    uint8_t *QS = (uint8_t *)wp;
+    uint16_t *D = reinterpret_cast<uint16_t *>(QS + N * nb * 16);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(q4_0_pack_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, (const uint8_t *)w, (int)N, nb, QS, D);
+    return launch_status();
+}
+
+BQ8_EXPORT bq8_status q4_0_mmvq_packed(const void *wp, int64_t N, int64_t K, const void *xq,
+                                       int64_t M, float *y, void *stream)
+{
+    if (!wp || !xq || !y)
+        return BQ8_ERR_NULL;
+    if (!packed_shape_ok(N, K) || M < 1 || M > 17 || M * K >= (int64_t(1) << 31))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(wp, 16) || !aligned(xq, 4) || !aligned(y, 4))
+        return BQ8_ERR_ALIGN;
+    const uint8_t *p = (const uint8_t *)wp;
+    hipStream_t s = (hipStream_t)stream;
+    switch (M) {
+    case 1: return packed_launch<1>(p, N, K, xq, y, s);
+    case 2: return packed_launch<2>(p, N, K, xq, y, s);
+    case 3: return packed_launch<3>(p, N, K, xq, y, s);
+    case 4: return packed_launch<4>(p, N, K, xq, y, s);
+    case 5: return packed_launch<5>(p, N, K, xq, y, s);
+    case 6: return packed_launch<6>(p, N, K, xq, y, s);
+    case 7: return packed_launch<7>(p, N, K, xq, y, s);
+    case 8: return packed_launch<8>(p, N, K, xq, y, s);
+    case 9: return packed_launch<9>(p, N, K, xq, y, s);
+    case 10: return packed_launch<10>(p, N, K, xq, y, s);
+    case 11: return packed_launch<11>(p, N, K, xq, y, s);
+    case 12: return packed_launch<12>(p, N, K, xq, y, s);
+    case 13: return packed_launch<13>(p, N, K, xq, y, s);
+    case 14: return packed_launch<14>(p, N, K, xq, y, s);
+    case 15: return packed_launch<15>(p, N, K, xq, y, s);
+    case 16: return packed_launch<16>(p, N, K, xq, y, s);
+    default: return packed_launch<17>(p, N, K, xq, y, s);
+    }
+}

@@ -132,6 +132,35 @@ bq8_status q4_0_mmvq(const void *w, int64_t N, int64_t K, const void *xq, int64_
                      void *stream);
 
 /* ------------------------------------------------------------------------
+ * Offline-packed Q4_0 (the closure page's width-6 gate/up and down
+ * projections ran on offline-packed weights, "What materially worked").  The
+ * pack holds the same 18 bytes per 32 weights, regrouped so that the MFMA
+ * kernel's weight operand is one contiguous kilobyte per wave load.
+ * Requires K % 512 == 0.  For row n: n0 = 16*(n/16), r = n - n0,
+ * rows_t = min(16, N - n0), nb = K/32.
+ *   QS plane (N*nb*16 bytes at 0): element j of block b of row n, with
+ *     h = j/16, jj = j%16, is nibble (jj >= 8 ? high : low) of byte
+ *       n0*nb*16 + u*(4*rows_t*16) + (g*rows_t + r)*16 + 8*v + jj%8,
+ *     u = b/4, v = (b%4)/2, g = 2*(b%2) + h; nibble values are the Q4_0
+ *     codes q (value d*(q - 8)).
+ *   D plane (N*nb*2 bytes at N*nb*16): the fp16 scale of block b of row n
+ *     is element n0*nb + ((b/16)*2 + b%2)*rows_t*8 + r*8 + (b%16)/2.
+ * q4_0_pack_bytes: host; N*K/32*18, or -1 if the shape is invalid.
+ * q4_0_pack: w Q4_0 [N][K/32] (2-byte aligned) -> wp (16-byte aligned,
+ *   wp_bytes == q4_0_pack_bytes(N, K), fully overwritten).  Run once, at
+ *   load time.
+ * q4_0_mmvq_packed: y[m][n] = sum_k W[n][k] X[m][k] as q4_0_mmvq_m<M>, for
+ *   M = 1..17, from the packed weight; xq, y as there.  Results equal the
+ *   standard-layout entry points up to the binary32 summation order.
+ * Shape: 1 <= N < 2^31, 512 <= K <= 2^26, K % 512 == 0.
+ * ---------------------------------------------------------------------- */
+int64_t q4_0_pack_bytes(int64_t N, int64_t K);
+bq8_status q4_0_pack(const void *w, int64_t N, int64_t K, void *wp, int64_t wp_bytes,
+                     void *stream);
+bq8_status q4_0_mmvq_packed(const void *wp, int64_t N, int64_t K, const void *xq, int64_t M,
+                            float *y, void *stream);
+
+/* ------------------------------------------------------------------------
  * Q6_K expansion (run once, at load time).  The fused-head page expands the
  * output tensor once into signed int8 quants, int8 subscales and fp16
  * superblock scales ("Why this was slow") and accepts the pack only with its
@@ -228,6 +257,14 @@ bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *const *w_up,
                            const void *const *w_down, int64_t layers, int64_t M, int64_t hidden,
                            int64_t ffn, const float *x0, float eps, float *y, void *work,
                            int64_t work_bytes, void *stream);
+
+/* The same pass on offline-packed weights (q4_0_pack of each matrix; the
+ * projections run through q4_0_mmvq_packed).  hidden and ffn must also be
+ * multiples of 512. */
+bq8_status q4_0_ffn_stream_packed(const void *const *w_gate, const void *const *w_up,
+                                  const void *const *w_down, int64_t layers, int64_t M,
+                                  int64_t hidden, int64_t ffn, const float *x0, float eps,
+                                  float *y, void *work, int64_t work_bytes, void *stream);
 
 #ifdef __cplusplus
 }

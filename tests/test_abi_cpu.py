@@ -35,7 +35,8 @@ def test_header_declares_expected_entry_points():
     for n in ["q8_1_quantize", "q4_0_mmvq", "q6k_pack_bytes", "q6k_pack_expand",
               "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1", "bq8_status_string",
               "bq8_abi_version", "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_ffn_stream_layout",
-              "q4_0_ffn_stream"]:
+              "q4_0_ffn_stream", "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed",
+              "q4_0_ffn_stream_packed"]:
         assert n in names
 
 
@@ -209,3 +210,26 @@ def test_stream_validation(L):
     assert call(x0=A + 2) == ALIGN
     assert call(work=A + 16) == ALIGN
     assert call(wb=total - 1) == SIZE
+
+
+def test_packed_q4_0_queries_and_validation(L):
+    import block_quantized_gemv_q8_amd as b
+
+    assert b.q4_0_pack_bytes(17408, 5120) == 50135040
+    assert b.q4_0_pack_bytes(5120, 17408) == 50135040
+    assert b.q4_0_pack_bytes(1, 512) == 16 * 18
+    assert b.q4_0_pack_bytes(4, 256) == -1           # K % 512 != 0
+    assert b.q4_0_pack_bytes(0, 512) == -1
+    n = 17408 * 160 * 18
+    assert L.q4_0_pack(None, 17408, 5120, A, n, None) == NULL
+    assert L.q4_0_pack(A, 17408, 5120, None, n, None) == NULL
+    assert L.q4_0_pack(A, 17408, 4096 + 256, A, n, None) == SHAPE
+    assert L.q4_0_pack(A + 1, 17408, 5120, A, n, None) == ALIGN
+    assert L.q4_0_pack(A, 17408, 5120, A + 8, n, None) == ALIGN
+    assert L.q4_0_pack(A, 17408, 5120, A, n - 1, None) == SIZE
+    assert L.q4_0_mmvq_packed(None, 17408, 5120, A, 6, A, None) == NULL
+    assert L.q4_0_mmvq_packed(A, 17408, 5120, A, 0, A, None) == SHAPE
+    assert L.q4_0_mmvq_packed(A, 17408, 5120, A, 18, A, None) == SHAPE
+    assert L.q4_0_mmvq_packed(A, 17408, 5376, A, 6, A, None) == SHAPE  # K % 512 != 0
+    assert L.q4_0_mmvq_packed(A + 8, 17408, 5120, A, 6, A, None) == ALIGN
+    assert L.q4_0_mmvq_packed(A, 17408, 5120, A + 2, 6, A, None) == ALIGN

@@ -1,0 +1,108 @@
+"""The library's calls captured in a HIP graph (torch.cuda.CUDAGraph) give,
+on every replay, exactly what the same calls give eagerly.
+
+Each replay is separated from the next by eager library work on other
+buffers and a synchronization, and every replay's outputs are compared bit
+for bit with the eager results (the kernels are deterministic).  No call
+enqueues a memset, so captured graphs hold kernel nodes only.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import block_quantized_gemv_q8_amd as bq  # noqa: E402
+from block_quantized_gemv_q8_amd import synth  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _capture(fn):
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_graph_of_quantize_and_products():
+    N, K, M = 2000, 1024, 6
+    ws, xs = [], []
+    for i in range(3):
+        w, x = synth.random_q4_0_case(500 + i, N, K, M)
+        ws.append(torch.from_numpy(w).to(DEV))
+        xs.append(torch.from_numpy(x).to(DEV))
+    wps = [bq.q4_0_pack(w) for w in ws]
+    xq = torch.empty((M, K // 32 * 36), dtype=torch.uint8, device=DEV)
+    ys = [torch.empty((M, N), dtype=torch.float32, device=DEV) for _ in range(6)]
+
+    def steps():
+        for i in range(3):
+            bq.q8_1_quantize(xs[i], xq)
+            bq.q4_0_mmvq_packed(wps[i], N, K, xq, M, ys[2 * i])
+            bq.q4_0_mmvq_m6(ws[i], xq, ys[2 * i + 1])
+
+    steps()
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+    g = _capture(steps)
+    other = torch.randn((M, K), device=DEV)
+    for rep in range(3):
+        say(f"graph replay {rep}")
+        for y in ys:
+            y.fill_(float("nan"))
+        bq.q8_1_quantize(other)            # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ys, ref):
+            assert torch.equal(a, b)
+
+
+def test_graph_of_packed_stream_and_top1():
+    M, H, F, L = 6, 512, 1024, 3
+    wg = [bq.q4_0_pack(synth.q4_0_weights_device(960 + 3 * l, F, H)) for l in range(L)]
+    wu = [bq.q4_0_pack(synth.q4_0_weights_device(961 + 3 * l, F, H)) for l in range(L)]
+    wd = [bq.q4_0_pack(synth.q4_0_weights_device(962 + 3 * l, H, F)) for l in range(L)]
+    x0 = torch.from_numpy(synth.stream_x0(M, H, seed=79)).to(DEV)
+    y = torch.empty((M, H), dtype=torch.float32, device=DEV)
+    work = torch.empty((bq.q4_0_ffn_stream_layout(M, H, F)["total"],), dtype=torch.uint8,
+                       device=DEV)
+    Nv, Kv = 3000, 1024
+    raw = synth.q6k_raw_weights_device(97, Nv, Kv)
+    pack = bq.q6k_pack_expand(raw, Nv, Kv)
+    xv = torch.from_numpy(synth.normal_rows(np.random.default_rng(98), 6, Kv)).to(DEV)
+    ids = torch.empty((5,), dtype=torch.int32, device=DEV)
+    scratch = torch.empty((bq.q6k_lmhead_top1_scratch_bytes(Nv, Kv, 5),), dtype=torch.uint8,
+                          device=DEV)
+
+    def work_fn():
+        bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, y=y, work=work, packed=True, ffn=F)
+        bq.q6k_lmhead_top1(pack, Nv, Kv, xv, 1, 5, ids, scratch)
+
+    work_fn()
+    torch.cuda.synchronize()
+    y_ref, ids_ref = y.clone(), ids.clone()
+    g = _capture(work_fn)
+    for rep in range(3):
+        say(f"graph replay {rep}")
+        y.fill_(float("nan"))
+        ids.fill_(-7)
+        scratch.fill_(0xEE)                # the scratch's contents on entry must not matter
+        bq.q8_1_quantize(torch.randn((4, 256), device=DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref)
+        assert torch.equal(ids, ids_ref)

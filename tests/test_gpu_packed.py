@@ -1,0 +1,113 @@
+"""GPU parity of the offline-packed Q4_0 path (q4_0_pack, q4_0_mmvq_packed).
+
+Bars: the packed bytes equal the oracle's packing bit for bit; products are
+within |gpu - oracle| <= 1e-5 * sum_b |t_b| + 1e-6 of the oracle's product
+read from the packed layout, for every M = 1..17, at shapes spanning several
+16-row tiles with a ragged last tile, and at the full ffn_up and down_sweep
+workloads.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import block_quantized_gemv_q8_amd as bq  # noqa: E402
+from block_quantized_gemv_q8_amd import synth  # noqa: E402
+
+DEV = "cuda:0"
+REL, ABS = 1e-5, 1e-6
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_close(gpu, ref, bound, what):
+    err = np.abs(gpu.astype(np.float64) - ref)
+    tol = REL * bound + ABS
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at "
+                           f"{tuple(np.argwhere(bad)[0])}")
+
+
+SHAPES = [(16, 512), (37, 1024), (200, 512), (1000, 1536), (16390, 512), (33, 5120)]
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_pack_bitexact(N, K):
+    say(f"q4_0_pack N={N} K={K}")
+    w, _ = synth.random_q4_0_case(2000 + N + K, N, K, 1)
+    wp = host(bq.q4_0_pack(dev(w)))
+    assert (wp == oracle.q4_0_pack(w, N, K)).all()
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_mmvq_packed_every_m(N, K):
+    w, x = synth.random_q4_0_case(3000 + N + K, N, K, 17)
+    xq = oracle.q8_1_quantize(x)
+    wpo = oracle.q4_0_pack(w, N, K)
+    ref, bound = oracle.q4_0p_gemv(wpo, N, K, xq, 17)
+    wp = bq.q4_0_pack(dev(w))
+    xqd = dev(xq)
+    for m in range(1, 18):
+        say(f"q4_0_mmvq_packed M={m} N={N} K={K}")
+        y = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
+        assert_close(y, ref[:m], bound[:m], f"packed m{m} N{N} K{K}")
+
+
+def test_mmvq_packed_ffn_up_full():
+    w, x = synth.ffn_up()
+    N, K, M = 17408, 5120, 6
+    say("ffn_up full: packed M=6")
+    xqd = bq.q8_1_quantize(dev(x))
+    xq = host(xqd)
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, M)
+    wp = bq.q4_0_pack(dev(w))
+    y = host(bq.q4_0_mmvq_packed(wp, N, K, xqd, M))
+    assert_close(y, ref, bound, "ffn_up packed")
+    # deterministic, and bitwise equal for equal weight rows in different tiles
+    y2 = host(bq.q4_0_mmvq_packed(wp, N, K, xqd, M))
+    assert (y2 == y).all()
+
+
+def test_mmvq_packed_down_sweep_full():
+    w, x = synth.down_sweep()
+    N, K = 5120, 17408
+    xqd = bq.q8_1_quantize(dev(x))
+    xq = host(xqd)
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
+    wp = bq.q4_0_pack(dev(w))
+    for m in synth.DOWN_SWEEP["Ms"]:
+        say(f"down_sweep packed M={m}")
+        y = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
+        assert_close(y, ref[:m], bound[:m], f"down packed m{m}")
+
+
+def test_mmvq_packed_equal_rows_and_guard_bytes():
+    N, K, M = 150, 1024, 6
+    w, x = synth.random_q4_0_case(79, N, K, M)
+    w[100] = w[5]                     # same weights in another tile
+    w[149] = w[5]                     # and in the ragged last tile
+    buf = torch.full((M * N + 64,), 12345.0, dtype=torch.float32, device=DEV)
+    y = buf[:M * N].view(M, N)
+    xqd = bq.q8_1_quantize(dev(x))
+    bq.q4_0_mmvq_packed(bq.q4_0_pack(dev(w)), N, K, xqd, M, y)
+    b = host(buf)
+    assert (b[M * N:] == 12345.0).all()
+    yy = b[:M * N].reshape(M, N)
+    assert (yy[:, 100] == yy[:, 5]).all() and (yy[:, 149] == yy[:, 5]).all()

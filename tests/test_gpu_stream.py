@@ -129,3 +129,57 @@ def test_stream_full_shape_last_layer_stages():
 
     # down projection from the stream's own requantized h
     _gemv_check(wd[-1], st["hq"], M, yh, "down")
+
+
+def composed_packed(wg, wu, wd, x0, eps, hidden, ffn):
+    """The packed stream's steps, one C-ABI call each."""
+    xq = bq.q8_1_quantize(x0)
+    M = x0.shape[0]
+    y = None
+    for l in range(len(wg)):
+        if l > 0:
+            xq = bq.rms_norm_q8_1(y, eps)
+        g = bq.q4_0_mmvq_packed(wg[l], ffn, hidden, xq, M)
+        u = bq.q4_0_mmvq_packed(wu[l], ffn, hidden, xq, M)
+        hq = bq.silu_mul_q8_1(g, u)
+        y = bq.q4_0_mmvq_packed(wd[l], hidden, ffn, hq, M)
+    return y, dict(xq=xq, g=g, u=u, hq=hq)
+
+
+@pytest.mark.parametrize("M,hidden,ffn,layers", [(6, 512, 1024, 3), (17, 1024, 1536, 2),
+                                                 (1, 512, 512, 2)])
+def test_packed_stream_equals_composed_calls(M, hidden, ffn, layers):
+    say(f"packed stream vs composed M={M} hidden={hidden} ffn={ffn} layers={layers}")
+    wg = [bq.q4_0_pack(synth.q4_0_weights_device(950 + 3 * l, ffn, hidden)) for l in range(layers)]
+    wu = [bq.q4_0_pack(synth.q4_0_weights_device(951 + 3 * l, ffn, hidden)) for l in range(layers)]
+    wd = [bq.q4_0_pack(synth.q4_0_weights_device(952 + 3 * l, hidden, ffn)) for l in range(layers)]
+    x0 = torch.from_numpy(synth.stream_x0(M, hidden, seed=78)).to(DEV)
+    y, work = bq.q4_0_ffn_stream(wg, wu, wd, x0, EPS, packed=True, ffn=ffn)
+    st = bq.stream_stages(work, M, hidden, ffn)
+    y_ref, st_ref = composed_packed(wg, wu, wd, x0, EPS, hidden, ffn)
+    assert torch.equal(y, y_ref)
+    for k in ("xq", "g", "u", "hq"):
+        assert torch.equal(st[k], st_ref[k]), k
+
+
+def test_packed_stream_full_shape_last_layer_stages():
+    cfg = synth.STREAM
+    L, M, H, F = 8, cfg["M"], cfg["hidden"], cfg["ffn"]   # the full layer shape, 8 layers
+    say(f"packed stream: {L} full-shape layers")
+    wg, wu, wd = synth.stream_weights_device(L, H, F)
+    pg = [bq.q4_0_pack(w) for w in wg]
+    pu = [bq.q4_0_pack(w) for w in wu]
+    pd = [bq.q4_0_pack(w) for w in wd]
+    x0 = torch.from_numpy(synth.stream_x0()).to(DEV)
+    y_prev, _ = bq.q4_0_ffn_stream(pg[:-1], pu[:-1], pd[:-1], x0, EPS, packed=True, ffn=F)
+    y_prev = y_prev.clone()
+    y, work = bq.q4_0_ffn_stream(pg, pu, pd, x0, EPS, packed=True, ffn=F)
+    st = {k: host(v) for k, v in bq.stream_stages(work, M, H, F).items()}
+    xq = host(bq.rms_norm_q8_1(y_prev, EPS))
+    assert (xq == st["xq"]).all()
+    # projections of the last layer against the oracle (standard layout of the same weights)
+    _gemv_check(wg[-1], st["xq"], M, st["g"], "gate")
+    _gemv_check(wu[-1], st["xq"], M, st["u"], "up")
+    hq = host(bq.silu_mul_q8_1(torch.from_numpy(st["g"]).to(DEV), torch.from_numpy(st["u"]).to(DEV)))
+    assert (hq == st["hq"]).all()
+    _gemv_check(wd[-1], st["hq"], M, host(y), "down")
