@@ -314,25 +314,22 @@ def main():
     s = setup_ffn_up(torch, bq, synth)
     N, K, M = s["N"], s["K"], s["M"]
     wbytes = q4_0_bytes(N, K)
-    # The timed steps run as one captured HIP graph of `steps` consecutive
-    # steps (each step: its own quantize and product launches), so Python's
-    # per-call launch cost does not set the pace; warm-up steps run eagerly.
     for i in range(args.warmup):
         step_packed(bq, s, i)
+    with Timer(torch) as t:
+        for i in range(args.steps):
+            step_packed(bq, s, i)
+    step_us = t.ms * 1000.0 / args.steps
+    value = wbytes / step_us / 1e3  # GB/s
+    log(f"bench: step (quantize + packed M=6) {step_us:.3f} us, {value:.1f} GB/s")
+    # the same steps captured as one HIP graph and replayed, for comparison
     g = capture(torch, lambda i: step_packed(bq, s, i), args.steps)
     g.replay()
     with Timer(torch) as t:
         g.replay()
-    step_us = t.ms * 1000.0 / args.steps
-    value = wbytes / step_us / 1e3  # GB/s
-    log(f"bench: step (quantize + packed M=6, graph) {step_us:.3f} us, {value:.1f} GB/s")
-    with Timer(torch) as t:
-        for i in range(args.steps):
-            step_packed(bq, s, i)
-    eager_step_us = t.ms * 1000.0 / args.steps
-    log(f"bench: step eager {eager_step_us:.3f} us")
+    graph_step_us = t.ms * 1000.0 / args.steps
+    log(f"bench: step as a replayed graph {graph_step_us:.3f} us")
     del g
-
     bq.q8_1_quantize(s["x"], s["xq"])
     reps = max(args.steps, 100)
     packed_us = time_calls(torch, lambda i: bq.q4_0_mmvq_packed(
@@ -390,8 +387,7 @@ def main():
             "N": N, "K": K, "M": M,
             "weight_bytes": wbytes,
             "step_us": round(step_us, 3),
-            "step_timing": "HIP graph of all timed steps, replayed once",
-            "step_eager_us": round(eager_step_us, 3),
+            "step_graph_replay_us": round(graph_step_us, 3),
             "packed_mmvq_us": round(packed_us, 3),
             "quantize_us": round(quant_us, 3),
             "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),

@@ -137,39 +137,45 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__
         a_on[s] = ((c16 >> 3) == hb) && (m < M);
         aoff[s] = (uint32_t)(a_on[s] ? m : 0) * SH::XRUN;
     }
+    // Addresses are a uniform per-chunk base (scalar registers) plus a fixed
+    // 32-bit per-lane offset, so the loads take the saddr + voffset form.
     // activation pieces: piece p = 64j + lane of a chunk is 16 bytes of row m
-    const uint8_t *xbase[LOADS];
+    uint32_t xoff[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         const int p = j * WAVE + lane;
         if (p < SH::XPIECES) {
             const int m = p / (SH::XRUN / 16);
             const int q = p - m * (SH::XRUN / 16);
-            xbase[j] = xq + (size_t)m * nb * Q8_1_BYTES + 16 * q;
+            xoff[j] = (uint32_t)m * (uint32_t)nb * Q8_1_BYTES + 16u * (uint32_t)q;
         } else {
-            xbase[j] = xq; // padding slot: a valid address, never read back
+            xoff[j] = 0u; // padding slot: a valid address, never read back
         }
     }
-    // this lane's weight piece of 4-block group u: wt + u * group_bytes
-    const uint8_t *wt = QS + (size_t)n0 * nb * 16 + (size_t)(g * rows_t + r) * 16;
+    // weights: this lane's piece of 4-block group u at tile + u * group_bytes + woff
+    const uint8_t *tile = QS + (size_t)n0 * nb * 16;
+    const uint32_t woff = (uint32_t)(g * rows_t + r) * 16u;
     const size_t group_bytes = (size_t)4 * rows_t * 16;
-    // scales of this lane's blocks (parity hb) of 16-block group q: dt + q * (2 rows_t 8)
-    const uint16_t *dt = D + (size_t)n0 * nb + (size_t)hb * rows_t * 8 + (size_t)r * 8;
+    // scales: this lane's blocks (parity hb) of 16-block group q at
+    // dtile + q * dgroup + doff, doff in elements
+    const uint16_t *dtile = D + (size_t)n0 * nb;
+    const uint32_t doff = (uint32_t)(hb * rows_t + r) * 8u;
     const size_t dgroup = (size_t)2 * rows_t * 8;
 
     auto issue = [&](int c, int st, u32x4(&wv)[2], uint32_t(&dv)[2]) {
         uint8_t *dst = ring + st * SH::STAGE;
+        const uint8_t *xc = xq + (size_t)c * SH::XRUN;
 #pragma unroll
         for (int j = 0; j < LOADS; ++j)
-            __builtin_amdgcn_global_load_lds((global_void_t *)(xbase[j] + (size_t)c * SH::XRUN),
+            __builtin_amdgcn_global_load_lds((global_void_t *)(xc + xoff[j]),
                                              (lds_void_t *)(dst + j * WAVE * 16), 16, 0, 0);
-        wv[0] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4 *>(wt + (size_t)(2 * c) * group_bytes));
+        const uint8_t *wc0 = tile + (size_t)(2 * c) * group_bytes;
+        wv[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wc0 + woff));
         wv[1] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4 *>(wt + (size_t)(2 * c + 1) * group_bytes));
+            reinterpret_cast<const u32x4 *>(wc0 + group_bytes + woff));
         // blocks 8c + 2i + hb, i = 0..3: elements 4*(c%2) .. +3 of group c/2
-        const uint32_t *dq = reinterpret_cast<const uint32_t *>(dt + (size_t)(c >> 1) * dgroup +
-                                                                (c & 1) * 4);
+        const uint16_t *dc = dtile + (size_t)(c >> 1) * dgroup + (c & 1) * 4;
+        const uint32_t *dq = reinterpret_cast<const uint32_t *>(dc + doff);
         dv[0] = dq[0];
         dv[1] = dq[1];
     };
@@ -192,25 +198,28 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__
                 stage + (m < M ? m : 0) * SH::XRUN + b * Q8_1_BYTES);
             dxs[i] = (m < M) ? h2f(bits) : 0.0f;
         }
+        // per-lane parts of the LDS addresses, folded once per chunk: block
+        // offset 36*hb, element half 16*h past the 4 header bytes
         const uint8_t *abase[MS];
 #pragma unroll
         for (int s = 0; s < MS; ++s)
-            abase[s] = a_on[s] ? stage + aoff[s] : zero;
+            abase[s] = (a_on[s] ? stage + aoff[s] : zero) + Q8_1_BYTES * hb + 4 + 16 * h;
+        const float *dxl = dxs + hb * 8 * MS + 4 * h;
         wave_lds_sync();
 #pragma unroll
         for (int t = 0; t < PK_CB / 2; ++t) {
-            const int bl = 2 * t + hb; // this lane's block within the chunk
+            // this lane's block within the chunk is 2t + hb
             i32x4 A[MS];
             f32x4 dx[MS];
 #pragma unroll
             for (int s = 0; s < MS; ++s) {
                 const uint32_t *xb =
-                    reinterpret_cast<const uint32_t *>(abase[s] + bl * Q8_1_BYTES);
-                A[s][0] = (int)xb[1 + 4 * h];
-                A[s][1] = (int)xb[2 + 4 * h];
-                A[s][2] = (int)xb[3 + 4 * h];
-                A[s][3] = (int)xb[4 + 4 * h];
-                dx[s] = *reinterpret_cast<const f32x4 *>(dxs + bl * 8 * MS + 8 * s + 4 * h);
+                    reinterpret_cast<const uint32_t *>(abase[s] + 2 * t * Q8_1_BYTES);
+                A[s][0] = (int)xb[0];
+                A[s][1] = (int)xb[1];
+                A[s][2] = (int)xb[2];
+                A[s][3] = (int)xb[3];
+                dx[s] = *reinterpret_cast<const f32x4 *>(dxl + 2 * t * 8 * MS + 8 * s);
             }
             // 8 packed bytes: byte i < 4 holds elements i (low) and 8+i (high),
             // byte 4+i elements 4+i and 12+i, of the lane's 16-element range
@@ -302,13 +311,15 @@ static int64_t packed_lds_limit()
     return cached;
 }
 
-// Waves per workgroup: enough for about 2048 waves in flight (two per tile
-// on the ffn_up shape, seven on the down shape), at most eight, never more
-// than the tile has chunks or the LDS holds.
-static int packed_waves(int64_t N, int nb, int64_t wave_lds, int64_t limit)
+// Waves per workgroup: about 1600 waves in flight for M >= 3 and 2560 for
+// the lighter M <= 2 (measured on the ffn_up and down shapes: two and five
+// waves per 16-row tile at M = 6, three and eight at M = 1), at least two, at
+// most eight, never more than the tile has chunks or the LDS holds.
+static int packed_waves(int64_t N, int nb, int M, int64_t wave_lds, int64_t limit)
 {
     const int64_t tiles = (N + PK_TILE - 1) / PK_TILE;
-    int64_t s = (2048 + tiles - 1) / tiles;
+    const int64_t target = M <= 2 ? 2560 : 1600;
+    int64_t s = (target + tiles - 1) / tiles;
     if (s < 2)
         s = 2;
     if (s > 8)
@@ -327,7 +338,7 @@ static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const v
     using SH = PkShape<M>;
     const int nb = (int)(K / QK);
     const int64_t limit = packed_lds_limit();
-    const int s = packed_waves(N, nb, SH::WAVE_LDS, limit);
+    const int s = packed_waves(N, nb, M, SH::WAVE_LDS, limit);
     const int64_t ring = (int64_t)s * SH::WAVE_LDS;
     const int64_t partial = (int64_t)s * SH::MS * 4 * 32 * (int64_t)sizeof(float);
     const int64_t lds = ring > partial ? ring : partial;
