@@ -280,31 +280,41 @@ q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ SC,
     }
 }
 
-// One workgroup: the maximum key of each row over every slot -> ids.
+// One workgroup: the maximum key of each row over every slot -> ids.  Each
+// thread takes every 256th slot and all R rows of it at once, so the loads
+// are independent and the kernel waits on memory once.
+template <int R>
 __global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_final_kernel(
-    const uint64_t *__restrict__ slots, int nslots, int R, int32_t *__restrict__ ids)
+    const uint64_t *__restrict__ slots, int nslots, int32_t *__restrict__ ids)
 {
-    __shared__ uint64_t wave_best[TOP1_WAVES][TOP1_MAX_ROWS];
+    __shared__ uint64_t wave_best[TOP1_WAVES][R];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    for (int i = 0; i < R; ++i) {
-        uint64_t k = 0;
-        for (int g = threadIdx.x; g < nslots; g += TOP1_THREADS) {
-            const uint64_t s = slots[(size_t)g * R + i];
-            k = s > k ? s : k;
+    uint64_t k[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        k[i] = 0;
+    for (int g = threadIdx.x; g < nslots; g += TOP1_THREADS) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const uint64_t v = slots[(size_t)g * R + i];
+            k[i] = v > k[i] ? v : k[i];
         }
-        k = wave_max_u64(k);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const uint64_t m = wave_max_u64(k[i]);
         if (lane == 0)
-            wave_best[wave][i] = k;
+            wave_best[wave][i] = m;
     }
     __syncthreads();
     if (threadIdx.x < R) {
-        uint64_t k = 0;
+        uint64_t m = 0;
 #pragma unroll
         for (int w = 0; w < TOP1_WAVES; ++w)
-            k = wave_best[w][threadIdx.x] > k ? wave_best[w][threadIdx.x] : k;
+            m = wave_best[w][threadIdx.x] > m ? wave_best[w][threadIdx.x] : m;
         // no finite logit at all -> -1
-        ids[threadIdx.x] = (k == 0) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+        ids[threadIdx.x] = (m == 0) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)m);
     }
 }
 
@@ -330,11 +340,13 @@ static int64_t dx_area(int64_t K, int64_t rows) { return round256(rows * (K / QK
 
 template <int R>
 static void launch_top1(const int8_t *Q, const int8_t *SC, const uint16_t *D, int N, int K,
-                        const int8_t *xq8, const float *dx, uint64_t *slots, int grid,
-                        hipStream_t s)
+                        const int8_t *xq8, const float *dx, uint64_t *slots, int32_t *ids,
+                        int grid, hipStream_t s)
 {
     hipLaunchKernelGGL(q6k_top1_kernel<R>, dim3(grid), dim3(TOP1_THREADS), 0, s, Q, SC, D, N, K,
                        xq8, dx, slots);
+    hipLaunchKernelGGL(q6k_top1_final_kernel<R>, dim3(1), dim3(TOP1_THREADS), 0, s, slots, grid,
+                       ids);
 }
 
 } // namespace bq8
@@ -410,19 +422,15 @@ BQ8_EXPORT bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, co
         return BQ8_ERR_HIP;
     const int n = (int)N, k = (int)K;
     switch (rows) {
-    case 1: launch_top1<1>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
-    case 2: launch_top1<2>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
-    case 3: launch_top1<3>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
-    case 4: launch_top1<4>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
-    case 5: launch_top1<5>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
-    case 6: launch_top1<6>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
-    case 7: launch_top1<7>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
-    case 8: launch_top1<8>(Q, SC, D, n, k, xq8, dx, slots, grid, s); break;
+    case 1: launch_top1<1>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
+    case 2: launch_top1<2>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
+    case 3: launch_top1<3>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
+    case 4: launch_top1<4>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
+    case 5: launch_top1<5>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
+    case 6: launch_top1<6>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
+    case 7: launch_top1<7>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
+    case 8: launch_top1<8>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
     }
-    if (hipGetLastError() != hipSuccess)
-        return BQ8_ERR_HIP;
-    hipLaunchKernelGGL(q6k_top1_final_kernel, dim3(1), dim3(TOP1_THREADS), 0, s, slots, grid,
-                       (int)rows, ids);
     return launch_status();
 }
 
