@@ -16,14 +16,17 @@ in device memory before timing starts.
 Printed: one JSON line with the effective weight bandwidth of a step
 (value, GB/s), the product kernel's roofline against the 8 TB/s HBM peak,
 the same projection on the weight's plain GGUF block layout
-(q4_0_mmvq_m6), the fused Q6_K LM-head top-1 time on the lm_head workload,
+(q4_0_mmvq_m6), the joint gate/up + SiLU*up + Q8_1 launch against the same
+three steps as separate launches (ffn_up shape, M = 6), the fused Q6_K
+LM-head top-1 time on the lm_head workload,
 the per-M times of the down_sweep workload on both layouts, ms per full
 width-6 pass of the 64-layer verifier FFN stream (both layouts), and the
 oracle's CPU throughput on a bounded sample.
 
 Profiling helpers (one kernel family per process, for rocprofv3):
     python bench.py --profile-target \\
-        packed_m6|mmvq_m6|lmhead_top1|down_sweep|stream|stream_packed|copy [--reps R]
+        packed_m6|mmvq_m6|gate_up|lmhead_top1|down_sweep|stream|stream_packed|copy
+        [--reps R]
 """
 from __future__ import annotations
 
@@ -117,7 +120,9 @@ def setup_ffn_up(torch, bq, synth):
     xd = torch.from_numpy(x).to("cuda")
     xq = torch.empty((M, K // 32 * 36), dtype=torch.uint8, device="cuda")
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    return dict(N=N, K=K, M=M, ws=ws, wps=wps, x=xd, xq=xq, y=y)
+    u = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    hq = torch.empty((M, N // 32 * 36), dtype=torch.uint8, device="cuda")
+    return dict(N=N, K=K, M=M, ws=ws, wps=wps, x=xd, xq=xq, y=y, u=u, hq=hq)
 
 
 def step_packed(bq, s, i):
@@ -128,6 +133,25 @@ def step_packed(bq, s, i):
 def step_standard(bq, s, i):
     bq.q8_1_quantize(s["x"], s["xq"])
     bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
+
+
+def gate_up_joint(bq, s, i):
+    """Joint gate/up + SiLU*up + Q8_1 on the ffn_up shape: gate is packed copy
+    i, up copy i + 6 (two different 50 MB weights per launch)."""
+    bq.q4_0_gate_up_silu_q8_1_packed(s["wps"][i % ROTATE], s["wps"][(i + 6) % ROTATE], s["N"],
+                                     s["K"], s["xq"], s["M"], s["hq"])
+
+
+def gate_up_separate(bq, s, i):
+    bq.q4_0_mmvq_packed(s["wps"][i % ROTATE], s["N"], s["K"], s["xq"], s["M"], s["y"])
+    bq.q4_0_mmvq_packed(s["wps"][(i + 6) % ROTATE], s["N"], s["K"], s["xq"], s["M"], s["u"])
+    bq.silu_mul_q8_1(s["y"], s["u"], s["hq"])
+
+
+def gate_up_separate_gguf(bq, s, i):
+    bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"])
+    bq.q4_0_mmvq_m6(s["ws"][(i + 6) % ROTATE], s["xq"], s["u"])
+    bq.silu_mul_q8_1(s["y"], s["u"], s["hq"])
 
 
 def setup_lm_head(torch, bq, synth):
@@ -208,7 +232,7 @@ def time_stream(torch, bq, synth, passes, packed):
             "layout": "packed" if packed else "gguf",
             "ms_median": round(med, 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
             "ms_p90": round(float(np.percentile(ms, 90)), 4), "weight_bytes": wbytes,
-            "GBps": round(wbytes / med / 1e6, 1), "launches_per_pass": 5 * L,
+            "GBps": round(wbytes / med / 1e6, 1), "launches_per_pass": (3 if packed else 5) * L,
             "graph_ms_median": round(gmed, 4),
             "graph_ms_p10": round(float(np.percentile(gms, 10)), 4),
             "graph_ms_p90": round(float(np.percentile(gms, 90)), 4),
@@ -264,9 +288,11 @@ def profile_target(torch, bq, synth, target, reps):
         torch.cuda.synchronize()
         log(f"copy: {reps} x {n} bytes")
         return
-    if target in ("packed_m6", "mmvq_m6"):
+    if target in ("packed_m6", "mmvq_m6", "gate_up"):
         s = setup_ffn_up(torch, bq, synth)
-        step = step_packed if target == "packed_m6" else step_standard
+        step = {"packed_m6": step_packed, "mmvq_m6": step_standard,
+                "gate_up": gate_up_joint}[target]
+        bq.q8_1_quantize(s["x"], s["xq"])
         for i in range(reps):
             step(bq, s, i)
     elif target == "lmhead_top1":
@@ -341,6 +367,11 @@ def main():
     std_step_us = time_calls(torch, lambda i: step_standard(bq, s, i), reps, warm=20)
     log(f"bench: q4_0_mmvq_m6 (GGUF layout) {std_us:.3f} us; step {std_step_us:.3f} us")
     quant_us = time_calls(torch, lambda i: bq.q8_1_quantize(s["x"], s["xq"]), reps, warm=20)
+    joint_us = time_calls(torch, lambda i: gate_up_joint(bq, s, i), reps, warm=20)
+    sep_us = time_calls(torch, lambda i: gate_up_separate(bq, s, i), reps, warm=20)
+    sep_gguf_us = time_calls(torch, lambda i: gate_up_separate_gguf(bq, s, i), reps, warm=20)
+    log(f"bench: gate/up + SiLU*up + Q8_1: joint {joint_us:.3f} us, separate {sep_us:.3f} us, "
+        f"separate GGUF layout {sep_gguf_us:.3f} us")
     del s
 
     log("bench: lm_head setup")
@@ -395,6 +426,13 @@ def main():
             "gguf_layout": {"q4_0_mmvq_m6_us": round(std_us, 3),
                             "GBps": round(wbytes / std_us / 1e3, 1),
                             "step_us": round(std_step_us, 3)},
+            "gate_up_silu_q8_1": {
+                "joint_us": round(joint_us, 3),
+                "joint_GBps": round(2 * wbytes / joint_us / 1e3, 1),
+                "separate_packed_us": round(sep_us, 3),
+                "separate_gguf_us": round(sep_gguf_us, 3),
+                "what": "gate [17408x5120] + up [17408x5120] Q4_0, M=6, SiLU(g)*u requantized "
+                        "to Q8_1: one joint launch vs two packed products + silu_mul_q8_1"},
             "lmhead_top1_us": round(lm_us, 2),
             "lmhead_pack_bytes": pack_bytes,
             "lmhead_GBps": round(pack_bytes / lm_us / 1e3, 1),

@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.q4_0_pack.argtypes = [_P, _I64, _I64, _P, _I64, _P]
         L.q4_0_mmvq_packed.restype = _ST
         L.q4_0_mmvq_packed.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
+        L.q4_0_gate_up_silu_q8_1_packed.restype = _ST
+        L.q4_0_gate_up_silu_q8_1_packed.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P,
+                                                    _P, _P]
         L.q4_0_ffn_stream_layout.restype = _ST
         L.q4_0_ffn_stream_layout.argtypes = [_I64, _I64, _I64, ctypes.POINTER(_I64)]
         for f in (L.q4_0_ffn_stream, L.q4_0_ffn_stream_packed):
@@ -278,6 +281,22 @@ def q4_0_mmvq_packed(wp: torch.Tensor, N: int, K: int, xq: torch.Tensor, M: int,
     return y
 
 
+def q4_0_gate_up_silu_q8_1_packed(wg: torch.Tensor, wu: torch.Tensor, N: int, K: int,
+                                  xq: torch.Tensor, M: int, hq: torch.Tensor | None = None,
+                                  g: torch.Tensor | None = None, u: torch.Tensor | None = None,
+                                  h: torch.Tensor | None = None) -> torch.Tensor:
+    """hq = Q8_1(SiLU(W_gate X) * (W_up X)) in one launch, from the packed gate
+    and up weights (q4_0_pack of Q4_0 [N][K] each) and the M Q8_1 rows of xq.
+    g, u, h, if given (f32 [M][N]), receive the two products and SiLU(g)*u."""
+    hq = _out(hq, (M, N // QK * Q8_1_BYTES), torch.uint8, wg.device, "hq")
+    opt = [None if t is None else _dev(_out(t, (M, N), torch.float32, wg.device, name), name)
+           for t, name in ((g, "g"), (u, "u"), (h, "h"))]
+    _check("q4_0_gate_up_silu_q8_1_packed", lib().q4_0_gate_up_silu_q8_1_packed(
+        _dev(wg, "wg", torch.uint8), _dev(wu, "wu", torch.uint8), N, K,
+        _dev(xq, "xq", torch.uint8), M, *opt, _dev(hq, "hq", torch.uint8), _stream()))
+    return hq
+
+
 # ------------------------------------------------------- verifier stream
 def q4_0_ffn_stream_layout(M: int, hidden: int, ffn: int) -> dict:
     """Byte offsets of the stage buffers in the stream workspace and its size."""
@@ -351,5 +370,5 @@ __all__ = ["Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "
            *[f"q4_0_mmvq_m{m}" for m in range(1, MAX_M + 1)], "q6k_pack_bytes",
            "q6k_pack_expand", "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1",
            "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed",
-           "q4_0_ffn_stream_layout", "q4_0_ffn_stream",
+           "q4_0_gate_up_silu_q8_1_packed", "q4_0_ffn_stream_layout", "q4_0_ffn_stream",
            "stream_weight_table", "stream_stages", "synth"]

@@ -10,10 +10,11 @@
 // blocker", "Q8_1 activation cache prototype": gate and up read the same
 // quantized activation.
 //
-// The whole pass is enqueued from native code: five launches per layer on
-// the caller's stream, no host synchronization, no allocation.  Every shape
-// and every layer's pointers are validated before the first launch, so a
-// rejected call enqueues nothing.
+// The whole pass is enqueued from native code on the caller's stream, no
+// host synchronization, no allocation: five launches per layer on standard
+// weights, three on packed ones, where gate, up and the SiLU*up requant are
+// one joint launch.  Every shape and every layer's pointers are validated
+// before the first launch, so a rejected call enqueues nothing.
 #include "bq8_dev.h"
 
 namespace bq8 {
@@ -62,7 +63,8 @@ BQ8_EXPORT bq8_status q4_0_ffn_stream_layout(int64_t M, int64_t hidden, int64_t 
 typedef bq8_status (*proj_fn)(const void *w, int64_t N, int64_t K, const void *xq, int64_t M,
                               float *y, void *stream);
 
-static bq8_status ffn_stream(proj_fn proj, int64_t align_k, const void *const *w_gate,
+static bq8_status ffn_stream(proj_fn proj, bool joint, int64_t align_k,
+                             const void *const *w_gate,
                              const void *const *w_up, const void *const *w_down, int64_t layers,
                              int64_t M, int64_t hidden, int64_t ffn, const float *x0, float eps,
                              float *y, void *work, int64_t work_bytes, void *stream)
@@ -97,11 +99,14 @@ static bq8_status ffn_stream(proj_fn proj, int64_t align_k, const void *const *w
     for (int64_t l = 0; l < layers && st == BQ8_OK; ++l) {
         if (l > 0)
             st = rms_norm_q8_1(y, M, hidden, eps, nullptr, xq, stream);
-        if (st == BQ8_OK)
+        if (st == BQ8_OK && joint)
+            st = q4_0_gate_up_silu_q8_1_packed(w_gate[l], w_up[l], ffn, hidden, xq, M, nullptr,
+                                               nullptr, nullptr, hq, stream);
+        if (st == BQ8_OK && !joint)
             st = proj(w_gate[l], ffn, hidden, xq, M, g, stream);
-        if (st == BQ8_OK)
+        if (st == BQ8_OK && !joint)
             st = proj(w_up[l], ffn, hidden, xq, M, u, stream);
-        if (st == BQ8_OK)
+        if (st == BQ8_OK && !joint)
             st = silu_mul_q8_1(g, u, M, ffn, nullptr, hq, stream);
         if (st == BQ8_OK)
             st = proj(w_down[l], hidden, ffn, hq, M, y, stream);
@@ -126,8 +131,8 @@ BQ8_EXPORT bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *con
                                       int64_t hidden, int64_t ffn, const float *x0, float eps,
                                       float *y, void *work, int64_t work_bytes, void *stream)
 {
-    return ffn_stream(proj_standard, QK, w_gate, w_up, w_down, layers, M, hidden, ffn, x0, eps, y,
-                      work, work_bytes, stream);
+    return ffn_stream(proj_standard, false, QK, w_gate, w_up, w_down, layers, M, hidden, ffn, x0,
+                      eps, y, work, work_bytes, stream);
 }
 
 BQ8_EXPORT bq8_status q4_0_ffn_stream_packed(const void *const *w_gate, const void *const *w_up,
@@ -136,6 +141,6 @@ BQ8_EXPORT bq8_status q4_0_ffn_stream_packed(const void *const *w_gate, const vo
                                              const float *x0, float eps, float *y, void *work,
                                              int64_t work_bytes, void *stream)
 {
-    return ffn_stream(proj_packed, 512, w_gate, w_up, w_down, layers, M, hidden, ffn, x0, eps, y,
-                      work, work_bytes, stream);
+    return ffn_stream(proj_packed, true, 512, w_gate, w_up, w_down, layers, M, hidden, ffn, x0,
+                      eps, y, work, work_bytes, stream);
 }

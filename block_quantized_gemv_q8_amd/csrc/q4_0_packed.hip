@@ -104,22 +104,27 @@ struct PkShape {
     static constexpr int WAVE_LDS = ZOFF + XRUN;
 };
 
-template <int M>
-__global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__restrict__ QS,
-                                                                const uint16_t *__restrict__ D,
-                                                                int N, int nb,
-                                                                const uint8_t *__restrict__ xq,
-                                                                float *__restrict__ y)
+// The main loop shared by the products: this wave's partial sums over its
+// chunks for NT 16-row tiles that read the same activation rows.  Tile i's
+// packed nibbles start at tile[i], its scales at dtile[i]; every tile has
+// rows_t rows; chunk c of tile i starts at tile[i] + c * chunk_stride bytes
+// and its scales at dtile[i] + (c/2) * dgroup_stride elements (+4 for odd
+// c).  The activations are staged once per chunk and each A operand feeds NT
+// MFMAs.  ring is this wave's LDS (PkShape<M>::WAVE_LDS bytes).
+// acc[i][s][x] (lanes l < 32 after pk_pair_sum) is the sum for weight row
+// l%16 of tile i and activation row 8s + 4*(l/16) + x, 16x the exact value.
+template <int M, int NT>
+__device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
+                                              const uint16_t *const (&dtile)[NT], int rows_t,
+                                              size_t chunk_stride, size_t dgroup_stride, int nb,
+                                              const uint8_t *__restrict__ xq,
+                                              uint8_t *ring, float (&acc)[NT][PkShape<M>::MS][4])
 {
     using SH = PkShape<M>;
     constexpr int MS = SH::MS, LOADS = SH::LOADS;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
-    const int n0 = blockIdx.x * PK_TILE;
-    const int rows_t = (N - n0 < PK_TILE) ? N - n0 : PK_TILE;
-    uint8_t *ring = smem + (size_t)wave * SH::WAVE_LDS;
     uint8_t *zero = ring + SH::ZOFF;
     for (int i = lane; i < SH::XRUN / 4; i += WAVE)
         reinterpret_cast<uint32_t *>(zero)[i] = 0u;
@@ -153,41 +158,45 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__
         }
     }
     // weights: this lane's piece of 4-block group u at tile + u * group_bytes + woff
-    const uint8_t *tile = QS + (size_t)n0 * nb * 16;
     const uint32_t woff = (uint32_t)(g * rows_t + r) * 16u;
     const size_t group_bytes = (size_t)4 * rows_t * 16;
     // scales: this lane's blocks (parity hb) of 16-block group q at
-    // dtile + q * dgroup + doff, doff in elements
-    const uint16_t *dtile = D + (size_t)n0 * nb;
+    // dtile + q * dgroup_stride + doff, doff in elements
     const uint32_t doff = (uint32_t)(hb * rows_t + r) * 8u;
-    const size_t dgroup = (size_t)2 * rows_t * 8;
 
-    auto issue = [&](int c, int st, u32x4(&wv)[2], uint32_t(&dv)[2]) {
+    auto issue = [&](int c, int st, u32x4(&wv)[NT][2], uint32_t(&dv)[NT][2]) {
         uint8_t *dst = ring + st * SH::STAGE;
         const uint8_t *xc = xq + (size_t)c * SH::XRUN;
 #pragma unroll
         for (int j = 0; j < LOADS; ++j)
             __builtin_amdgcn_global_load_lds((global_void_t *)(xc + xoff[j]),
                                              (lds_void_t *)(dst + j * WAVE * 16), 16, 0, 0);
-        const uint8_t *wc0 = tile + (size_t)(2 * c) * group_bytes;
-        wv[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wc0 + woff));
-        wv[1] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4 *>(wc0 + group_bytes + woff));
-        // blocks 8c + 2i + hb, i = 0..3: elements 4*(c%2) .. +3 of group c/2
-        const uint16_t *dc = dtile + (size_t)(c >> 1) * dgroup + (c & 1) * 4;
-        const uint32_t *dq = reinterpret_cast<const uint32_t *>(dc + doff);
-        dv[0] = dq[0];
-        dv[1] = dq[1];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const uint8_t *wc0 = tile[i] + (size_t)c * chunk_stride;
+            wv[i][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wc0 + woff));
+            wv[i][1] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(wc0 + group_bytes + woff));
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            // blocks 8c + 2i + hb, i = 0..3: elements 4*(c%2) .. +3 of group c/2
+            const uint16_t *dc = dtile[i] + (size_t)(c >> 1) * dgroup_stride + (c & 1) * 4;
+            const uint32_t *dq = reinterpret_cast<const uint32_t *>(dc + doff);
+            dv[i][0] = dq[0];
+            dv[i][1] = dq[1];
+        }
     };
 
-    float acc[MS][4];
 #pragma unroll
-    for (int s = 0; s < MS; ++s)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-            acc[s][x] = 0.0f;
+        for (int s = 0; s < MS; ++s)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                acc[i][s][x] = 0.0f;
 
-    auto compute = [&](int st, const u32x4(&wv)[2], const uint32_t(&dv)[2]) {
+    auto compute = [&](int st, const u32x4(&wv)[NT][2], const uint32_t(&dv)[NT][2]) {
         const uint8_t *stage = ring + st * SH::STAGE;
         float *dxs = reinterpret_cast<float *>(ring + st * SH::STAGE + SH::DXOFF);
         // d_x of the chunk's blocks as f32: dxs[b*8*MS + m], 0 past M
@@ -221,22 +230,34 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__
                 A[s][3] = (int)xb[3];
                 dx[s] = *reinterpret_cast<const f32x4 *>(dxl + 2 * t * 8 * MS + 8 * s);
             }
-            // 8 packed bytes: byte i < 4 holds elements i (low) and 8+i (high),
-            // byte 4+i elements 4+i and 12+i, of the lane's 16-element range
-            const uint32_t w0 = wv[t >> 1][2 * (t & 1)], w1 = wv[t >> 1][2 * (t & 1) + 1];
-            i32x4 B;
-            B[0] = (int)(((w0 << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
-            B[1] = (int)(((w1 << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
-            B[2] = (int)((w0 & 0xF0F0F0F0u) ^ 0x80808080u);
-            B[3] = (int)((w1 & 0xF0F0F0F0u) ^ 0x80808080u);
-            const float dw = h2f(dv[t >> 1] >> (16 * (t & 1)));
+            // every tile's MFMAs first, then their scaling, so that the
+            // products' latency overlaps the next tile's unpacking
+            i32x4 Dm[NT][MS];
 #pragma unroll
-            for (int s = 0; s < MS; ++s) {
-                const i32x4 Dm =
-                    __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s], B, (i32x4){0, 0, 0, 0}, 0, 0, 0);
+            for (int i = 0; i < NT; ++i) {
+                // 8 packed bytes: byte i < 4 holds elements i (low) and 8+i
+                // (high), byte 4+i elements 4+i and 12+i, of the lane's
+                // 16-element range
+                const uint32_t w0 = wv[i][t >> 1][2 * (t & 1)];
+                const uint32_t w1 = wv[i][t >> 1][2 * (t & 1) + 1];
+                i32x4 B;
+                B[0] = (int)(((w0 << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
+                B[1] = (int)(((w1 << 4) & 0xF0F0F0F0u) ^ 0x80808080u);
+                B[2] = (int)((w0 & 0xF0F0F0F0u) ^ 0x80808080u);
+                B[3] = (int)((w1 & 0xF0F0F0F0u) ^ 0x80808080u);
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    acc[s][x] = fmaf((float)Dm[x], dw * dx[s][x], acc[s][x]);
+                for (int s = 0; s < MS; ++s)
+                    Dm[i][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s], B, (i32x4){0, 0, 0, 0},
+                                                                     0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const float dw = h2f(dv[i][t >> 1] >> (16 * (t & 1)));
+#pragma unroll
+                for (int s = 0; s < MS; ++s)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        acc[i][s][x] = fmaf((float)Dm[i][s][x], dw * dx[s][x], acc[i][s][x]);
             }
         }
         wave_lds_sync();
@@ -245,32 +266,69 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__
     const int nchunks = nb / PK_CB;
     if (wave < nchunks) {
         const int mine = (nchunks - wave + S - 1) / S;
-        u32x4 wn[2], wc[2];
-        uint32_t dn[2], dc[2];
+        u32x4 wn[NT][2], wc[NT][2];
+        uint32_t dn[NT][2], dc[NT][2];
         issue(wave, 0, wn, dn);
         for (int k = 0; k < mine; ++k) {
             // Taking chunk k out of the prefetch registers waits for exactly
             // its loads (nothing younger is in flight yet); the explicit wait
             // also covers its activation DMA, which the compiler does not track.
-            wc[0] = wn[0];
-            wc[1] = wn[1];
-            dc[0] = dn[0];
-            dc[1] = dn[1];
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                wc[i][0] = wn[i][0];
+                wc[i][1] = wn[i][1];
+                dc[i][0] = dn[i][0];
+                dc[i][1] = dn[i][1];
+            }
             __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
-            // past the wave's last chunk the prefetch repeats it (cache hits, never used)
-            const int kn = k + 1 < mine ? k + 1 : mine - 1;
-            issue(wave + S * kn, (k + 1) & 1, wn, dn);
+            // no prefetch past the wave's last chunk: a repeated chunk would
+            // be fetched from HBM again (the weight loads are nontemporal)
+            if (k + 1 < mine)
+                issue(wave + S * (k + 1), (k + 1) & 1, wn, dn);
             compute(k & 1, wc, dc);
         }
     }
+}
 
-    // the two blocks of each pair (lanes l and l+32), then the S waves in order
+// Adds the two blocks of each pair (lanes l and l + 32) into lanes l < 32,
+// then waits for every load of the wave (no DMA may still be writing the LDS
+// the caller reuses next).
+template <int NT, int MS>
+__device__ __forceinline__ void pk_pair_sum(float (&acc)[NT][MS][4])
+{
 #pragma unroll
-    for (int s = 0; s < MS; ++s)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-            acc[s][x] += __shfl_xor(acc[s][x], 32, 64);
-    __builtin_amdgcn_s_waitcnt(0); // no load may still be writing the LDS reused below
+        for (int s = 0; s < MS; ++s)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                acc[i][s][x] += __shfl_xor(acc[i][s][x], 32, 64);
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// y[m][n] for the 16-row tile of workgroup blockIdx.x; the tile's S waves
+// take its 8-block chunks round-robin and their sums are added in wave order.
+template <int M>
+__global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__restrict__ QS,
+                                                                const uint16_t *__restrict__ D,
+                                                                int N, int nb,
+                                                                const uint8_t *__restrict__ xq,
+                                                                float *__restrict__ y)
+{
+    using SH = PkShape<M>;
+    constexpr int MS = SH::MS;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+    const int n0 = blockIdx.x * PK_TILE;
+    const int rows_t = (N - n0 < PK_TILE) ? N - n0 : PK_TILE;
+    const uint8_t *tile[1] = {QS + (size_t)n0 * nb * 16};
+    const uint16_t *dtile[1] = {D + (size_t)n0 * nb};
+    float acc[1][MS][4];
+    pk_accumulate<M, 1>(tile, dtile, rows_t, (size_t)8 * rows_t * 16, (size_t)2 * rows_t * 8, nb,
+                        xq, smem + (size_t)wave * SH::WAVE_LDS, acc);
+    pk_pair_sum(acc);
     __syncthreads();
     constexpr int SLOTS = MS * 4;
     float *partial = reinterpret_cast<float *>(smem); // [S][SLOTS][32]
@@ -279,7 +337,7 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__
         for (int s = 0; s < MS; ++s)
 #pragma unroll
             for (int x = 0; x < 4; ++x)
-                partial[(wave * SLOTS + s * 4 + x) * 32 + lane] = acc[s][x];
+                partial[(wave * SLOTS + s * 4 + x) * 32 + lane] = acc[0][s][x];
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x) {
@@ -292,6 +350,85 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__
             sacc += partial[(v * SLOTS + slot) * 32 + l];
         if (m < M && nn < N)
             y[(size_t)m * N + nn] = sacc * 0.0625f;
+    }
+}
+
+// Gate and up projections of one Q8_1 activation with the SiLU(gate) * up
+// product and its Q8_1 requantization as the epilogue ("Q6_K M=6 fused
+// DFlash top-1 production record", "Strict run identity": joint gate/up over
+// the packed width-6 projections).  Workgroup p owns
+// output columns 32p .. 32p+31 of both matrices (N % 32 == 0, so its four
+// 16-row tiles -- gate 2p, 2p+1, up 2p, 2p+1 -- are full); its waves take the
+// 8-block chunks round-robin with all four tiles per chunk, so each staged
+// activation block and each A operand serves four MFMAs.  The 32 columns are
+// one Q8_1 block of h per activation row, quantized where it is computed; g,
+// u and h never reach memory unless asked for.  Per column and row, g and u
+// are the sums of the plain product (same per-wave order, waves added in
+// order), h = g / (1 + exp(-g)) * u in binary32, then the Q8_1 block of h.
+template <int M>
+__global__ __launch_bounds__(512) void q4_0_gate_up_packed_kernel(
+    const uint8_t *__restrict__ QG, const uint16_t *__restrict__ DG,
+    const uint8_t *__restrict__ QU, const uint16_t *__restrict__ DU, int N, int nb,
+    const uint8_t *__restrict__ xq, float *__restrict__ g, float *__restrict__ u,
+    float *__restrict__ h, uint8_t *__restrict__ hq)
+{
+    using SH = PkShape<M>;
+    constexpr int MS = SH::MS;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+    const int n0 = blockIdx.x * 2 * PK_TILE;
+    const size_t tb = (size_t)PK_TILE * nb * 16; // nibble bytes of one full tile
+    const size_t t0 = (size_t)n0 * nb * 16;
+    const uint8_t *tile[4] = {QG + t0, QG + t0 + tb, QU + t0, QU + t0 + tb};
+    const uint16_t *dtile[4] = {DG + (size_t)n0 * nb, DG + (size_t)(n0 + PK_TILE) * nb,
+                                DU + (size_t)n0 * nb, DU + (size_t)(n0 + PK_TILE) * nb};
+    float acc[4][MS][4];
+    pk_accumulate<M, 4>(tile, dtile, PK_TILE, (size_t)8 * PK_TILE * 16, (size_t)2 * PK_TILE * 8,
+                        nb, xq, smem + (size_t)wave * SH::WAVE_LDS, acc);
+    pk_pair_sum(acc);
+    __syncthreads();
+    constexpr int SLOTS = MS * 4;
+    float *partial = reinterpret_cast<float *>(smem); // [S][4][SLOTS][32]
+    if (lane < 32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int s = 0; s < MS; ++s)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    partial[((wave * 4 + i) * SLOTS + s * 4 + x) * 32 + lane] = acc[i][s][x];
+    }
+    __syncthreads();
+    // one 32-lane group per activation row m: lane c is column n0 + c
+    const int groups = blockDim.x >> 5;
+    const int c = threadIdx.x & 31;
+    const int half = c >> 4; // tile 2p + half of each matrix
+    for (int m0 = 0; m0 < M; m0 += groups) {
+        const int m = m0 + (int)(threadIdx.x >> 5);
+        const bool valid = m < M;
+        const int mc = valid ? m : M - 1;
+        const int slot = (mc >> 3) * 4 + (mc & 3);
+        const int l = 16 * ((mc >> 2) & 1) + (c & 15);
+        float sg = 0.0f, su = 0.0f;
+        for (int v = 0; v < S; ++v) {
+            sg += partial[((v * 4 + half) * SLOTS + slot) * 32 + l];
+            su += partial[((v * 4 + 2 + half) * SLOTS + slot) * 32 + l];
+        }
+        const float gv = sg * 0.0625f, uv = su * 0.0625f;
+        const float hv = gv / (1.0f + expf(-gv)) * uv;
+        const size_t o = (size_t)mc * N + n0 + c;
+        if (valid) {
+            if (g)
+                g[o] = gv;
+            if (u)
+                u[o] = uv;
+            if (h)
+                h[o] = hv;
+        }
+        q8_1_block_store(hv, c, valid,
+                         hq + ((size_t)mc * (N / QK) + blockIdx.x) * Q8_1_BYTES);
     }
 }
 
@@ -357,6 +494,54 @@ static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const v
     hipLaunchKernelGGL((q4_0_mmvq_packed_kernel<M>), dim3((unsigned)((N + PK_TILE - 1) / PK_TILE)),
                        dim3(WAVE * s), (size_t)lds, stream, QS, D, (int)N, nb,
                        (const uint8_t *)xq, y);
+    return launch_status();
+}
+
+// Waves per gate/up workgroup: about 2176 waves in flight for M >= 3 and
+// 1088 for M <= 2 (measured on the 17408 x 5120 shape: four and two waves
+// per 32-column workgroup), at least one, at most eight, never more than the
+// row has chunks or the LDS holds.
+static int gate_up_waves(int64_t groups, int nb, int M, int64_t wave_lds, int64_t limit)
+{
+    const int64_t target = M <= 2 ? 1088 : 2176;
+    int64_t s = (target + groups - 1) / groups;
+    if (s > 8)
+        s = 8;
+    if (s > nb / PK_CB)
+        s = nb / PK_CB;
+    while (s > 1 && s * wave_lds > limit)
+        --s;
+    return (int)(s < 1 ? 1 : s);
+}
+
+template <int M>
+static bq8_status gate_up_launch(const uint8_t *wg, const uint8_t *wu, int64_t N, int64_t K,
+                                 const void *xq, float *g, float *u, float *h, void *hq,
+                                 hipStream_t stream)
+{
+    using SH = PkShape<M>;
+    const int nb = (int)(K / QK);
+    const int64_t groups = N / (2 * PK_TILE);
+    const int64_t limit = packed_lds_limit();
+    const int s = gate_up_waves(groups, nb, M, SH::WAVE_LDS, limit);
+    const int64_t ring = (int64_t)s * SH::WAVE_LDS;
+    const int64_t partial = (int64_t)s * 4 * SH::MS * 4 * 32 * (int64_t)sizeof(float);
+    const int64_t lds = ring > partial ? ring : partial;
+    if (lds > limit)
+        return BQ8_ERR_SHAPE;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)q4_0_gate_up_packed_kernel<M>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit) != hipSuccess)
+            return BQ8_ERR_HIP;
+        attr_set = true;
+    }
+    const size_t dplane = (size_t)N * nb * 16;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((q4_0_gate_up_packed_kernel<M>), dim3((unsigned)groups), dim3(WAVE * s),
+                       (size_t)lds, stream, wg, reinterpret_cast<const uint16_t *>(wg + dplane), wu,
+                       reinterpret_cast<const uint16_t *>(wu + dplane), (int)N, nb,
+                       (const uint8_t *)xq, g, u, h, (uint8_t *)hq);
     return launch_status();
 }
 
@@ -427,5 +612,41 @@ BQ8_EXPORT bq8_status q4_0_mmvq_packed(const void *wp, int64_t N, int64_t K, con
     case 15: return packed_launch<15>(p, N, K, xq, y, s);
     case 16: return packed_launch<16>(p, N, K, xq, y, s);
     default: return packed_launch<17>(p, N, K, xq, y, s);
+    }
+}
+
+BQ8_EXPORT bq8_status q4_0_gate_up_silu_q8_1_packed(const void *wg, const void *wu, int64_t N,
+                                                    int64_t K, const void *xq, int64_t M,
+                                                    float *g, float *u, float *h, void *hq,
+                                                    void *stream)
+{
+    if (!wg || !wu || !xq || !hq)
+        return BQ8_ERR_NULL;
+    if (!packed_shape_ok(N, K) || N % (2 * PK_TILE) != 0 || M < 1 || M > 17 ||
+        M * K >= (int64_t(1) << 31) || M * N >= (int64_t(1) << 31))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(wg, 16) || !aligned(wu, 16) || !aligned(xq, 4) || !aligned(hq, 4) ||
+        (g && !aligned(g, 4)) || (u && !aligned(u, 4)) || (h && !aligned(h, 4)))
+        return BQ8_ERR_ALIGN;
+    const uint8_t *a = (const uint8_t *)wg, *b = (const uint8_t *)wu;
+    hipStream_t s = (hipStream_t)stream;
+    switch (M) {
+    case 1: return gate_up_launch<1>(a, b, N, K, xq, g, u, h, hq, s);
+    case 2: return gate_up_launch<2>(a, b, N, K, xq, g, u, h, hq, s);
+    case 3: return gate_up_launch<3>(a, b, N, K, xq, g, u, h, hq, s);
+    case 4: return gate_up_launch<4>(a, b, N, K, xq, g, u, h, hq, s);
+    case 5: return gate_up_launch<5>(a, b, N, K, xq, g, u, h, hq, s);
+    case 6: return gate_up_launch<6>(a, b, N, K, xq, g, u, h, hq, s);
+    case 7: return gate_up_launch<7>(a, b, N, K, xq, g, u, h, hq, s);
+    case 8: return gate_up_launch<8>(a, b, N, K, xq, g, u, h, hq, s);
+    case 9: return gate_up_launch<9>(a, b, N, K, xq, g, u, h, hq, s);
+    case 10: return gate_up_launch<10>(a, b, N, K, xq, g, u, h, hq, s);
+    case 11: return gate_up_launch<11>(a, b, N, K, xq, g, u, h, hq, s);
+    case 12: return gate_up_launch<12>(a, b, N, K, xq, g, u, h, hq, s);
+    case 13: return gate_up_launch<13>(a, b, N, K, xq, g, u, h, hq, s);
+    case 14: return gate_up_launch<14>(a, b, N, K, xq, g, u, h, hq, s);
+    case 15: return gate_up_launch<15>(a, b, N, K, xq, g, u, h, hq, s);
+    case 16: return gate_up_launch<16>(a, b, N, K, xq, g, u, h, hq, s);
+    default: return gate_up_launch<17>(a, b, N, K, xq, g, u, h, hq, s);
     }
 }

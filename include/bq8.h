@@ -161,6 +161,29 @@ bq8_status q4_0_mmvq_packed(const void *wp, int64_t N, int64_t K, const void *xq
                             float *y, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Joint gate/up projection with SiLU(gate)*up and its Q8_1 requantization
+ * as the epilogue (the fused-head page's run identity has joint gate/up
+ * enabled over its packed width-6 projections, "Strict run identity"; the
+ * closure page's packed gate/up projections, "What materially worked").
+ * One launch:
+ *   g = W_gate X,  u = W_up X               (as q4_0_mmvq_packed)
+ *   h = g / (1 + exp(-g)) * u               (binary32, as silu_mul_q8_1)
+ *   hq = Q8_1(h)                            (as silu_mul_q8_1)
+ * wg, wu: q4_0_pack of the gate and up weights, each Q4_0 [N][K]; 16-byte
+ *   aligned.  xq: Q8_1 [M][K/32], 4-byte aligned.  hq: Q8_1 [M][N/32],
+ *   4-byte aligned, fully overwritten.  g, u, h: optional f32 [M][N]
+ *   (NULL to skip), receive the gate and up products and h; hq does not
+ *   depend on whether they are given.  hq is bitwise the Q8_1 of the h
+ *   computed here; g and u equal q4_0_mmvq_packed's up to the binary32
+ *   summation order.
+ * Shape: M = 1..17, N % 32 == 0, 32 <= N < 2^31, K as q4_0_mmvq_packed,
+ *   M*K < 2^31, M*N < 2^31.
+ * ---------------------------------------------------------------------- */
+bq8_status q4_0_gate_up_silu_q8_1_packed(const void *wg, const void *wu, int64_t N, int64_t K,
+                                         const void *xq, int64_t M, float *g, float *u, float *h,
+                                         void *hq, void *stream);
+
+/* ------------------------------------------------------------------------
  * Q6_K expansion (run once, at load time).  The fused-head page expands the
  * output tensor once into signed int8 quants, int8 subscales and fp16
  * superblock scales ("Why this was slow") and accepts the pack only with its
@@ -258,9 +281,11 @@ bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *const *w_up,
                            int64_t ffn, const float *x0, float eps, float *y, void *work,
                            int64_t work_bytes, void *stream);
 
-/* The same pass on offline-packed weights (q4_0_pack of each matrix; the
- * projections run through q4_0_mmvq_packed).  hidden and ffn must also be
- * multiples of 512. */
+/* The same pass on offline-packed weights (q4_0_pack of each matrix), three
+ * launches per layer: the gate, up and SiLU*up steps are one
+ * q4_0_gate_up_silu_q8_1_packed launch and down runs through
+ * q4_0_mmvq_packed.  The g and u stage buffers of the workspace are not
+ * written.  hidden and ffn must also be multiples of 512. */
 bq8_status q4_0_ffn_stream_packed(const void *const *w_gate, const void *const *w_up,
                                   const void *const *w_down, int64_t layers, int64_t M,
                                   int64_t hidden, int64_t ffn, const float *x0, float eps,

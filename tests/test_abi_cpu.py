@@ -36,7 +36,7 @@ def test_header_declares_expected_entry_points():
               "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1", "bq8_status_string",
               "bq8_abi_version", "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_ffn_stream_layout",
               "q4_0_ffn_stream", "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed",
-              "q4_0_ffn_stream_packed"]:
+              "q4_0_ffn_stream_packed", "q4_0_gate_up_silu_q8_1_packed"]:
         assert n in names
 
 
@@ -233,3 +233,28 @@ def test_packed_q4_0_queries_and_validation(L):
     assert L.q4_0_mmvq_packed(A, 17408, 5376, A, 6, A, None) == SHAPE  # K % 512 != 0
     assert L.q4_0_mmvq_packed(A + 8, 17408, 5120, A, 6, A, None) == ALIGN
     assert L.q4_0_mmvq_packed(A, 17408, 5120, A + 2, 6, A, None) == ALIGN
+
+
+def test_gate_up_silu_validation(L):
+    f = L.q4_0_gate_up_silu_q8_1_packed
+
+    def call(wg=A, wu=A, N=17408, K=5120, xq=A, M=6, g=None, u=None, h=None, hq=A):
+        return f(wg, wu, N, K, xq, M, g, u, h, hq, None)
+
+    assert call(wg=None) == NULL
+    assert call(wu=None) == NULL
+    assert call(xq=None) == NULL
+    assert call(hq=None) == NULL
+    assert call(M=0) == SHAPE
+    assert call(M=18) == SHAPE
+    assert call(N=17408 + 16) == SHAPE   # N % 32 != 0
+    assert call(N=0) == SHAPE
+    assert call(K=5376) == SHAPE         # K % 512 != 0
+    assert call(M=17, K=2 ** 27) == SHAPE
+    assert call(wg=A + 8) == ALIGN
+    assert call(wu=A + 8) == ALIGN
+    assert call(xq=A + 2) == ALIGN
+    assert call(hq=A + 2) == ALIGN
+    assert call(g=A + 2) == ALIGN
+    assert call(u=A + 1) == ALIGN
+    assert call(h=A + 3) == ALIGN

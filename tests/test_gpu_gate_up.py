@@ -1,0 +1,116 @@
+"""GPU parity of the joint gate/up kernel (q4_0_gate_up_silu_q8_1_packed).
+
+Bars, per shape:
+  * g and u within |gpu - oracle| <= 1e-5 * sum_b |t_b| + 1e-6 of the
+    oracle's Q4_0 x Q8_1 products of the standard-layout weights;
+  * h within 1e-5 relative (+1e-6) of the oracle's SiLU(g) * u of the GPU's
+    own g and u;
+  * hq bit for bit the oracle's Q8_1 of the GPU's own h (the quant decision is
+    taken in binary32 on both sides);
+  * h and hq bitwise equal to the standalone silu_mul_q8_1 of the same g, u,
+    and hq independent of whether the optional outputs are requested.
+Shapes span one to many 32-column workgroups, two to 160 chunks of 8 blocks
+and every M class (1..8, 9..16, 17), up to the full ffn_up shape.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import block_quantized_gemv_q8_amd as bq  # noqa: E402
+from block_quantized_gemv_q8_amd import synth  # noqa: E402
+
+DEV = "cuda:0"
+REL, ABS = 1e-5, 1e-6
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_close(gpu, ref, bound, what):
+    err = np.abs(gpu.astype(np.float64) - ref)
+    tol = REL * bound + ABS
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at "
+                           f"{tuple(np.argwhere(bad)[0])}")
+
+
+def run_case(wg, wu, x, N, K, M):
+    """Joint kernel with every optional output, checked stage by stage."""
+    xq = oracle.q8_1_quantize(x)
+    pg, pu, xqd = bq.q4_0_pack(dev(wg)), bq.q4_0_pack(dev(wu)), dev(xq)
+    g = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    u = torch.empty_like(g)
+    h = torch.empty_like(g)
+    hq = host(bq.q4_0_gate_up_silu_q8_1_packed(pg, pu, N, K, xqd, M, g=g, u=u, h=h))
+    gg, ug, hg = host(g), host(u), host(h)
+
+    ref_g, bound_g = oracle.q4_0_gemv(wg, N, K, xq, M)
+    assert_close(gg, ref_g, bound_g, f"gate M{M} N{N} K{K}")
+    ref_u, bound_u = oracle.q4_0_gemv(wu, N, K, xq, M)
+    assert_close(ug, ref_u, bound_u, f"up M{M} N{N} K{K}")
+    ref_h = oracle.silu_mul(gg, ug)
+    err = np.abs(hg.astype(np.float64) - ref_h)
+    assert (err <= REL * np.abs(ref_h) + ABS).all(), "h outside tolerance"
+    assert (hq == oracle.q8_1_quantize(hg)).all(), "hq differs from Q8_1 of the GPU's h"
+
+    # the epilogue is the standalone SiLU*up requant, bit for bit
+    h2 = torch.empty_like(g)
+    hq2 = host(bq.silu_mul_q8_1(g, u, h=h2))
+    assert np.array_equal(host(h2).view(np.uint32), hg.view(np.uint32))
+    assert (hq2 == hq).all()
+    # no optional outputs: same hq
+    hq3 = host(bq.q4_0_gate_up_silu_q8_1_packed(pg, pu, N, K, xqd, M))
+    assert (hq3 == hq).all()
+    return gg, ug, hg, hq
+
+
+SHAPES = [(1, 64, 512), (8, 32, 512), (3, 96, 2048), (17, 1024, 1536), (16, 4096, 1024),
+          (9, 544, 4608), (6, 64, 5120), (5, 2048, 5120)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gate_up_silu_small(M, N, K):
+    say(f"gate_up_silu M={M} N={N} K={K}")
+    wg, x = synth.random_q4_0_case(6100 + M + N + K, N, K, M)
+    wu, _ = synth.random_q4_0_case(6200 + M + N + K, N, K, 1)
+    run_case(wg, wu, x, N, K, M)
+
+
+@pytest.mark.parametrize("M", [6, 1, 17])
+def test_gate_up_silu_full_ffn_shape(M):
+    N, K = synth.FFN_UP["N"], synth.FFN_UP["K"]
+    say(f"gate_up_silu full ffn shape M={M}")
+    wu, x = synth.ffn_up(M=max(M, 6))
+    wg, _ = synth.random_q4_0_case(6300, N, K, 1)
+    run_case(wg, wu, x[:M], N, K, M)
+
+
+def test_gate_up_silu_zero_activation():
+    M, N, K = 6, 256, 1024
+    say("gate_up_silu zero activation")
+    wg, _ = synth.random_q4_0_case(6400, N, K, 1)
+    wu, _ = synth.random_q4_0_case(6401, N, K, 1)
+    x = np.zeros((M, K), np.float32)
+    x[2] = 1.0  # one live row among zero rows
+    gg, ug, hg, hq = run_case(wg, wu, x, N, K, M)
+    for m in (0, 1, 3, 4, 5):
+        assert not gg[m].any() and not ug[m].any() and not hg[m].any()
+        assert not hq[m].any()   # d = s = 0, every quant 0
+

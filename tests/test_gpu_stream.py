@@ -139,11 +139,9 @@ def composed_packed(wg, wu, wd, x0, eps, hidden, ffn):
     for l in range(len(wg)):
         if l > 0:
             xq = bq.rms_norm_q8_1(y, eps)
-        g = bq.q4_0_mmvq_packed(wg[l], ffn, hidden, xq, M)
-        u = bq.q4_0_mmvq_packed(wu[l], ffn, hidden, xq, M)
-        hq = bq.silu_mul_q8_1(g, u)
+        hq = bq.q4_0_gate_up_silu_q8_1_packed(wg[l], wu[l], ffn, hidden, xq, M)
         y = bq.q4_0_mmvq_packed(wd[l], hidden, ffn, hq, M)
-    return y, dict(xq=xq, g=g, u=u, hq=hq)
+    return y, dict(xq=xq, hq=hq)
 
 
 @pytest.mark.parametrize("M,hidden,ffn,layers", [(6, 512, 1024, 3), (17, 1024, 1536, 2),
@@ -158,7 +156,7 @@ def test_packed_stream_equals_composed_calls(M, hidden, ffn, layers):
     st = bq.stream_stages(work, M, hidden, ffn)
     y_ref, st_ref = composed_packed(wg, wu, wd, x0, EPS, hidden, ffn)
     assert torch.equal(y, y_ref)
-    for k in ("xq", "g", "u", "hq"):
+    for k in ("xq", "hq"):
         assert torch.equal(st[k], st_ref[k]), k
 
 
@@ -177,9 +175,20 @@ def test_packed_stream_full_shape_last_layer_stages():
     st = {k: host(v) for k, v in bq.stream_stages(work, M, H, F).items()}
     xq = host(bq.rms_norm_q8_1(y_prev, EPS))
     assert (xq == st["xq"]).all()
-    # projections of the last layer against the oracle (standard layout of the same weights)
-    _gemv_check(wg[-1], st["xq"], M, st["g"], "gate")
-    _gemv_check(wu[-1], st["xq"], M, st["u"], "up")
-    hq = host(bq.silu_mul_q8_1(torch.from_numpy(st["g"]).to(DEV), torch.from_numpy(st["u"]).to(DEV)))
+    # the joint gate/up launch of the last layer, rerun on the stream's own xq
+    # with its optional outputs: products against the oracle (standard layout
+    # of the same weights), h against SiLU(g)*u, hq against Q8_1(h) and the
+    # stream's hq
+    g = torch.empty((M, F), dtype=torch.float32, device=DEV)
+    u, h = torch.empty_like(g), torch.empty_like(g)
+    hq = host(bq.q4_0_gate_up_silu_q8_1_packed(pg[-1], pu[-1], F, H,
+                                               torch.from_numpy(st["xq"]).to(DEV), M,
+                                               g=g, u=u, h=h))
+    gg, ug, hg = host(g), host(u), host(h)
+    _gemv_check(wg[-1], st["xq"], M, gg, "gate")
+    _gemv_check(wu[-1], st["xq"], M, ug, "up")
+    ref = oracle.silu_mul(gg, ug)
+    assert (np.abs(hg.astype(np.float64) - ref) <= REL * np.abs(ref) + ABS).all()
+    assert (oracle.q8_1_quantize(hg) == hq).all()
     assert (hq == st["hq"]).all()
     _gemv_check(wd[-1], st["hq"], M, host(y), "down")
