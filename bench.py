@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 ROTATE = 12
 PMC_RECORD = os.path.join(ROOT, "profiles", "pmc_q4_0_mmvq_packed_m6_ffn_up.json")
+PMC_RECORD_GATE_UP = os.path.join(ROOT, "profiles", "pmc_q4_0_gate_up_silu_q8_1_packed_m6_ffn.json")
 KERNEL_SOURCES = ["block_quantized_gemv_q8_amd/csrc/q4_0_packed.hip",
                   "block_quantized_gemv_q8_amd/csrc/bq8_dev.h"]
 
@@ -263,11 +264,11 @@ def cpu_baseline(synth, budget_s=10.0):
                       f"[17408x5120], M=6) in {el:.1f} s"}
 
 
-def pmc_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter record,
-    if it was taken on the current kernel source; else None."""
+def pmc_traffic(record=PMC_RECORD):
+    """HBM bytes per launch from a committed rocprofv3 counter record, if it
+    was taken on the current kernel source; else None."""
     try:
-        with open(PMC_RECORD) as f:
+        with open(record) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -431,6 +432,9 @@ def main():
                 "joint_GBps": round(2 * wbytes / joint_us / 1e3, 1),
                 "separate_packed_us": round(sep_us, 3),
                 "separate_gguf_us": round(sep_gguf_us, 3),
+                "pct_hbm_peak": round(100 * 2 * wbytes / joint_us / 1e3 / HBM_PEAK_GBS, 2),
+                "traffic": pmc_traffic(PMC_RECORD_GATE_UP),
+                "algorithmic_weight_bytes": 2 * wbytes,
                 "what": "gate [17408x5120] + up [17408x5120] Q4_0, M=6, SiLU(g)*u requantized "
                         "to Q8_1: one joint launch vs two packed products + silu_mul_q8_1"},
             "lmhead_top1_us": round(lm_us, 2),

@@ -249,9 +249,10 @@ bq8_status rms_norm_q8_1(const float *y, int64_t M, int64_t K, float eps, float 
 
 /* ------------------------------------------------------------------------
  * Width-M verifier FFN stream over `layers` layers, enqueued from native
- * code (five launches per layer, no host synchronization; the closure page's
- * width-6 gate/up and down projections and down-to-next-RMS/Q8 boundary, and
- * the follow-up page's shared Q8_1 activation for sibling matmuls).
+ * code (five launches per layer on standard weights, no host
+ * synchronization; the closure page's width-6 gate/up and down projections
+ * and down-to-next-RMS/Q8 boundary, and the follow-up page's shared Q8_1
+ * activation for sibling matmuls).
  * Per layer l:
  *   xq = Q8_1(x0)                        if l == 0   (q8_1_quantize)
  *   xq = rms_norm_q8_1(y, eps)           otherwise
