@@ -184,15 +184,21 @@ def time_down_sweep(torch, bq, synth, reps):
     wps = [bq.q4_0_pack(wi) for wi in ws]
     xq = bq.q8_1_quantize(torch.from_numpy(x).to("cuda"))
     wb = q4_0_bytes(N, K)
-    out = {}
+    P = bq.q4_0_mmvq_packed_splits(N, K)
+    out = {"packed_split_ranges": P}
     for m in cfg["Ms"]:
         f = getattr(bq, f"q4_0_mmvq_m{m}")
         xm = xq[:m]
         y = torch.empty((m, N), dtype=torch.float32, device="cuda")
+        yp = torch.empty((P, m, N), dtype=torch.float32, device="cuda")
         usp = time_calls(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % ROTATE], N, K, xm, m, y),
                          reps)
+        uss = time_calls(torch, lambda i: bq.q4_0_mmvq_packed_split(wps[i % ROTATE], N, K, xm, m,
+                                                                    P, yp), reps)
         us = time_calls(torch, lambda i: f(ws[i % ROTATE], xm, y), reps)
         out[str(m)] = {"packed_us": round(usp, 3), "packed_GBps": round(wb / usp / 1e3, 1),
+                       "packed_split_us": round(uss, 3),
+                       "packed_split_GBps": round(wb / uss / 1e3, 1),
                        "gguf_us": round(us, 3), "gguf_GBps": round(wb / us / 1e3, 1)}
     return out
 

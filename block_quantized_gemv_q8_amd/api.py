@@ -80,6 +80,12 @@ def lib() -> ctypes.CDLL:
         L.q4_0_pack.argtypes = [_P, _I64, _I64, _P, _I64, _P]
         L.q4_0_mmvq_packed.restype = _ST
         L.q4_0_mmvq_packed.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
+        L.q4_0_mmvq_packed_split.restype = _ST
+        L.q4_0_mmvq_packed_split.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _P, _P]
+        L.q4_0_mmvq_packed_splits.restype = _I64
+        L.q4_0_mmvq_packed_splits.argtypes = [_I64, _I64]
+        L.rms_norm_q8_1_sum.restype = _ST
+        L.rms_norm_q8_1_sum.argtypes = [_P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P]
         L.q4_0_gate_up_silu_q8_1_packed.restype = _ST
         L.q4_0_gate_up_silu_q8_1_packed.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P,
                                                     _P, _P]
@@ -254,6 +260,23 @@ def rms_norm_q8_1(y: torch.Tensor, eps: float, xq: torch.Tensor | None = None,
     return xq
 
 
+def rms_norm_q8_1_sum(yparts: torch.Tensor, eps: float, xq: torch.Tensor | None = None,
+                      y: torch.Tensor | None = None, x: torch.Tensor | None = None,
+                      want_xq: bool = True):
+    """The RMS step on the part-order sum of yparts (f32 [P][M][K]): returns
+    xq (Q8_1 [M][K/32]) unless want_xq is False; y and x, if given, receive
+    the summed and the normalized rows."""
+    P, M, K = yparts.shape
+    if want_xq:
+        xq = _out(xq, (M, K // QK * Q8_1_BYTES), torch.uint8, yparts.device, "xq")
+    xqp = _dev(xq, "xq", torch.uint8) if want_xq else None
+    yp = None if y is None else _dev(_out(y, (M, K), torch.float32, yparts.device, "y"), "y")
+    xp = None if x is None else _dev(_out(x, (M, K), torch.float32, yparts.device, "x"), "x")
+    _check("rms_norm_q8_1_sum", lib().rms_norm_q8_1_sum(
+        _dev(yparts, "yparts", torch.float32), P, M, K, float(eps), yp, xp, xqp, _stream()))
+    return xq if want_xq else None
+
+
 # ------------------------------------------------------------ packed Q4_0
 def q4_0_pack_bytes(N: int, K: int) -> int:
     return int(lib().q4_0_pack_bytes(N, K))
@@ -279,6 +302,21 @@ def q4_0_mmvq_packed(wp: torch.Tensor, N: int, K: int, xq: torch.Tensor, M: int,
         _dev(wp, "wp", torch.uint8), N, K, _dev(xq, "xq", torch.uint8), M,
         _dev(y, "y", torch.float32), _stream()))
     return y
+
+
+def q4_0_mmvq_packed_splits(N: int, K: int) -> int:
+    return int(lib().q4_0_mmvq_packed_splits(N, K))
+
+
+def q4_0_mmvq_packed_split(wp: torch.Tensor, N: int, K: int, xq: torch.Tensor, M: int,
+                           nsplit: int, ypart: torch.Tensor | None = None) -> torch.Tensor:
+    """ypart f32 [nsplit][M][N]: the packed product with K cut into nsplit
+    chunk ranges; y = ypart[0] + ypart[1] + ... in that order."""
+    ypart = _out(ypart, (nsplit, M, N), torch.float32, wp.device, "ypart")
+    _check("q4_0_mmvq_packed_split", lib().q4_0_mmvq_packed_split(
+        _dev(wp, "wp", torch.uint8), N, K, _dev(xq, "xq", torch.uint8), M, nsplit,
+        _dev(ypart, "ypart", torch.float32), _stream()))
+    return ypart
 
 
 def q4_0_gate_up_silu_q8_1_packed(wg: torch.Tensor, wu: torch.Tensor, N: int, K: int,
@@ -369,6 +407,7 @@ def stream_stages(work: torch.Tensor, M: int, hidden: int, ffn: int) -> dict:
 __all__ = ["Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "q4_0_mmvq",
            *[f"q4_0_mmvq_m{m}" for m in range(1, MAX_M + 1)], "q6k_pack_bytes",
            "q6k_pack_expand", "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1",
-           "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed",
+           "silu_mul_q8_1", "rms_norm_q8_1", "rms_norm_q8_1_sum", "q4_0_pack_bytes", "q4_0_pack",
+           "q4_0_mmvq_packed", "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits",
            "q4_0_gate_up_silu_q8_1_packed", "q4_0_ffn_stream_layout", "q4_0_ffn_stream",
            "stream_weight_table", "stream_stages", "synth"]

@@ -12,8 +12,10 @@
 //
 // The whole pass is enqueued from native code on the caller's stream, no
 // host synchronization, no allocation: five launches per layer on standard
-// weights, three on packed ones, where gate, up and the SiLU*up requant are
-// one joint launch.  Every shape and every layer's pointers are validated
+// weights, three on packed ones -- the RMS step, one joint launch for gate,
+// up and the SiLU*up requant, and a down projection split along K into
+// enough ranges to spread over every CU, whose partial sums the next RMS
+// step adds (one last sum writes y).  Every shape and every layer's pointers are validated
 // before the first launch, so a rejected call enqueues nothing.
 #include "bq8_dev.h"
 
@@ -21,9 +23,11 @@ namespace bq8 {
 
 static int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
-// Offsets of the stage buffers inside the caller's workspace.
+// Offsets of the stage buffers inside the caller's workspace; `parts`
+// holds the packed path's split down-projection sums (up to eight partial
+// [M][hidden] rows), internal to the pass.
 struct StreamLayout {
-    int64_t xq, g, u, hq, total;
+    int64_t xq, g, u, hq, parts, total;
 };
 
 static bool stream_layout(int64_t M, int64_t hidden, int64_t ffn, StreamLayout *L)
@@ -36,7 +40,8 @@ static bool stream_layout(int64_t M, int64_t hidden, int64_t ffn, StreamLayout *
     L->g = align256(M * (hidden / QK) * Q8_1_BYTES);
     L->u = L->g + align256(M * ffn * 4);
     L->hq = L->u + align256(M * ffn * 4);
-    L->total = L->hq + align256(M * (ffn / QK) * Q8_1_BYTES);
+    L->parts = L->hq + align256(M * (ffn / QK) * Q8_1_BYTES);
+    L->total = L->parts + align256(8 * M * hidden * 4);
     return true;
 }
 
@@ -92,12 +97,20 @@ static bq8_status ffn_stream(proj_fn proj, bool joint, int64_t align_k,
     float *g = reinterpret_cast<float *>(base + L.g);
     float *u = reinterpret_cast<float *>(base + L.u);
     void *hq = base + L.hq;
+    // packed path: the down projection is split in P ranges of its K, summed
+    // in range order by the next layer's RMS step (and by a last sum into y)
+    float *parts = reinterpret_cast<float *>(base + L.parts);
+    const int64_t P = joint ? q4_0_mmvq_packed_splits(hidden, ffn) : 1;
+    if (P < 1)
+        return BQ8_ERR_SHAPE;
 
     // Everything below was validated above; a nonzero status can only be a
     // launch failure, reported as is.
     bq8_status st = q8_1_quantize(x0, M, hidden, xq, stream);
     for (int64_t l = 0; l < layers && st == BQ8_OK; ++l) {
-        if (l > 0)
+        if (l > 0 && joint)
+            st = rms_norm_q8_1_sum(parts, P, M, hidden, eps, nullptr, nullptr, xq, stream);
+        if (l > 0 && !joint)
             st = rms_norm_q8_1(y, M, hidden, eps, nullptr, xq, stream);
         if (st == BQ8_OK && joint)
             st = q4_0_gate_up_silu_q8_1_packed(w_gate[l], w_up[l], ffn, hidden, xq, M, nullptr,
@@ -108,9 +121,13 @@ static bq8_status ffn_stream(proj_fn proj, bool joint, int64_t align_k,
             st = proj(w_up[l], ffn, hidden, xq, M, u, stream);
         if (st == BQ8_OK && !joint)
             st = silu_mul_q8_1(g, u, M, ffn, nullptr, hq, stream);
-        if (st == BQ8_OK)
+        if (st == BQ8_OK && joint)
+            st = q4_0_mmvq_packed_split(w_down[l], hidden, ffn, hq, M, P, parts, stream);
+        if (st == BQ8_OK && !joint)
             st = proj(w_down[l], hidden, ffn, hq, M, y, stream);
     }
+    if (st == BQ8_OK && joint)
+        st = rms_norm_q8_1_sum(parts, P, M, hidden, eps, y, nullptr, nullptr, stream);
     return st;
 }
 

@@ -109,7 +109,7 @@ struct PkShape {
 // packed nibbles start at tile[i], its scales at dtile[i]; every tile has
 // rows_t rows; chunk c of tile i starts at tile[i] + c * chunk_stride bytes
 // and its scales at dtile[i] + (c/2) * dgroup_stride elements (+4 for odd
-// c).  The activations are staged once per chunk and each A operand feeds NT
+// c).  The wave sums chunks c0 + wave, c0 + wave + S, ... below c0 + nc.  The activations are staged once per chunk and each A operand feeds NT
 // MFMAs.  ring is this wave's LDS (PkShape<M>::WAVE_LDS bytes).
 // acc[i][s][x] (lanes l < 32 after pk_pair_sum) is the sum for weight row
 // l%16 of tile i and activation row 8s + 4*(l/16) + x, 16x the exact value.
@@ -117,7 +117,7 @@ template <int M, int NT>
 __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
                                               const uint16_t *const (&dtile)[NT], int rows_t,
                                               size_t chunk_stride, size_t dgroup_stride, int nb,
-                                              const uint8_t *__restrict__ xq,
+                                              int c0, int nc, const uint8_t *__restrict__ xq,
                                               uint8_t *ring, float (&acc)[NT][PkShape<M>::MS][4])
 {
     using SH = PkShape<M>;
@@ -263,12 +263,11 @@ __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
         wave_lds_sync();
     };
 
-    const int nchunks = nb / PK_CB;
-    if (wave < nchunks) {
-        const int mine = (nchunks - wave + S - 1) / S;
+    if (wave < nc) {
+        const int mine = (nc - wave + S - 1) / S;
         u32x4 wn[NT][2], wc[NT][2];
         uint32_t dn[NT][2], dc[NT][2];
-        issue(wave, 0, wn, dn);
+        issue(c0 + wave, 0, wn, dn);
         for (int k = 0; k < mine; ++k) {
             // Taking chunk k out of the prefetch registers waits for exactly
             // its loads (nothing younger is in flight yet); the explicit wait
@@ -284,7 +283,7 @@ __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
             // no prefetch past the wave's last chunk: a repeated chunk would
             // be fetched from HBM again (the weight loads are nontemporal)
             if (k + 1 < mine)
-                issue(wave + S * (k + 1), (k + 1) & 1, wn, dn);
+                issue(c0 + wave + S * (k + 1), (k + 1) & 1, wn, dn);
             compute(k & 1, wc, dc);
         }
     }
@@ -306,12 +305,15 @@ __device__ __forceinline__ void pk_pair_sum(float (&acc)[NT][MS][4])
     __builtin_amdgcn_s_waitcnt(0);
 }
 
-// y[m][n] for the 16-row tile of workgroup blockIdx.x; the tile's S waves
-// take its 8-block chunks round-robin and their sums are added in wave order.
+// y[m][n] for one 16-row tile; the tile's S waves take its 8-block chunks
+// round-robin and their sums are added in wave order.  With nsplit > 1 the
+// chunks of each tile are cut into nsplit consecutive ranges (range p =
+// chunks p*nch/nsplit .. (p+1)*nch/nsplit - 1), workgroup p*tiles + t takes
+// range p of tile t, and its sums go to y + p*M*N.
 template <int M>
 __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__restrict__ QS,
                                                                 const uint16_t *__restrict__ D,
-                                                                int N, int nb,
+                                                                int N, int nb, int nsplit,
                                                                 const uint8_t *__restrict__ xq,
                                                                 float *__restrict__ y)
 {
@@ -321,13 +323,19 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
-    const int n0 = blockIdx.x * PK_TILE;
+    const int tiles = (N + PK_TILE - 1) / PK_TILE;
+    const int part = blockIdx.x / tiles;
+    const int n0 = (blockIdx.x - part * tiles) * PK_TILE;
     const int rows_t = (N - n0 < PK_TILE) ? N - n0 : PK_TILE;
+    const int nch = nb / PK_CB;
+    const int c0 = (int)((int64_t)part * nch / nsplit);
+    const int c1 = (int)((int64_t)(part + 1) * nch / nsplit);
+    y += (size_t)part * M * N;
     const uint8_t *tile[1] = {QS + (size_t)n0 * nb * 16};
     const uint16_t *dtile[1] = {D + (size_t)n0 * nb};
     float acc[1][MS][4];
     pk_accumulate<M, 1>(tile, dtile, rows_t, (size_t)8 * rows_t * 16, (size_t)2 * rows_t * 8, nb,
-                        xq, smem + (size_t)wave * SH::WAVE_LDS, acc);
+                        c0, c1 - c0, xq, smem + (size_t)wave * SH::WAVE_LDS, acc);
     pk_pair_sum(acc);
     __syncthreads();
     constexpr int SLOTS = MS * 4;
@@ -386,7 +394,7 @@ __global__ __launch_bounds__(512) void q4_0_gate_up_packed_kernel(
                                 DU + (size_t)n0 * nb, DU + (size_t)(n0 + PK_TILE) * nb};
     float acc[4][MS][4];
     pk_accumulate<M, 4>(tile, dtile, PK_TILE, (size_t)8 * PK_TILE * 16, (size_t)2 * PK_TILE * 8,
-                        nb, xq, smem + (size_t)wave * SH::WAVE_LDS, acc);
+                        nb, 0, nb / PK_CB, xq, smem + (size_t)wave * SH::WAVE_LDS, acc);
     pk_pair_sum(acc);
     __syncthreads();
     constexpr int SLOTS = MS * 4;
@@ -452,30 +460,30 @@ static int64_t packed_lds_limit()
 // the lighter M <= 2 (measured on the ffn_up and down shapes: two and five
 // waves per 16-row tile at M = 6, three and eight at M = 1), at least two, at
 // most eight, never more than the tile has chunks or the LDS holds.
-static int packed_waves(int64_t N, int nb, int M, int64_t wave_lds, int64_t limit)
+static int packed_waves(int64_t wgs, int64_t chunks, int M, int64_t wave_lds, int64_t limit)
 {
-    const int64_t tiles = (N + PK_TILE - 1) / PK_TILE;
     const int64_t target = M <= 2 ? 2560 : 1600;
-    int64_t s = (target + tiles - 1) / tiles;
+    int64_t s = (target + wgs - 1) / wgs;
     if (s < 2)
         s = 2;
     if (s > 8)
         s = 8;
-    if (s > nb / PK_CB)
-        s = nb / PK_CB;
+    if (s > chunks)
+        s = chunks;
     while (s > 1 && s * wave_lds > limit)
         --s;
     return (int)(s < 1 ? 1 : s);
 }
 
 template <int M>
-static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const void *xq, float *y,
-                                hipStream_t stream)
+static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const void *xq, int nsplit,
+                                float *y, hipStream_t stream)
 {
     using SH = PkShape<M>;
     const int nb = (int)(K / QK);
+    const int64_t tiles = (N + PK_TILE - 1) / PK_TILE;
     const int64_t limit = packed_lds_limit();
-    const int s = packed_waves(N, nb, M, SH::WAVE_LDS, limit);
+    const int s = packed_waves(tiles * nsplit, nb / PK_CB / nsplit, M, SH::WAVE_LDS, limit);
     const int64_t ring = (int64_t)s * SH::WAVE_LDS;
     const int64_t partial = (int64_t)s * SH::MS * 4 * 32 * (int64_t)sizeof(float);
     const int64_t lds = ring > partial ? ring : partial;
@@ -491,8 +499,8 @@ static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const v
     const uint8_t *QS = wp;
     const uint16_t *D = reinterpret_cast<const uint16_t *>(wp + N * nb * 16);
     (void)hipGetLastError();
-    hipLaunchKernelGGL((q4_0_mmvq_packed_kernel<M>), dim3((unsigned)((N + PK_TILE - 1) / PK_TILE)),
-                       dim3(WAVE * s), (size_t)lds, stream, QS, D, (int)N, nb,
+    hipLaunchKernelGGL((q4_0_mmvq_packed_kernel<M>), dim3((unsigned)(tiles * nsplit)),
+                       dim3(WAVE * s), (size_t)lds, stream, QS, D, (int)N, nb, nsplit,
                        (const uint8_t *)xq, y);
     return launch_status();
 }
@@ -551,6 +559,58 @@ static bool packed_shape_ok(int64_t N, int64_t K)
            K <= (int64_t(1) << 26) && N * (K / QK) * Q4_0_BYTES < (int64_t(1) << 40);
 }
 
+constexpr int MAX_SPLIT = 8;
+
+// The split count for a shape: enough K ranges that the launch has at least
+// 1024 workgroups (four per CU), at most MAX_SPLIT and at most one range per
+// chunk.  1 for the ffn_up shape (1088 tiles), 4 for down (320 tiles).
+static int packed_default_splits(int64_t N, int64_t K)
+{
+    const int64_t tiles = (N + PK_TILE - 1) / PK_TILE;
+    int64_t p = (1024 + tiles - 1) / tiles;
+    const int64_t nch = K / QK / PK_CB;
+    if (p > MAX_SPLIT)
+        p = MAX_SPLIT;
+    if (p > nch)
+        p = nch;
+    return (int)(p < 1 ? 1 : p);
+}
+
+static bq8_status packed_product(const void *wp, int64_t N, int64_t K, const void *xq, int64_t M,
+                                 int nsplit, float *y, void *stream)
+{
+    if (!wp || !xq || !y)
+        return BQ8_ERR_NULL;
+    if (!packed_shape_ok(N, K) || M < 1 || M > 17 || M * K >= (int64_t(1) << 31) || nsplit < 1 ||
+        nsplit > MAX_SPLIT || nsplit > K / QK / PK_CB ||
+        (int64_t)nsplit * M * N >= (int64_t(1) << 40) ||
+        (int64_t)nsplit * ((N + PK_TILE - 1) / PK_TILE) >= (int64_t(1) << 31))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(wp, 16) || !aligned(xq, 4) || !aligned(y, 4))
+        return BQ8_ERR_ALIGN;
+    const uint8_t *p = (const uint8_t *)wp;
+    hipStream_t s = (hipStream_t)stream;
+    switch (M) {
+    case 1: return packed_launch<1>(p, N, K, xq, nsplit, y, s);
+    case 2: return packed_launch<2>(p, N, K, xq, nsplit, y, s);
+    case 3: return packed_launch<3>(p, N, K, xq, nsplit, y, s);
+    case 4: return packed_launch<4>(p, N, K, xq, nsplit, y, s);
+    case 5: return packed_launch<5>(p, N, K, xq, nsplit, y, s);
+    case 6: return packed_launch<6>(p, N, K, xq, nsplit, y, s);
+    case 7: return packed_launch<7>(p, N, K, xq, nsplit, y, s);
+    case 8: return packed_launch<8>(p, N, K, xq, nsplit, y, s);
+    case 9: return packed_launch<9>(p, N, K, xq, nsplit, y, s);
+    case 10: return packed_launch<10>(p, N, K, xq, nsplit, y, s);
+    case 11: return packed_launch<11>(p, N, K, xq, nsplit, y, s);
+    case 12: return packed_launch<12>(p, N, K, xq, nsplit, y, s);
+    case 13: return packed_launch<13>(p, N, K, xq, nsplit, y, s);
+    case 14: return packed_launch<14>(p, N, K, xq, nsplit, y, s);
+    case 15: return packed_launch<15>(p, N, K, xq, nsplit, y, s);
+    case 16: return packed_launch<16>(p, N, K, xq, nsplit, y, s);
+    default: return packed_launch<17>(p, N, K, xq, nsplit, y, s);
+    }
+}
+
 } // namespace bq8
 
 using namespace bq8;
@@ -586,33 +646,23 @@ BQ8_EXPORT bq8_status q4_0_pack(const void *w, int64_t N, int64_t K, void *wp, i
 BQ8_EXPORT bq8_status q4_0_mmvq_packed(const void *wp, int64_t N, int64_t K, const void *xq,
                                        int64_t M, float *y, void *stream)
 {
-    if (!wp || !xq || !y)
-        return BQ8_ERR_NULL;
-    if (!packed_shape_ok(N, K) || M < 1 || M > 17 || M * K >= (int64_t(1) << 31))
+    return packed_product(wp, N, K, xq, M, 1, y, stream);
+}
+
+BQ8_EXPORT int64_t q4_0_mmvq_packed_splits(int64_t N, int64_t K)
+{
+    if (!packed_shape_ok(N, K))
+        return -1;
+    return packed_default_splits(N, K);
+}
+
+BQ8_EXPORT bq8_status q4_0_mmvq_packed_split(const void *wp, int64_t N, int64_t K,
+                                             const void *xq, int64_t M, int64_t nsplit,
+                                             float *ypart, void *stream)
+{
+    if (nsplit < 1 || nsplit > MAX_SPLIT)
         return BQ8_ERR_SHAPE;
-    if (!aligned(wp, 16) || !aligned(xq, 4) || !aligned(y, 4))
-        return BQ8_ERR_ALIGN;
-    const uint8_t *p = (const uint8_t *)wp;
-    hipStream_t s = (hipStream_t)stream;
-    switch (M) {
-    case 1: return packed_launch<1>(p, N, K, xq, y, s);
-    case 2: return packed_launch<2>(p, N, K, xq, y, s);
-    case 3: return packed_launch<3>(p, N, K, xq, y, s);
-    case 4: return packed_launch<4>(p, N, K, xq, y, s);
-    case 5: return packed_launch<5>(p, N, K, xq, y, s);
-    case 6: return packed_launch<6>(p, N, K, xq, y, s);
-    case 7: return packed_launch<7>(p, N, K, xq, y, s);
-    case 8: return packed_launch<8>(p, N, K, xq, y, s);
-    case 9: return packed_launch<9>(p, N, K, xq, y, s);
-    case 10: return packed_launch<10>(p, N, K, xq, y, s);
-    case 11: return packed_launch<11>(p, N, K, xq, y, s);
-    case 12: return packed_launch<12>(p, N, K, xq, y, s);
-    case 13: return packed_launch<13>(p, N, K, xq, y, s);
-    case 14: return packed_launch<14>(p, N, K, xq, y, s);
-    case 15: return packed_launch<15>(p, N, K, xq, y, s);
-    case 16: return packed_launch<16>(p, N, K, xq, y, s);
-    default: return packed_launch<17>(p, N, K, xq, y, s);
-    }
+    return packed_product(wp, N, K, xq, M, (int)nsplit, ypart, stream);
 }
 
 BQ8_EXPORT bq8_status q4_0_gate_up_silu_q8_1_packed(const void *wg, const void *wu, int64_t N,

@@ -152,6 +152,17 @@ bq8_status q4_0_mmvq(const void *w, int64_t N, int64_t K, const void *xq, int64_
  * q4_0_mmvq_packed: y[m][n] = sum_k W[n][k] X[m][k] as q4_0_mmvq_m<M>, for
  *   M = 1..17, from the packed weight; xq, y as there.  Results equal the
  *   standard-layout entry points up to the binary32 summation order.
+ * q4_0_mmvq_packed_split: the same product with K cut into nsplit ranges of
+ *   8-block chunks (range p = chunks floor(p*C/nsplit) .. floor((p+1)*C/
+ *   nsplit) - 1 of the C = K/256 chunks), each computed by its own
+ *   workgroups, so that a shape with few 16-row tiles still fills every CU.
+ *   ypart: f32 [nsplit][M][N], 4-byte aligned; ypart[p] holds range p's
+ *   sums, and y = ypart[0] + ypart[1] + ... in that order (binary32; see
+ *   rms_norm_q8_1_sum).  1 <= nsplit <= 8, nsplit <= K/256.
+ * q4_0_mmvq_packed_splits: host; the nsplit the packed stream uses for an
+ *   [N][K] projection (enough ranges for at least 1024 workgroups, at most
+ *   8), or -1 if the shape is invalid.  1 for [17408 x 5120], 4 for
+ *   [5120 x 17408].
  * Shape: 1 <= N < 2^31, 512 <= K <= 2^26, K % 512 == 0.
  * ---------------------------------------------------------------------- */
 int64_t q4_0_pack_bytes(int64_t N, int64_t K);
@@ -159,6 +170,9 @@ bq8_status q4_0_pack(const void *w, int64_t N, int64_t K, void *wp, int64_t wp_b
                      void *stream);
 bq8_status q4_0_mmvq_packed(const void *wp, int64_t N, int64_t K, const void *xq, int64_t M,
                             float *y, void *stream);
+bq8_status q4_0_mmvq_packed_split(const void *wp, int64_t N, int64_t K, const void *xq,
+                                  int64_t M, int64_t nsplit, float *ypart, void *stream);
+int64_t q4_0_mmvq_packed_splits(int64_t N, int64_t K);
 
 /* ------------------------------------------------------------------------
  * Joint gate/up projection with SiLU(gate)*up and its Q8_1 requantization
@@ -241,11 +255,19 @@ bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, const float *
  *   y: f32 [M][K]; x: optional f32 [M][K] copy (NULL to skip); xq: Q8_1
  *   [M][K/32].  Shape: 1 <= M <= 64, 32 <= K <= 32768, K % 32 == 0;
  *   eps > 0.  4-byte alignment.
+ * rms_norm_q8_1_sum: the same step on y = yparts[0] + ... + yparts[nparts-1]
+ *   (f32 [nparts][M][K], added in part order in binary32, 1 <= nparts <= 8):
+ *   the down-to-next-RMS/Q8 boundary of a split down projection.  y, x, xq
+ *   are each optional (at least one given): y receives the summed rows, x the
+ *   normalized rows, xq their Q8_1 blocks.  With nparts == 1 and y NULL it is
+ *   rms_norm_q8_1.
  * ---------------------------------------------------------------------- */
 bq8_status silu_mul_q8_1(const float *g, const float *u, int64_t M, int64_t N, float *h, void *hq,
                          void *stream);
 bq8_status rms_norm_q8_1(const float *y, int64_t M, int64_t K, float eps, float *x, void *xq,
                          void *stream);
+bq8_status rms_norm_q8_1_sum(const float *yparts, int64_t nparts, int64_t M, int64_t K, float eps,
+                             float *y, float *x, void *xq, void *stream);
 
 /* ------------------------------------------------------------------------
  * Width-M verifier FFN stream over `layers` layers, enqueued from native
@@ -269,7 +291,7 @@ bq8_status rms_norm_q8_1(const float *y, int64_t M, int64_t K, float eps, float 
  * work: device workspace of at least offsets[4] bytes from
  *   q4_0_ffn_stream_layout, 256-byte aligned.  On completion it holds the
  *   last layer's stage buffers: xq at offsets[0], g at offsets[1], u at
- *   offsets[2], hq at offsets[3].
+ *   offsets[2], hq at offsets[3].  The rest of it is internal.
  * Shape: 1 <= M <= 17, hidden and ffn multiples of 32, 32 <= hidden <= 32768,
  *   32 <= ffn <= 2^26, M*ffn < 2^31, 1 <= layers <= 2^20, eps > 0.
  * Every layer's pointers are checked before anything is enqueued.
@@ -283,10 +305,14 @@ bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *const *w_up,
                            int64_t work_bytes, void *stream);
 
 /* The same pass on offline-packed weights (q4_0_pack of each matrix), three
- * launches per layer: the gate, up and SiLU*up steps are one
- * q4_0_gate_up_silu_q8_1_packed launch and down runs through
- * q4_0_mmvq_packed.  The g and u stage buffers of the workspace are not
- * written.  hidden and ffn must also be multiples of 512. */
+ * launches per layer plus one at the end:
+ *   xq = rms_norm_q8_1_sum(parts, P)              if l > 0
+ *   hq = q4_0_gate_up_silu_q8_1_packed(w_gate[l], w_up[l], xq)
+ *   parts = q4_0_mmvq_packed_split(w_down[l], hq, P)
+ * with P = q4_0_mmvq_packed_splits(hidden, ffn), and after the last layer
+ * y = the sum of its parts (rms_norm_q8_1_sum with only y).  y is written
+ * only by that last step; the g and u stage buffers are not written.
+ * hidden and ffn must also be multiples of 512. */
 bq8_status q4_0_ffn_stream_packed(const void *const *w_gate, const void *const *w_up,
                                   const void *const *w_down, int64_t layers, int64_t M,
                                   int64_t hidden, int64_t ffn, const float *x0, float eps,

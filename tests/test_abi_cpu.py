@@ -36,7 +36,8 @@ def test_header_declares_expected_entry_points():
               "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1", "bq8_status_string",
               "bq8_abi_version", "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_ffn_stream_layout",
               "q4_0_ffn_stream", "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed",
-              "q4_0_ffn_stream_packed", "q4_0_gate_up_silu_q8_1_packed"]:
+              "q4_0_ffn_stream_packed", "q4_0_gate_up_silu_q8_1_packed",
+              "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "rms_norm_q8_1_sum"]:
         assert n in names
 
 
@@ -258,3 +259,30 @@ def test_gate_up_silu_validation(L):
     assert call(g=A + 2) == ALIGN
     assert call(u=A + 1) == ALIGN
     assert call(h=A + 3) == ALIGN
+
+
+def test_split_product_and_summed_rms_validation(L):
+    import block_quantized_gemv_q8_amd as b
+
+    assert b.q4_0_mmvq_packed_splits(17408, 5120) == 1
+    assert b.q4_0_mmvq_packed_splits(5120, 17408) == 4
+    assert b.q4_0_mmvq_packed_splits(16, 512) == 2        # capped at the 2 chunks
+    assert b.q4_0_mmvq_packed_splits(16, 4096) == 8       # capped at 8
+    assert b.q4_0_mmvq_packed_splits(16, 256) == -1
+    f = L.q4_0_mmvq_packed_split
+    assert f(None, 5120, 17408, A, 6, 4, A, None) == NULL
+    assert f(A, 5120, 17408, A, 6, 0, A, None) == SHAPE
+    assert f(A, 5120, 17408, A, 6, 9, A, None) == SHAPE
+    assert f(A, 16, 512, A, 6, 3, A, None) == SHAPE        # more ranges than chunks
+    assert f(A, 5120, 17408, A, 18, 4, A, None) == SHAPE
+    assert f(A, 5120, 17408, A, 6, 4, A + 2, None) == ALIGN
+    r = L.rms_norm_q8_1_sum
+    assert r(None, 4, 6, 5120, 1e-6, A, None, A, None) == NULL
+    assert r(A, 4, 6, 5120, 1e-6, None, None, None, None) == NULL   # nothing asked for
+    assert r(A, 0, 6, 5120, 1e-6, None, None, A, None) == SHAPE
+    assert r(A, 9, 6, 5120, 1e-6, None, None, A, None) == SHAPE
+    assert r(A, 4, 65, 5120, 1e-6, None, None, A, None) == SHAPE
+    assert r(A, 4, 6, 5120 + 16, 1e-6, None, None, A, None) == SHAPE
+    assert r(A, 4, 6, 5120, 0.0, None, None, A, None) == SHAPE
+    assert r(A + 2, 4, 6, 5120, 1e-6, None, None, A, None) == ALIGN
+    assert r(A, 4, 6, 5120, 1e-6, A + 2, None, None, None) == ALIGN

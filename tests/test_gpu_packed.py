@@ -111,3 +111,86 @@ def test_mmvq_packed_equal_rows_and_guard_bytes():
     assert (b[M * N:] == 12345.0).all()
     yy = b[:M * N].reshape(M, N)
     assert (yy[:, 100] == yy[:, 5]).all() and (yy[:, 149] == yy[:, 5]).all()
+
+
+def part_sum(parts):
+    """Sum of partial rows in part order, in binary32 (the documented order)."""
+    y = parts[0].copy()
+    for p in range(1, parts.shape[0]):
+        y += parts[p]
+    return y
+
+
+@pytest.mark.parametrize("N,K,splits", [(37, 1024, (1, 2, 3, 4)), (200, 2560, (2, 5, 8)),
+                                        (33, 5120, (3, 7)), (16, 512, (2,))])
+def test_mmvq_packed_split_ranges(N, K, splits):
+    w, x = synth.random_q4_0_case(4000 + N + K, N, K, 17)
+    xq = oracle.q8_1_quantize(x)
+    wp = bq.q4_0_pack(dev(w))
+    xqd = dev(xq)
+    for m in (1, 6, 17):
+        ref, bound = oracle.q4_0_gemv(w, N, K, xq[:m], m)
+        whole = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
+        for p in splits:
+            say(f"q4_0_mmvq_packed_split M={m} N={N} K={K} nsplit={p}")
+            parts = host(bq.q4_0_mmvq_packed_split(wp, N, K, xqd[:m], m, p))
+            assert parts.shape == (p, m, N)
+            assert_close(part_sum(parts), ref, bound, f"split {p} m{m}")
+            if p == 1:
+                assert np.array_equal(parts[0].view(np.uint32), whole.view(np.uint32))
+
+
+def test_mmvq_packed_split_ranges_are_the_documented_chunks():
+    """Part p holds exactly the blocks of chunks floor(p*C/P) .. floor((p+1)*C/P)-1:
+    weights that are zero outside one range give zero in every other part."""
+    N, K, M, P = 48, 2560, 6, 3           # C = 10 chunks: ranges 0-2, 3-5, 6-9
+    w, x = synth.random_q4_0_case(4100, N, K, M)
+    xq = oracle.q8_1_quantize(x)
+    nb = K // 32
+    blocks = w.reshape(N, nb, 18).copy()
+    blocks[:, :, 0:2] = 0                 # d = 0 everywhere ...
+    keep = slice(6 * 8, 10 * 8)           # ... except in chunks 6..9 (range 2)
+    src = w.reshape(N, nb, 18)
+    blocks[:, keep, 0:2] = src[:, keep, 0:2]
+    wz = blocks.reshape(N, nb * 18)
+    parts = host(bq.q4_0_mmvq_packed_split(bq.q4_0_pack(dev(wz)), N, K, dev(xq), M, P))
+    assert not parts[0].any() and not parts[1].any()
+    ref, bound = oracle.q4_0_gemv(wz, N, K, xq, M)
+    assert_close(parts[2], ref, bound, "range 2")
+
+
+def test_mmvq_packed_split_down_full():
+    w, x = synth.down_sweep()
+    N, K = 5120, 17408
+    P = bq.q4_0_mmvq_packed_splits(N, K)
+    assert P == 4
+    xqd = bq.q8_1_quantize(dev(x))
+    xq = host(xqd)
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
+    wp = bq.q4_0_pack(dev(w))
+    for m in (1, 6, 17):
+        say(f"down split {P} M={m}")
+        parts = host(bq.q4_0_mmvq_packed_split(wp, N, K, xqd[:m], m, P))
+        assert_close(part_sum(parts), ref[:m], bound[:m], f"down split m{m}")
+
+
+@pytest.mark.parametrize("P,M,K", [(4, 6, 5120), (1, 6, 5120), (3, 17, 1056), (8, 2, 32768),
+                                   (2, 1, 32)])
+def test_rms_norm_q8_1_sum(P, M, K):
+    say(f"rms_norm_q8_1_sum P={P} M={M} K={K}")
+    rng = np.random.default_rng(4200 + P + M + K)
+    parts = (rng.standard_normal((P, M, K)) * 10).astype(np.float32)
+    y = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    x = torch.empty_like(y)
+    xq = host(bq.rms_norm_q8_1_sum(dev(parts), 1e-6, y=y, x=x))
+    yg, xg = host(y), host(x)
+    assert np.array_equal(yg.view(np.uint32), part_sum(parts).view(np.uint32))
+    ref = oracle.rms_norm(yg, 1e-6)
+    assert (np.abs(xg.astype(np.float64) - ref) <= REL * np.abs(ref) + ABS).all()
+    assert (xq == oracle.q8_1_quantize(xg)).all()
+    # the same step on the summed rows through rms_norm_q8_1: bitwise equal
+    assert (host(bq.rms_norm_q8_1(y, 1e-6)) == xq).all()
+    # y only
+    y2 = torch.empty_like(y)
+    assert bq.rms_norm_q8_1_sum(dev(parts), 1e-6, y=y2, want_xq=False) is None
+    assert torch.equal(y2, y)

@@ -135,19 +135,23 @@ def composed_packed(wg, wu, wd, x0, eps, hidden, ffn):
     """The packed stream's steps, one C-ABI call each."""
     xq = bq.q8_1_quantize(x0)
     M = x0.shape[0]
-    y = None
+    P = bq.q4_0_mmvq_packed_splits(hidden, ffn)
+    parts = None
     for l in range(len(wg)):
         if l > 0:
-            xq = bq.rms_norm_q8_1(y, eps)
+            xq = bq.rms_norm_q8_1_sum(parts, eps)
         hq = bq.q4_0_gate_up_silu_q8_1_packed(wg[l], wu[l], ffn, hidden, xq, M)
-        y = bq.q4_0_mmvq_packed(wd[l], hidden, ffn, hq, M)
+        parts = bq.q4_0_mmvq_packed_split(wd[l], hidden, ffn, hq, M, P)
+    y = torch.empty((M, hidden), dtype=torch.float32, device=DEV)
+    bq.rms_norm_q8_1_sum(parts, eps, y=y, want_xq=False)
     return y, dict(xq=xq, hq=hq)
 
 
 @pytest.mark.parametrize("M,hidden,ffn,layers", [(6, 512, 1024, 3), (17, 1024, 1536, 2),
-                                                 (1, 512, 512, 2)])
+                                                 (1, 512, 512, 2), (6, 5120, 1024, 2)])
 def test_packed_stream_equals_composed_calls(M, hidden, ffn, layers):
-    say(f"packed stream vs composed M={M} hidden={hidden} ffn={ffn} layers={layers}")
+    say(f"packed stream vs composed M={M} hidden={hidden} ffn={ffn} layers={layers} "
+        f"down split {bq.q4_0_mmvq_packed_splits(hidden, ffn)}")
     wg = [bq.q4_0_pack(synth.q4_0_weights_device(950 + 3 * l, ffn, hidden)) for l in range(layers)]
     wu = [bq.q4_0_pack(synth.q4_0_weights_device(951 + 3 * l, ffn, hidden)) for l in range(layers)]
     wd = [bq.q4_0_pack(synth.q4_0_weights_device(952 + 3 * l, hidden, ffn)) for l in range(layers)]
