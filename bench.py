@@ -386,6 +386,17 @@ def main():
     lm_us = time_calls(torch, lambda i: lm_head_call(bq, lm), 50, warm=5)
     pack_bytes = lm["pack"].numel()
     log(f"bench: lmhead_top1 {lm_us:.2f} us, {pack_bytes / lm_us / 1e3:.1f} GB/s")
+    # head variants: all six target-side rows, and candidate-max (one drafted
+    # candidate per row) on rows 1..5
+    scratch6 = torch.empty((bq.q6k_lmhead_top1_scratch_bytes(lm["N"], lm["K"], 6),),
+                           dtype=torch.uint8, device="cuda")
+    ids6 = torch.empty((6,), dtype=torch.int32, device="cuda")
+    lm6_us = time_calls(torch, lambda i: bq.q6k_lmhead_top1(
+        lm["pack"], lm["N"], lm["K"], lm["x"], 0, 6, ids6, scratch6), 50, warm=5)
+    cand = torch.arange(5, dtype=torch.int32, device="cuda").view(5, 1) * 1000
+    cm_us = time_calls(torch, lambda i: bq.q6k_lmhead_candidate_max(
+        lm["pack"], lm["N"], lm["K"], lm["x"], 1, 5, cand, lm["scratch"]), 50, warm=5)
+    log(f"bench: lmhead rows 0..5 {lm6_us:.2f} us; candidate-max rows 1..5 {cm_us:.2f} us")
     del lm
 
     log("bench: down_sweep")
@@ -444,6 +455,8 @@ def main():
                 "what": "gate [17408x5120] + up [17408x5120] Q4_0, M=6, SiLU(g)*u requantized "
                         "to Q8_1: one joint launch vs two packed products + silu_mul_q8_1"},
             "lmhead_top1_us": round(lm_us, 2),
+            "lmhead_target_rows_0_5_us": round(lm6_us, 2),
+            "lmhead_candidate_max_rows_1_5_us": round(cm_us, 2),
             "lmhead_pack_bytes": pack_bytes,
             "lmhead_GBps": round(pack_bytes / lm_us / 1e3, 1),
             "lmhead_pct_hbm_peak": round(100 * pack_bytes / lm_us / 1e3 / HBM_PEAK_GBS, 2),

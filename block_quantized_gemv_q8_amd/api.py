@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.q6k_lmhead_top1_scratch_bytes.argtypes = [_I64, _I64, _I64]
         L.q6k_lmhead_top1.restype = _ST
         L.q6k_lmhead_top1.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P, _P, _I64, _P]
+        L.q6k_lmhead_candidate_max.restype = _ST
+        L.q6k_lmhead_candidate_max.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P, _I64,
+                                               _P, _P, _P, _P, _I64, _P]
         L.silu_mul_q8_1.restype = _ST
         L.silu_mul_q8_1.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
         L.rms_norm_q8_1.restype = _ST
@@ -232,6 +235,32 @@ def q6k_lmhead_top1(pack: torch.Tensor, N: int, K: int, x: torch.Tensor, row0: i
         _dev(ids, "ids", torch.int32), _dev(scratch, "scratch", torch.uint8), scratch.numel(),
         _stream()))
     return ids
+
+
+def q6k_lmhead_candidate_max(pack: torch.Tensor, N: int, K: int, x: torch.Tensor, row0: int,
+                             rows: int, cand_ids: torch.Tensor | None = None,
+                             scratch: torch.Tensor | None = None):
+    """(ids int32 [rows], top_vals f32 [rows], cand_scores f32 [rows][ncand]) of
+    rows row0.. of x through the pack; cand_ids int32 [rows][ncand] (or None)."""
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [M][K]")
+    ncand = 0 if cand_ids is None else cand_ids.shape[1]
+    if cand_ids is not None and cand_ids.shape[0] != rows:
+        raise ValueError("cand_ids must be [rows][ncand]")
+    ids = torch.empty((rows,), dtype=torch.int32, device=x.device)
+    vals = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    scores = torch.empty((rows, ncand), dtype=torch.float32, device=x.device)
+    need = q6k_lmhead_top1_scratch_bytes(N, K, rows)
+    if scratch is None:
+        scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    cp = _dev(cand_ids, "cand_ids", torch.int32) if ncand else None
+    sp = _dev(scores, "cand_scores", torch.float32) if ncand else None
+    _check("q6k_lmhead_candidate_max", lib().q6k_lmhead_candidate_max(
+        _dev(pack, "pack", torch.uint8), N, K, _dev(x, "x", torch.float32), M, row0, rows, cp,
+        ncand, _dev(ids, "ids", torch.int32), _dev(vals, "top_vals", torch.float32), sp,
+        _dev(scratch, "scratch", torch.uint8), scratch.numel(), _stream()))
+    return ids, vals, scores
 
 
 # --------------------------------------------------------- layer glue
@@ -407,6 +436,7 @@ def stream_stages(work: torch.Tensor, M: int, hidden: int, ffn: int) -> dict:
 __all__ = ["Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "q4_0_mmvq",
            *[f"q4_0_mmvq_m{m}" for m in range(1, MAX_M + 1)], "q6k_pack_bytes",
            "q6k_pack_expand", "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1",
+           "q6k_lmhead_candidate_max",
            "silu_mul_q8_1", "rms_norm_q8_1", "rms_norm_q8_1_sum", "q4_0_pack_bytes", "q4_0_pack",
            "q4_0_mmvq_packed", "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits",
            "q4_0_gate_up_silu_q8_1_packed", "q4_0_ffn_stream_layout", "q4_0_ffn_stream",

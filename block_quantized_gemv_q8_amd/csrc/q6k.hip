@@ -135,12 +135,17 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k)
 // Rows 0..R-1 of x (starting at row0) -> the Q8_1 quants and scales in
 // scratch, block-major so that one superblock's activations for every row
 // are contiguous: quants int8 [nb][R][32], scales f32 [nb][R] (the fp16 d of
-// the block, widened exactly).
+// the block, widened exactly).  Also sets the nscores candidate scores to
+// NaN; the fused kernel overwrites those whose id names a vocabulary row.
 __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restrict__ x, int R,
                                                             int nb, int8_t *__restrict__ xq8,
-                                                            float *__restrict__ dx)
+                                                            float *__restrict__ dx,
+                                                            float *__restrict__ scores,
+                                                            int nscores)
 {
     const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid < nscores)
+        scores[gid] = __builtin_nanf("");
     const int blk = gid >> 5; // row-major (r, b) over the R rows of x
     const int j = gid & 31;
     const bool valid = blk < R * nb;
@@ -155,11 +160,16 @@ __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restr
     }
 }
 
+// cand / ncand / scores: per activation row i, the logits of vocabulary rows
+// cand[i*ncand + c] (c < ncand) are written to scores[i*ncand + c] by the
+// one lane that computes them -- the same binary32 values the keys are made
+// of (ncand = 0: no candidates).
 template <int R>
 __global__ __launch_bounds__(TOP1_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
 q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ SC,
                 const uint16_t *__restrict__ D, int N, int K, const int8_t *__restrict__ xq8,
-                const float *__restrict__ dx, uint64_t *__restrict__ slots)
+                const float *__restrict__ dx, uint64_t *__restrict__ slots,
+                const int32_t *__restrict__ cand, int ncand, float *__restrict__ scores)
 {
     __shared__ uint64_t wave_best[TOP1_WAVES][R];
     const int lane = threadIdx.x & 63;
@@ -261,6 +271,11 @@ q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ SC,
                     best[i] = k > best[i] ? k : best[i];
                 }
             }
+            for (int c = 0; c < ncand; ++c)
+#pragma unroll
+                for (int i = 0; i < R; ++i)
+                    if (n_raw == cand[i * ncand + c])
+                        scores[i * ncand + c] = acc[i];
         }
     }
 
@@ -280,12 +295,14 @@ q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ SC,
     }
 }
 
-// One workgroup: the maximum key of each row over every slot -> ids.  Each
-// thread takes every 256th slot and all R rows of it at once, so the loads
-// are independent and the kernel waits on memory once.
+// One workgroup: the maximum key of each row over every slot -> ids, and
+// (if vals) the logit the key was made of.  Each thread takes every 256th
+// slot and all R rows of it at once, so the loads are independent and the
+// kernel waits on memory once.
 template <int R>
 __global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_final_kernel(
-    const uint64_t *__restrict__ slots, int nslots, int32_t *__restrict__ ids)
+    const uint64_t *__restrict__ slots, int nslots, int32_t *__restrict__ ids,
+    float *__restrict__ vals)
 {
     __shared__ uint64_t wave_best[TOP1_WAVES][R];
     const int lane = threadIdx.x & 63;
@@ -315,6 +332,12 @@ __global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_final_kernel(
             m = wave_best[w][threadIdx.x] > m ? wave_best[w][threadIdx.x] : m;
         // no finite logit at all -> -1
         ids[threadIdx.x] = (m == 0) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)m);
+        if (vals) {
+            // invert the order-preserving map of make_key (-0 came in as +0)
+            const uint32_t u = (uint32_t)(m >> 32);
+            const uint32_t bits = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+            vals[threadIdx.x] = (m == 0) ? __builtin_nanf("") : __builtin_bit_cast(float, bits);
+        }
     }
 }
 
@@ -341,12 +364,50 @@ static int64_t dx_area(int64_t K, int64_t rows) { return round256(rows * (K / QK
 template <int R>
 static void launch_top1(const int8_t *Q, const int8_t *SC, const uint16_t *D, int N, int K,
                         const int8_t *xq8, const float *dx, uint64_t *slots, int32_t *ids,
-                        int grid, hipStream_t s)
+                        float *vals, const int32_t *cand, int ncand, float *scores, int grid,
+                        hipStream_t s)
 {
     hipLaunchKernelGGL(q6k_top1_kernel<R>, dim3(grid), dim3(TOP1_THREADS), 0, s, Q, SC, D, N, K,
-                       xq8, dx, slots);
+                       xq8, dx, slots, cand, ncand, scores);
     hipLaunchKernelGGL(q6k_top1_final_kernel<R>, dim3(1), dim3(TOP1_THREADS), 0, s, slots, grid,
-                       ids);
+                       ids, vals);
+}
+
+constexpr int TOP1_MAX_CAND = 8;
+
+// Everything but argument checks: prep, fused kernel, final reduction.
+static bq8_status lmhead_run(const void *pack, int64_t N, int64_t K, const float *x, int64_t row0,
+                             int64_t rows, const int32_t *cand, int64_t ncand, int32_t *ids,
+                             float *vals, float *scores, void *scratch, hipStream_t s)
+{
+    const int8_t *Q = (const int8_t *)pack;
+    const int8_t *SC = Q + N * K;
+    const uint16_t *D = (const uint16_t *)(SC + N * (K / 16));
+    uint8_t *base = (uint8_t *)scratch;
+    int8_t *xq8 = (int8_t *)base;
+    float *dx = (float *)(base + xq8_area(K, rows));
+    uint64_t *slots = (uint64_t *)(base + xq8_area(K, rows) + dx_area(K, rows));
+    const int nb = (int)(K / QK);
+    const int nblocks = (int)rows * nb;
+    const int grid = (int)top1_grid(N);
+    const int nc = (int)ncand;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(q6k_top1_prep_kernel, dim3((nblocks * 32 + 255) / 256), dim3(256), 0, s,
+                       x + row0 * K, (int)rows, nb, xq8, dx, scores, (int)(rows * ncand));
+    if (hipGetLastError() != hipSuccess)
+        return BQ8_ERR_HIP;
+    const int n = (int)N, k = (int)K;
+    switch (rows) {
+    case 1: launch_top1<1>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
+    case 2: launch_top1<2>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
+    case 3: launch_top1<3>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
+    case 4: launch_top1<4>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
+    case 5: launch_top1<5>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
+    case 6: launch_top1<6>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
+    case 7: launch_top1<7>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
+    default: launch_top1<8>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
+    }
+    return launch_status();
 }
 
 } // namespace bq8
@@ -404,34 +465,29 @@ BQ8_EXPORT bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, co
         return BQ8_ERR_ALIGN;
     if (scratch_bytes < q6k_lmhead_top1_scratch_bytes(N, K, rows))
         return BQ8_ERR_SIZE;
-    const int8_t *Q = (const int8_t *)pack;
-    const int8_t *SC = Q + N * K;
-    const uint16_t *D = (const uint16_t *)(SC + N * (K / 16));
-    uint8_t *base = (uint8_t *)scratch;
-    int8_t *xq8 = (int8_t *)base;
-    float *dx = (float *)(base + xq8_area(K, rows));
-    uint64_t *slots = (uint64_t *)(base + xq8_area(K, rows) + dx_area(K, rows));
-    const int nb = (int)(K / QK);
-    const int nblocks = (int)rows * nb;
-    const int grid = (int)top1_grid(N);
-    hipStream_t s = (hipStream_t)stream;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(q6k_top1_prep_kernel, dim3((nblocks * 32 + 255) / 256), dim3(256), 0, s,
-                       x + row0 * K, (int)rows, nb, xq8, dx);
-    if (hipGetLastError() != hipSuccess)
-        return BQ8_ERR_HIP;
-    const int n = (int)N, k = (int)K;
-    switch (rows) {
-    case 1: launch_top1<1>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
-    case 2: launch_top1<2>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
-    case 3: launch_top1<3>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
-    case 4: launch_top1<4>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
-    case 5: launch_top1<5>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
-    case 6: launch_top1<6>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
-    case 7: launch_top1<7>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
-    case 8: launch_top1<8>(Q, SC, D, n, k, xq8, dx, slots, ids, grid, s); break;
-    }
-    return launch_status();
+    return lmhead_run(pack, N, K, x, row0, rows, nullptr, 0, ids, nullptr, nullptr, scratch,
+                      (hipStream_t)stream);
+}
+
+BQ8_EXPORT bq8_status q6k_lmhead_candidate_max(const void *pack, int64_t N, int64_t K,
+                                               const float *x, int64_t M, int64_t row0,
+                                               int64_t rows, const int32_t *cand_ids,
+                                               int64_t ncand, int32_t *ids, float *top_vals,
+                                               float *cand_scores, void *scratch,
+                                               int64_t scratch_bytes, void *stream)
+{
+    if (!pack || !x || !ids || !top_vals || !scratch || (ncand > 0 && (!cand_ids || !cand_scores)))
+        return BQ8_ERR_NULL;
+    if (!top1_shape_ok(N, K) || rows < 1 || rows > TOP1_MAX_ROWS || M < 1 || row0 < 0 ||
+        row0 + rows > M || M * K >= (int64_t(1) << 31) || ncand < 0 || ncand > TOP1_MAX_CAND)
+        return BQ8_ERR_SHAPE;
+    if (!aligned(pack, 16) || !aligned(x, 4) || !aligned(ids, 4) || !aligned(top_vals, 4) ||
+        !aligned(scratch, 16) || (ncand > 0 && (!aligned(cand_ids, 4) || !aligned(cand_scores, 4))))
+        return BQ8_ERR_ALIGN;
+    if (scratch_bytes < q6k_lmhead_top1_scratch_bytes(N, K, rows))
+        return BQ8_ERR_SIZE;
+    return lmhead_run(pack, N, K, x, row0, rows, ncand > 0 ? cand_ids : nullptr, ncand, ids,
+                      top_vals, ncand > 0 ? cand_scores : nullptr, scratch, (hipStream_t)stream);
 }
 
 BQ8_EXPORT const char *bq8_status_string(bq8_status status)

@@ -242,6 +242,30 @@ bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, const float *
                            int64_t scratch_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The same fused head with the outputs target-verified speculation needs
+ * ("Qwen3.6 27B AutoRound Handoff", "Current next-execution plan": a
+ * candidate-max head gives the true top ids and values plus per-row
+ * candidate scores).  For each projected row r (0 <= r < rows):
+ *   ids[r]      as q6k_lmhead_top1;
+ *   top_vals[r] the binary32 logit of ids[r] (NaN when ids[r] == -1; a
+ *               maximal -0 is reported as +0);
+ *   cand_scores[r*ncand + c], c < ncand: the binary32 logit of vocabulary
+ *               row cand_ids[r*ncand + c], the same value the top-1 search
+ *               compared (so it equals top_vals[r] bitwise when the
+ *               candidate is ids[r]); NaN when the id is outside [0, N).
+ * Target-side use: row0 = 0, rows = M = 6 projects all six rows.
+ * cand_ids: device int32 [rows][ncand]; cand_scores: device f32
+ *   [rows][ncand]; both may be NULL when ncand == 0; 0 <= ncand <= 8.
+ * top_vals: device f32 [rows].  4-byte alignment.  Other arguments, scratch
+ *   and shape as q6k_lmhead_top1.
+ * ---------------------------------------------------------------------- */
+bq8_status q6k_lmhead_candidate_max(const void *pack, int64_t N, int64_t K, const float *x,
+                                    int64_t M, int64_t row0, int64_t rows,
+                                    const int32_t *cand_ids, int64_t ncand, int32_t *ids,
+                                    float *top_vals, float *cand_scores, void *scratch,
+                                    int64_t scratch_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Verifier-layer glue between projections (a width-6 FFN block whose gate
  * and up projections share one Q8_1 activation and whose down projection
  * consumes SiLU(gate)*up requantized to Q8_1; the closure page's width-6

@@ -37,7 +37,8 @@ def test_header_declares_expected_entry_points():
               "bq8_abi_version", "silu_mul_q8_1", "rms_norm_q8_1", "q4_0_ffn_stream_layout",
               "q4_0_ffn_stream", "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed",
               "q4_0_ffn_stream_packed", "q4_0_gate_up_silu_q8_1_packed",
-              "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "rms_norm_q8_1_sum"]:
+              "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "rms_norm_q8_1_sum",
+              "q6k_lmhead_candidate_max"]:
         assert n in names
 
 
@@ -286,3 +287,28 @@ def test_split_product_and_summed_rms_validation(L):
     assert r(A, 4, 6, 5120, 0.0, None, None, A, None) == SHAPE
     assert r(A + 2, 4, 6, 5120, 1e-6, None, None, A, None) == ALIGN
     assert r(A, 4, 6, 5120, 1e-6, A + 2, None, None, None) == ALIGN
+
+
+def test_candidate_max_validation(L):
+    import block_quantized_gemv_q8_amd as b
+
+    N, K = 248320, 5120
+    need = b.q6k_lmhead_top1_scratch_bytes(N, K, 5)
+    f = L.q6k_lmhead_candidate_max
+
+    def call(pack=A, x=A, M=6, row0=1, rows=5, cand=A, ncand=2, ids=A, vals=A, scores=A,
+             scratch=A, nbytes=need):
+        return f(pack, N, K, x, M, row0, rows, cand, ncand, ids, vals, scores, scratch, nbytes,
+                 None)
+
+    assert call(vals=None) == NULL
+    assert call(cand=None) == NULL
+    assert call(scores=None) == NULL
+    assert call(ncand=9) == SHAPE
+    assert call(ncand=-1) == SHAPE
+    assert call(rows=9) == SHAPE
+    assert call(row0=2) == SHAPE            # row0 + rows > M
+    assert call(vals=A + 2) == ALIGN
+    assert call(cand=A + 2) == ALIGN
+    assert call(scores=A + 1) == ALIGN
+    assert call(nbytes=need - 1) == SIZE
