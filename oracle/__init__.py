@@ -80,6 +80,10 @@ def _declare(L):
     L.orc_q6k_pack_bytes.argtypes = [_I64, _I64]
     L.orc_q6k_pack_expand.argtypes = [_P, _I64, _I64, _P]
     L.orc_q6k_pack_logits.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
+    L.orc_q6k_compact_bytes.restype = _I64
+    L.orc_q6k_compact_bytes.argtypes = [_I64, _I64]
+    L.orc_q6k_pack_compact.argtypes = [_P, _I64, _I64, _P]
+    L.orc_q6k_compact_unpack.argtypes = [_P, _I64, _I64, _P]
     L.orc_top1.argtypes = [_P, _I64, _I64, _P]
     L.orc_q6k_lmhead_top1.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P]
     L.orc_silu_mul.argtypes = [_P, _P, _I64, _P]
@@ -237,6 +241,34 @@ def q6k_pack_logits(pack, N: int, K: int, xq, rows: int):
     bound = np.empty((rows, N), np.float64)
     lib().orc_q6k_pack_logits(_ptr(pack), N, K, _ptr(xq), rows, _ptr(logits), _ptr(bound))
     return logits, bound
+
+
+def q6k_compact_bytes(N: int, K: int) -> int:
+    return int(lib().orc_q6k_compact_bytes(N, K))
+
+
+def q6k_pack_compact(raw, N: int, K: int) -> np.ndarray:
+    """raw Q6_K [N][K/256 * 210] -> the compact pack (the same bytes, re-tiled)."""
+    raw = _c(raw, np.uint8)
+    assert raw.size == q6k_compact_bytes(N, K)
+    pack = np.empty(q6k_compact_bytes(N, K), np.uint8)
+    lib().orc_q6k_pack_compact(_ptr(raw), N, K, _ptr(pack))
+    return pack
+
+
+def q6k_compact_unpack(pack, N: int, K: int) -> np.ndarray:
+    pack = _c(pack, np.uint8)
+    assert pack.size == q6k_compact_bytes(N, K)
+    raw = np.empty((N, K // QK_K * Q6_K_BYTES), np.uint8)
+    lib().orc_q6k_compact_unpack(_ptr(pack), N, K, _ptr(raw))
+    return raw
+
+
+def q6k_compact_lmhead_top1(cpack, N: int, K: int, x, row0: int, rows: int):
+    """q6k_lmhead_top1 of the weights a compact pack encodes: unpack to raw
+    Q6_K, expand, then the same quantize + logits + top-1."""
+    return q6k_lmhead_top1(q6k_pack_expand(q6k_compact_unpack(cpack, N, K), N, K), N, K, x,
+                           row0, rows)
 
 
 def top1(logits) -> np.ndarray:

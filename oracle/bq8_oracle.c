@@ -549,6 +549,84 @@ void orc_q6k_pack_logits(const uint8_t *pack, int64_t N, int64_t K, const uint8_
 }
 
 /* ------------------------------------------------------------------------ */
+/* Compact Q6_K pack: the raw Q6_K bits themselves, re-tiled ([TOP1]         */
+/* "Memory and startup": the expanded pack is kept beside the raw Q6_K       */
+/* weights at 1,360,793,600 bytes; "Transfer to DeepSeek and future lanes":  */
+/* persistent packs are ranked by time saved per GiB).  READING -- this      */
+/* layout is the library's, not the pages': the 210 bytes of every           */
+/* superblock, in four planes, each in the 64-row tiles of the expanded      */
+/* pack (n0, r, rows_t as there):                                            */
+/*   QL plane at 0:         raw byte i (0..127) of superblock s of row n at  */
+/*        n0*(K/2) + ((8*s + i/16)*rows_t + r)*16 + i%16                     */
+/*   QH plane at N*K/2:     raw byte 128 + i (i = 0..63) at                  */
+/*        n0*(K/4) + ((4*s + i/16)*rows_t + r)*16 + i%16                     */
+/*   SC plane at N*K*3/4:   raw byte 192 + i (subscale j = 16*s + i) at the  */
+/*        expanded pack's SC position of (n, j)                              */
+/*   D  plane at N*K*13/16: raw bytes 208..209 at the expanded D position.   */
+/* Size 210 * N * K/256 bytes, the raw size.  The weights it encodes are     */
+/* those of the raw superblocks (orc_q6k_decode).                            */
+/* ------------------------------------------------------------------------ */
+
+int64_t orc_q6k_compact_bytes(int64_t N, int64_t K) { return Q6_K_BYTES * N * (K / QK_K); }
+
+/* byte offsets, within the whole pack, of raw byte `i` of superblock s of row n */
+static int64_t cpk_ql_at(int64_t n, int64_t s, int64_t i, int64_t N, int64_t K)
+{
+    int64_t n0, r, rows_t = tile_rows(n, N, &n0, &r);
+    return n0 * (K / 2) + ((8 * s + i / 16) * rows_t + r) * 16 + i % 16;
+}
+
+static int64_t cpk_qh_at(int64_t n, int64_t s, int64_t i, int64_t N, int64_t K)
+{
+    int64_t n0, r, rows_t = tile_rows(n, N, &n0, &r);
+    return N * (K / 2) + n0 * (K / 4) + ((4 * s + i / 16) * rows_t + r) * 16 + i % 16;
+}
+
+static int64_t cpk_sc_at(int64_t n, int64_t s, int64_t i, int64_t N, int64_t K)
+{
+    return N * (K / 2) + N * (K / 4) + pack_sc_at(n, 16 * s + i, N, K);
+}
+
+static int64_t cpk_d_at(int64_t n, int64_t s, int64_t N, int64_t K)
+{
+    return N * (K / 2) + N * (K / 4) + N * (K / 16) + 2 * pack_d_at(n, s, N, K);
+}
+
+void orc_q6k_pack_compact(const uint8_t *raw, int64_t N, int64_t K, uint8_t *pack)
+{
+    const int64_t ns = K / QK_K;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t s = 0; s < ns; ++s) {
+            const uint8_t *blk = raw + (n * ns + s) * Q6_K_BYTES;
+            for (int i = 0; i < 128; ++i)
+                pack[cpk_ql_at(n, s, i, N, K)] = blk[i];
+            for (int i = 0; i < 64; ++i)
+                pack[cpk_qh_at(n, s, i, N, K)] = blk[128 + i];
+            for (int i = 0; i < 16; ++i)
+                pack[cpk_sc_at(n, s, i, N, K)] = blk[192 + i];
+            pack[cpk_d_at(n, s, N, K)] = blk[208];
+            pack[cpk_d_at(n, s, N, K) + 1] = blk[209];
+        }
+}
+
+void orc_q6k_compact_unpack(const uint8_t *pack, int64_t N, int64_t K, uint8_t *raw)
+{
+    const int64_t ns = K / QK_K;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t s = 0; s < ns; ++s) {
+            uint8_t *blk = raw + (n * ns + s) * Q6_K_BYTES;
+            for (int i = 0; i < 128; ++i)
+                blk[i] = pack[cpk_ql_at(n, s, i, N, K)];
+            for (int i = 0; i < 64; ++i)
+                blk[128 + i] = pack[cpk_qh_at(n, s, i, N, K)];
+            for (int i = 0; i < 16; ++i)
+                blk[192 + i] = pack[cpk_sc_at(n, s, i, N, K)];
+            blk[208] = pack[cpk_d_at(n, s, N, K)];
+            blk[209] = pack[cpk_d_at(n, s, N, K) + 1];
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Greedy top-1 with the lowest-token-ID tie rule ([TOP1] "Exactness and     */
 /* safety contracts": generic argmax and the fused reducer share one         */
 /* lowest-ID finite-tie contract).  Scan ids ascending and replace the best  */

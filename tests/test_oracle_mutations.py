@@ -50,6 +50,14 @@ MUTATIONS = {
         "double wv = dw * (double)SC[pack_sc_at(n, k / 16, N, K)] *",
         "double wv = dw * (double)SC[pack_sc_at(n, k / 32, N, K)] *",
         ["test_oracle_q6k.py"]),
+    "q6k_compact_qh_piece_stride": (
+        "return N * (K / 2) + n0 * (K / 4) + ((4 * s + i / 16) * rows_t + r) * 16 + i % 16;",
+        "return N * (K / 2) + n0 * (K / 4) + ((4 * s + i / 16) * rows_t + r) * 16 + (i * 5) % 16;",
+        ["test_oracle_q6k_compact.py"]),
+    "q6k_compact_ql_tile_base": (
+        "return n0 * (K / 2) + ((8 * s + i / 16) * rows_t + r) * 16 + i % 16;",
+        "return n0 * (K / 2) + ((8 * s + i / 16) + r * 8 * (K / QK_K)) * 16 + i % 16;",
+        ["test_oracle_q6k_compact.py"]),
     "q4_0_packed_nibble_choice": (
         "*hi = (jj >= 8);",
         "*hi = (jj % 2);",
