@@ -25,7 +25,7 @@ oracle's CPU throughput on a bounded sample.
 
 Profiling helpers (one kernel family per process, for rocprofv3):
     python bench.py --profile-target \\
-        packed_m6|mmvq_m6|gate_up|lmhead_top1|down_sweep|stream|stream_packed|copy
+        packed_m6|mmvq_m6|gate_up|lmhead_top1|lmhead_compact|down_sweep|stream|stream_packed|copy
         [--reps R]
 """
 from __future__ import annotations
@@ -160,13 +160,12 @@ def setup_lm_head(torch, bq, synth):
     N, K = cfg["N"], cfg["K"]
     raw = synth.q6k_raw_weights_device(cfg["seed"], N, K)
     pack = bq.q6k_pack_expand(raw, N, K)
-    del raw
     rng = np.random.default_rng(cfg["seed"])
     x = torch.from_numpy(synth.normal_rows(rng, cfg["M"], K)).to("cuda")
     ids = torch.empty((cfg["rows"],), dtype=torch.int32, device="cuda")
     scratch = torch.empty((bq.q6k_lmhead_top1_scratch_bytes(N, K, cfg["rows"]),),
                           dtype=torch.uint8, device="cuda")
-    return dict(N=N, K=K, pack=pack, x=x, ids=ids, scratch=scratch, row0=cfg["row0"],
+    return dict(N=N, K=K, raw=raw, pack=pack, x=x, ids=ids, scratch=scratch, row0=cfg["row0"],
                 rows=cfg["rows"])
 
 
@@ -306,6 +305,12 @@ def profile_target(torch, bq, synth, target, reps):
         s = setup_lm_head(torch, bq, synth)
         for _ in range(reps):
             lm_head_call(bq, s)
+    elif target == "lmhead_compact":
+        s = setup_lm_head(torch, bq, synth)
+        cpk = bq.q6k_pack_compact(s["raw"], s["N"], s["K"])
+        for _ in range(reps):
+            bq.q6k_lmhead_top1(cpk, s["N"], s["K"], s["x"], s["row0"], s["rows"], s["ids"],
+                               s["scratch"], compact=True)
     elif target == "down_sweep":
         time_down_sweep(torch, bq, synth, reps)
     elif target in ("stream", "stream_packed"):
@@ -397,6 +402,14 @@ def main():
     cm_us = time_calls(torch, lambda i: bq.q6k_lmhead_candidate_max(
         lm["pack"], lm["N"], lm["K"], lm["x"], 1, 5, cand, lm["scratch"]), 50, warm=5)
     log(f"bench: lmhead rows 0..5 {lm6_us:.2f} us; candidate-max rows 1..5 {cm_us:.2f} us")
+    # the compact pack (raw Q6_K bits re-tiled) of the same weights
+    cpk = bq.q6k_pack_compact(lm["raw"], lm["N"], lm["K"])
+    lmc_us = time_calls(torch, lambda i: bq.q6k_lmhead_top1(
+        cpk, lm["N"], lm["K"], lm["x"], lm["row0"], lm["rows"], lm["ids"], lm["scratch"],
+        compact=True), 50, warm=5)
+    cpk_bytes = cpk.numel()
+    log(f"bench: lmhead_top1 compact {lmc_us:.2f} us, {cpk_bytes / lmc_us / 1e3:.1f} GB/s")
+    del cpk
     del lm
 
     log("bench: down_sweep")
@@ -456,6 +469,8 @@ def main():
                         "to Q8_1: one joint launch vs two packed products + silu_mul_q8_1"},
             "lmhead_top1_us": round(lm_us, 2),
             "lmhead_target_rows_0_5_us": round(lm6_us, 2),
+            "lmhead_top1_compact": {"us": round(lmc_us, 2), "pack_bytes": cpk_bytes,
+                                    "GBps": round(cpk_bytes / lmc_us / 1e3, 1)},
             "lmhead_candidate_max_rows_1_5_us": round(cm_us, 2),
             "lmhead_pack_bytes": pack_bytes,
             "lmhead_GBps": round(pack_bytes / lm_us / 1e3, 1),

@@ -73,6 +73,16 @@ def lib() -> ctypes.CDLL:
         L.q6k_lmhead_candidate_max.restype = _ST
         L.q6k_lmhead_candidate_max.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P, _I64,
                                                _P, _P, _P, _P, _I64, _P]
+        L.q6k_compact_bytes.restype = _I64
+        L.q6k_compact_bytes.argtypes = [_I64, _I64]
+        L.q6k_pack_compact.restype = _ST
+        L.q6k_pack_compact.argtypes = [_P, _I64, _I64, _P, _I64, _P]
+        L.q6k_lmhead_top1_compact.restype = _ST
+        L.q6k_lmhead_top1_compact.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P, _P, _I64,
+                                              _P]
+        L.q6k_lmhead_candidate_max_compact.restype = _ST
+        L.q6k_lmhead_candidate_max_compact.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P,
+                                                       _I64, _P, _P, _P, _P, _I64, _P]
         L.silu_mul_q8_1.restype = _ST
         L.silu_mul_q8_1.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
         L.rms_norm_q8_1.restype = _ST
@@ -221,8 +231,10 @@ def q6k_lmhead_top1_scratch_bytes(N: int, K: int, rows: int) -> int:
 
 
 def q6k_lmhead_top1(pack: torch.Tensor, N: int, K: int, x: torch.Tensor, row0: int, rows: int,
-                    ids: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
-    """Greedy ids int32 [rows] of rows row0.. of f32 x [M][K] through the pack."""
+                    ids: torch.Tensor | None = None, scratch: torch.Tensor | None = None,
+                    compact: bool = False):
+    """Greedy ids int32 [rows] of rows row0.. of f32 x [M][K] through the pack
+    (the expanded pack, or the compact one with compact=True)."""
     M = x.shape[0]
     if x.shape[1] != K:
         raise ValueError("x must be [M][K]")
@@ -230,16 +242,33 @@ def q6k_lmhead_top1(pack: torch.Tensor, N: int, K: int, x: torch.Tensor, row0: i
     need = q6k_lmhead_top1_scratch_bytes(N, K, rows)
     if scratch is None:
         scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    _check("q6k_lmhead_top1", lib().q6k_lmhead_top1(
+    name = "q6k_lmhead_top1_compact" if compact else "q6k_lmhead_top1"
+    _check(name, getattr(lib(), name)(
         _dev(pack, "pack", torch.uint8), N, K, _dev(x, "x", torch.float32), M, row0, rows,
         _dev(ids, "ids", torch.int32), _dev(scratch, "scratch", torch.uint8), scratch.numel(),
         _stream()))
     return ids
 
 
+def q6k_compact_bytes(N: int, K: int) -> int:
+    return int(lib().q6k_compact_bytes(N, K))
+
+
+def q6k_pack_compact(raw: torch.Tensor, N: int, K: int, pack: torch.Tensor | None = None):
+    """raw Q6_K uint8 [N][K/256*210] -> the compact pack, uint8 [bytes]."""
+    nbytes = q6k_compact_bytes(N, K)
+    if nbytes < 0:
+        raise Bq8Error("q6k_pack_compact", 2, status_string(2))
+    pack = _out(pack, (nbytes,), torch.uint8, raw.device, "pack")
+    _check("q6k_pack_compact", lib().q6k_pack_compact(
+        _dev(raw, "raw", torch.uint8), N, K, _dev(pack, "pack", torch.uint8), pack.numel(),
+        _stream()))
+    return pack
+
+
 def q6k_lmhead_candidate_max(pack: torch.Tensor, N: int, K: int, x: torch.Tensor, row0: int,
                              rows: int, cand_ids: torch.Tensor | None = None,
-                             scratch: torch.Tensor | None = None):
+                             scratch: torch.Tensor | None = None, compact: bool = False):
     """(ids int32 [rows], top_vals f32 [rows], cand_scores f32 [rows][ncand]) of
     rows row0.. of x through the pack; cand_ids int32 [rows][ncand] (or None)."""
     M = x.shape[0]
@@ -256,7 +285,8 @@ def q6k_lmhead_candidate_max(pack: torch.Tensor, N: int, K: int, x: torch.Tensor
         scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     cp = _dev(cand_ids, "cand_ids", torch.int32) if ncand else None
     sp = _dev(scores, "cand_scores", torch.float32) if ncand else None
-    _check("q6k_lmhead_candidate_max", lib().q6k_lmhead_candidate_max(
+    name = "q6k_lmhead_candidate_max_compact" if compact else "q6k_lmhead_candidate_max"
+    _check(name, getattr(lib(), name)(
         _dev(pack, "pack", torch.uint8), N, K, _dev(x, "x", torch.float32), M, row0, rows, cp,
         ncand, _dev(ids, "ids", torch.int32), _dev(vals, "top_vals", torch.float32), sp,
         _dev(scratch, "scratch", torch.uint8), scratch.numel(), _stream()))
@@ -436,7 +466,7 @@ def stream_stages(work: torch.Tensor, M: int, hidden: int, ffn: int) -> dict:
 __all__ = ["Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "q4_0_mmvq",
            *[f"q4_0_mmvq_m{m}" for m in range(1, MAX_M + 1)], "q6k_pack_bytes",
            "q6k_pack_expand", "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1",
-           "q6k_lmhead_candidate_max",
+           "q6k_lmhead_candidate_max", "q6k_compact_bytes", "q6k_pack_compact",
            "silu_mul_q8_1", "rms_norm_q8_1", "rms_norm_q8_1_sum", "q4_0_pack_bytes", "q4_0_pack",
            "q4_0_mmvq_packed", "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits",
            "q4_0_gate_up_silu_q8_1_packed", "q4_0_ffn_stream_layout", "q4_0_ffn_stream",

@@ -137,9 +137,12 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k)
 // are contiguous: quants int8 [nb][R][32], scales f32 [nb][R] (the fp16 d of
 // the block, widened exactly).  Also sets the nscores candidate scores to
 // NaN; the fused kernel overwrites those whose id names a vocabulary row.
+// With sx, also 32 x the sum of each 16-value half of every block's quants,
+// int32 [nb][R][2] (the compact layout's -32 offset correction).
 __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restrict__ x, int R,
                                                             int nb, int8_t *__restrict__ xq8,
                                                             float *__restrict__ dx,
+                                                            int32_t *__restrict__ sx,
                                                             float *__restrict__ scores,
                                                             int nscores)
 {
@@ -152,11 +155,17 @@ __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restr
     const float v = valid ? x[(size_t)blk * QK + j] : 0.0f;
     float d;
     const int q = q8_1_block_quant(v, d);
+    int hs = q; // sum over the lane's 16-value half
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1)
+        hs += __shfl_xor(hs, off, 16);
     if (valid) {
         const int r = blk / nb, b = blk - r * nb;
         xq8[((size_t)b * R + r) * QK + j] = (int8_t)q;
         if (j == 0)
             dx[(size_t)b * R + r] = h2f(f2h(d));
+        if (sx && (j & 15) == 0)
+            sx[((size_t)b * R + r) * 2 + (j >> 4)] = 32 * hs;
     }
 }
 
@@ -164,11 +173,17 @@ __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restr
 // cand[i*ncand + c] (c < ncand) are written to scores[i*ncand + c] by the
 // one lane that computes them -- the same binary32 values the keys are made
 // of (ncand = 0: no candidates).
-template <int R>
+// COMPACT: the weight comes as the compact pack's ql (Q) and qh (QH) planes
+// instead of the expanded int8 quants; per 32-block the 6-bit codes 0..63
+// are rebuilt in registers, dotted as int8, and 32 x sum(x quants) of each
+// 16-value half (sx) is subtracted, which gives the expanded kernel's
+// integer exactly.
+template <int R, bool COMPACT>
 __global__ __launch_bounds__(TOP1_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
-q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ SC,
-                const uint16_t *__restrict__ D, int N, int K, const int8_t *__restrict__ xq8,
-                const float *__restrict__ dx, uint64_t *__restrict__ slots,
+q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ QH,
+                const int8_t *__restrict__ SC, const uint16_t *__restrict__ D, int N, int K,
+                const int8_t *__restrict__ xq8, const float *__restrict__ dx,
+                const int32_t *__restrict__ sx, uint64_t *__restrict__ slots,
                 const int32_t *__restrict__ cand, int ncand, float *__restrict__ scores)
 {
     __shared__ uint64_t wave_best[TOP1_WAVES][R];
@@ -187,7 +202,8 @@ q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ SC,
         const int rows_t = (N - n0 < PACK_TILE) ? N - n0 : PACK_TILE;
         const int r = lane < rows_t ? lane : rows_t - 1; // ragged tile: repeat the last row
         const int n_raw = n0 + lane;
-        const int8_t *qt = Q + (size_t)n0 * K;
+        const int8_t *qt = Q + (size_t)n0 * (COMPACT ? K / 2 : K);
+        const int8_t *ht = COMPACT ? QH + (size_t)n0 * (K / 4) : nullptr;
         const int8_t *st = SC + (size_t)n0 * (K / 16);
         const uint16_t *dt = D + (size_t)n0 * nsb;
         float acc[R];
@@ -195,34 +211,71 @@ q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ SC,
         for (int i = 0; i < R; ++i)
             acc[i] = 0.0f;
 
-        // pieces 16 sb + 8 half .. +7 of this lane's row: 128 quants
+        // expanded: pieces 16 sb + 8 half .. +7 of this lane's row (128
+        // quants); compact: ql pieces 8 sb + 4 half .. +3 in v[0..3], qh
+        // pieces 4 sb + 2 half .. +1 in v[4..5]
         auto load_half = [&](u32x4(&v)[8], int sb, int half) {
-            const int c0 = sb * 16 + half * 8;
+            if constexpr (COMPACT) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                    qt + ((size_t)(c0 + j) * rows_t + r) * 16));
+                for (int j = 0; j < 4; ++j)
+                    v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                        qt + ((size_t)(sb * 8 + half * 4 + j) * rows_t + r) * 16));
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    v[4 + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                        ht + ((size_t)(sb * 4 + half * 2 + j) * rows_t + r) * 16));
+            } else {
+                const int c0 = sb * 16 + half * 8;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                        qt + ((size_t)(c0 + j) * rows_t + r) * 16));
+            }
         };
         // 32-blocks 4 half .. 4 half + 3 of the superblock, every activation row
         auto compute_half = [&](const u32x4(&v)[8], int half, const u32x4 &scw,
-                                const int8_t *xs, const float *ds, float(&accsb)[R]) {
+                                const int8_t *xs, const float *ds, const int32_t *xsum,
+                                float(&accsb)[R]) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int bl = half * 4 + j;
                 const uint32_t scword = scw[bl >> 1];
                 const int sca = __builtin_amdgcn_sbfe(scword, 16 * (bl & 1), 8);
                 const int scb = __builtin_amdgcn_sbfe(scword, 16 * (bl & 1) + 8, 8);
+                // the block's 32 weights as 8 words of 4 signed bytes
+                int w[8];
+                if constexpr (COMPACT) {
+                    // code of value l (0..31) of block 4 half + j: low (j < 2)
+                    // or high nibble of ql byte 32 (j & 1) + l of the half,
+                    // bits 2j..2j+1 of its qh byte l
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const uint32_t qlw = v[2 * (j & 1) + (k >> 2)][k & 3];
+                        const uint32_t qhw = v[4 + (k >> 2)][k & 3];
+                        const uint32_t lo = ((j < 2) ? qlw : (qlw >> 4)) & 0x0F0F0F0Fu;
+                        w[k] = (int)(lo | (((qhw >> (2 * j)) & 0x03030303u) << 4));
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        w[k] = (int)v[2 * j + (k >> 2)][k & 3];
+                }
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
                     const int *xb = reinterpret_cast<const int *>(xs + (bl * R + i) * QK);
-                    int sa = dot4((int)v[2 * j][0], xb[0], 0);
-                    sa = dot4((int)v[2 * j][1], xb[1], sa);
-                    sa = dot4((int)v[2 * j][2], xb[2], sa);
-                    sa = dot4((int)v[2 * j][3], xb[3], sa);
-                    int sbv = dot4((int)v[2 * j + 1][0], xb[4], 0);
-                    sbv = dot4((int)v[2 * j + 1][1], xb[5], sbv);
-                    sbv = dot4((int)v[2 * j + 1][2], xb[6], sbv);
-                    sbv = dot4((int)v[2 * j + 1][3], xb[7], sbv);
+                    int sa = dot4(w[0], xb[0], 0);
+                    sa = dot4(w[1], xb[1], sa);
+                    sa = dot4(w[2], xb[2], sa);
+                    sa = dot4(w[3], xb[3], sa);
+                    int sbv = dot4(w[4], xb[4], 0);
+                    sbv = dot4(w[5], xb[5], sbv);
+                    sbv = dot4(w[6], xb[6], sbv);
+                    sbv = dot4(w[7], xb[7], sbv);
+                    if constexpr (COMPACT) {
+                        // codes 0..63 stand for q + 32
+                        sa -= xsum[(bl * R + i) * 2];
+                        sbv -= xsum[(bl * R + i) * 2 + 1];
+                    }
                     // |sa|, |sbv| <= 16 * 32 * 127 < 2^23: exact 24-bit products
                     const int I = __mul24(sa, sca) + __mul24(sbv, scb);
                     accsb[i] = fmaf((float)I, ds[bl * R + i], accsb[i]);
@@ -247,13 +300,14 @@ q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ SC,
             const uint32_t dbits_next = dt[(size_t)sbn * rows_t + r];
             const int8_t *xs = xq8 + (size_t)sb * 8 * R * QK;
             const float *ds = dx + (size_t)sb * 8 * R;
+            const int32_t *xsum = COMPACT ? sx + (size_t)sb * 8 * R * 2 : nullptr;
             float accsb[R];
 #pragma unroll
             for (int i = 0; i < R; ++i)
                 accsb[i] = 0.0f;
-            compute_half(va, 0, scw, xs, ds, accsb);
+            compute_half(va, 0, scw, xs, ds, xsum, accsb);
             load_half(va, sbn, 0);
-            compute_half(vb, 1, scw, xs, ds, accsb);
+            compute_half(vb, 1, scw, xs, ds, xsum, accsb);
             load_half(vb, sbn, 1);
             const float dw = h2f(dbits);
 #pragma unroll
@@ -360,54 +414,124 @@ static int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 // per (workgroup, row); each area starts on a 256-byte boundary.
 static int64_t xq8_area(int64_t K, int64_t rows) { return round256(rows * K); }
 static int64_t dx_area(int64_t K, int64_t rows) { return round256(rows * (K / QK) * 4); }
+static int64_t sx_area(int64_t K, int64_t rows) { return round256(rows * (K / QK) * 2 * 4); }
 
-template <int R>
-static void launch_top1(const int8_t *Q, const int8_t *SC, const uint16_t *D, int N, int K,
-                        const int8_t *xq8, const float *dx, uint64_t *slots, int32_t *ids,
-                        float *vals, const int32_t *cand, int ncand, float *scores, int grid,
-                        hipStream_t s)
+template <int R, bool COMPACT>
+static void launch_top1(const int8_t *Q, const int8_t *QH, const int8_t *SC, const uint16_t *D,
+                        int N, int K, const int8_t *xq8, const float *dx, const int32_t *sx,
+                        uint64_t *slots, int32_t *ids, float *vals, const int32_t *cand,
+                        int ncand, float *scores, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(q6k_top1_kernel<R>, dim3(grid), dim3(TOP1_THREADS), 0, s, Q, SC, D, N, K,
-                       xq8, dx, slots, cand, ncand, scores);
+    hipLaunchKernelGGL((q6k_top1_kernel<R, COMPACT>), dim3(grid), dim3(TOP1_THREADS), 0, s, Q, QH,
+                       SC, D, N, K, xq8, dx, sx, slots, cand, ncand, scores);
     hipLaunchKernelGGL(q6k_top1_final_kernel<R>, dim3(1), dim3(TOP1_THREADS), 0, s, slots, grid,
                        ids, vals);
+}
+
+template <bool COMPACT>
+static void launch_top1_rows(int rows, const int8_t *Q, const int8_t *QH, const int8_t *SC,
+                             const uint16_t *D, int N, int K, const int8_t *xq8, const float *dx,
+                             const int32_t *sx, uint64_t *slots, int32_t *ids, float *vals,
+                             const int32_t *cand, int ncand, float *scores, int grid,
+                             hipStream_t s)
+{
+#define BQ8_TOP1_CASE(r)                                                                           \
+    case r:                                                                                        \
+        launch_top1<r, COMPACT>(Q, QH, SC, D, N, K, xq8, dx, sx, slots, ids, vals, cand, ncand,    \
+                                scores, grid, s);                                                  \
+        break;
+    switch (rows) {
+        BQ8_TOP1_CASE(1)
+        BQ8_TOP1_CASE(2)
+        BQ8_TOP1_CASE(3)
+        BQ8_TOP1_CASE(4)
+        BQ8_TOP1_CASE(5)
+        BQ8_TOP1_CASE(6)
+        BQ8_TOP1_CASE(7)
+        BQ8_TOP1_CASE(8)
+    }
+#undef BQ8_TOP1_CASE
 }
 
 constexpr int TOP1_MAX_CAND = 8;
 
 // Everything but argument checks: prep, fused kernel, final reduction.
-static bq8_status lmhead_run(const void *pack, int64_t N, int64_t K, const float *x, int64_t row0,
-                             int64_t rows, const int32_t *cand, int64_t ncand, int32_t *ids,
-                             float *vals, float *scores, void *scratch, hipStream_t s)
+// compact: pack is the compact layout (ql | qh | subscales | scales planes),
+// else the expanded one (quants | subscales | scales).
+static bq8_status lmhead_run(const void *pack, bool compact, int64_t N, int64_t K, const float *x,
+                             int64_t row0, int64_t rows, const int32_t *cand, int64_t ncand,
+                             int32_t *ids, float *vals, float *scores, void *scratch,
+                             hipStream_t s)
 {
     const int8_t *Q = (const int8_t *)pack;
-    const int8_t *SC = Q + N * K;
+    const int8_t *QH = compact ? Q + N * (K / 2) : nullptr;
+    const int8_t *SC = compact ? Q + N * (K / 2) + N * (K / 4) : Q + N * K;
     const uint16_t *D = (const uint16_t *)(SC + N * (K / 16));
     uint8_t *base = (uint8_t *)scratch;
     int8_t *xq8 = (int8_t *)base;
     float *dx = (float *)(base + xq8_area(K, rows));
-    uint64_t *slots = (uint64_t *)(base + xq8_area(K, rows) + dx_area(K, rows));
+    int32_t *sx = (int32_t *)(base + xq8_area(K, rows) + dx_area(K, rows));
+    uint64_t *slots =
+        (uint64_t *)(base + xq8_area(K, rows) + dx_area(K, rows) + sx_area(K, rows));
     const int nb = (int)(K / QK);
     const int nblocks = (int)rows * nb;
     const int grid = (int)top1_grid(N);
     const int nc = (int)ncand;
     (void)hipGetLastError();
     hipLaunchKernelGGL(q6k_top1_prep_kernel, dim3((nblocks * 32 + 255) / 256), dim3(256), 0, s,
-                       x + row0 * K, (int)rows, nb, xq8, dx, scores, (int)(rows * ncand));
+                       x + row0 * K, (int)rows, nb, xq8, dx, compact ? sx : nullptr, scores,
+                       (int)(rows * ncand));
     if (hipGetLastError() != hipSuccess)
         return BQ8_ERR_HIP;
-    const int n = (int)N, k = (int)K;
-    switch (rows) {
-    case 1: launch_top1<1>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
-    case 2: launch_top1<2>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
-    case 3: launch_top1<3>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
-    case 4: launch_top1<4>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
-    case 5: launch_top1<5>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
-    case 6: launch_top1<6>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
-    case 7: launch_top1<7>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
-    default: launch_top1<8>(Q, SC, D, n, k, xq8, dx, slots, ids, vals, cand, nc, scores, grid, s); break;
-    }
+    const int n = (int)N, k = (int)K, r = (int)rows;
+    if (compact)
+        launch_top1_rows<true>(r, Q, QH, SC, D, n, k, xq8, dx, sx, slots, ids, vals, cand, nc,
+                               scores, grid, s);
+    else
+        launch_top1_rows<false>(r, Q, QH, SC, D, n, k, xq8, dx, sx, slots, ids, vals, cand, nc,
+                                scores, grid, s);
     return launch_status();
+}
+
+// Compact pack, one thread per (row, superblock, 16-byte piece): pieces
+// 0..7 of ql, 0..3 of qh, the 16 subscales (that thread also moves d).  The
+// raw superblocks are 2-byte aligned, so pieces are read as halfwords.
+__global__ __launch_bounds__(256) void q6k_compact_kernel(const uint8_t *__restrict__ raw, int N,
+                                                          int K, uint8_t *__restrict__ QL,
+                                                          uint8_t *__restrict__ QH,
+                                                          uint8_t *__restrict__ SCP,
+                                                          uint16_t *__restrict__ DP)
+{
+    const int ns = K / QK_K;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)N * ns * 13)
+        return;
+    const int part = (int)(i % 13);
+    const int64_t ns_i = i / 13;
+    const int n = (int)(ns_i / ns), sb = (int)(ns_i - (int64_t)n * ns);
+    int n0, r;
+    const int rows_t = tile_of(n, N, n0, r);
+    const uint8_t *blk = raw + ((int64_t)n * ns + sb) * Q6_K_BYTES;
+    int src;
+    uint8_t *dst;
+    if (part < 8) {
+        src = 16 * part;
+        dst = QL + (int64_t)n0 * (K / 2) + ((int64_t)(8 * sb + part) * rows_t + r) * 16;
+    } else if (part < 12) {
+        src = 128 + 16 * (part - 8);
+        dst = QH + (int64_t)n0 * (K / 4) + ((int64_t)(4 * sb + part - 8) * rows_t + r) * 16;
+    } else {
+        src = 192;
+        dst = SCP + (int64_t)n0 * (K / 16) + ((int64_t)sb * rows_t + r) * 16;
+        DP[(int64_t)n0 * ns + (int64_t)sb * rows_t + r] =
+            *reinterpret_cast<const uint16_t *>(blk + 208);
+    }
+    const uint16_t *hw = reinterpret_cast<const uint16_t *>(blk + src);
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        v[w] = (uint32_t)hw[2 * w] | ((uint32_t)hw[2 * w + 1] << 16);
+    *reinterpret_cast<u32x4 *>(dst) = v;
 }
 
 } // namespace bq8
@@ -449,7 +573,8 @@ BQ8_EXPORT int64_t q6k_lmhead_top1_scratch_bytes(int64_t N, int64_t K, int64_t r
 {
     if (!top1_shape_ok(N, K) || rows < 1 || rows > TOP1_MAX_ROWS)
         return -1;
-    return xq8_area(K, rows) + dx_area(K, rows) + top1_grid(N) * rows * (int64_t)sizeof(uint64_t);
+    return xq8_area(K, rows) + dx_area(K, rows) + sx_area(K, rows) +
+           top1_grid(N) * rows * (int64_t)sizeof(uint64_t);
 }
 
 BQ8_EXPORT bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, const float *x,
@@ -465,16 +590,15 @@ BQ8_EXPORT bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, co
         return BQ8_ERR_ALIGN;
     if (scratch_bytes < q6k_lmhead_top1_scratch_bytes(N, K, rows))
         return BQ8_ERR_SIZE;
-    return lmhead_run(pack, N, K, x, row0, rows, nullptr, 0, ids, nullptr, nullptr, scratch,
-                      (hipStream_t)stream);
+    return lmhead_run(pack, false, N, K, x, row0, rows, nullptr, 0, ids, nullptr, nullptr,
+                      scratch, (hipStream_t)stream);
 }
 
-BQ8_EXPORT bq8_status q6k_lmhead_candidate_max(const void *pack, int64_t N, int64_t K,
-                                               const float *x, int64_t M, int64_t row0,
-                                               int64_t rows, const int32_t *cand_ids,
-                                               int64_t ncand, int32_t *ids, float *top_vals,
-                                               float *cand_scores, void *scratch,
-                                               int64_t scratch_bytes, void *stream)
+static bq8_status candidate_max(const void *pack, bool compact, int64_t N, int64_t K,
+                                const float *x, int64_t M, int64_t row0, int64_t rows,
+                                const int32_t *cand_ids, int64_t ncand, int32_t *ids,
+                                float *top_vals, float *cand_scores, void *scratch,
+                                int64_t scratch_bytes, void *stream)
 {
     if (!pack || !x || !ids || !top_vals || !scratch || (ncand > 0 && (!cand_ids || !cand_scores)))
         return BQ8_ERR_NULL;
@@ -486,8 +610,81 @@ BQ8_EXPORT bq8_status q6k_lmhead_candidate_max(const void *pack, int64_t N, int6
         return BQ8_ERR_ALIGN;
     if (scratch_bytes < q6k_lmhead_top1_scratch_bytes(N, K, rows))
         return BQ8_ERR_SIZE;
-    return lmhead_run(pack, N, K, x, row0, rows, ncand > 0 ? cand_ids : nullptr, ncand, ids,
-                      top_vals, ncand > 0 ? cand_scores : nullptr, scratch, (hipStream_t)stream);
+    return lmhead_run(pack, compact, N, K, x, row0, rows, ncand > 0 ? cand_ids : nullptr, ncand,
+                      ids, top_vals, ncand > 0 ? cand_scores : nullptr, scratch,
+                      (hipStream_t)stream);
+}
+
+BQ8_EXPORT bq8_status q6k_lmhead_candidate_max(const void *pack, int64_t N, int64_t K,
+                                               const float *x, int64_t M, int64_t row0,
+                                               int64_t rows, const int32_t *cand_ids,
+                                               int64_t ncand, int32_t *ids, float *top_vals,
+                                               float *cand_scores, void *scratch,
+                                               int64_t scratch_bytes, void *stream)
+{
+    return candidate_max(pack, false, N, K, x, M, row0, rows, cand_ids, ncand, ids, top_vals,
+                         cand_scores, scratch, scratch_bytes, stream);
+}
+
+BQ8_EXPORT int64_t q6k_compact_bytes(int64_t N, int64_t K)
+{
+    if (N < 1 || N >= (int64_t(1) << 31) || K < QK_K || K % QK_K != 0 ||
+        N > (int64_t(1) << 40) / K)
+        return -1;
+    return N * (K / QK_K) * Q6_K_BYTES;
+}
+
+BQ8_EXPORT bq8_status q6k_pack_compact(const void *raw, int64_t N, int64_t K, void *pack,
+                                       int64_t pack_bytes, void *stream)
+{
+    if (!raw || !pack)
+        return BQ8_ERR_NULL;
+    if (q6k_compact_bytes(N, K) < 0 || N * (K / QK_K) * 13 >= (int64_t(1) << 40))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(raw, 2) || !aligned(pack, 16))
+        return BQ8_ERR_ALIGN;
+    if (pack_bytes != q6k_compact_bytes(N, K))
+        return BQ8_ERR_SIZE;
+    uint8_t *QL = (uint8_t *)pack;
+    uint8_t *QH = QL + N * (K / 2);
+    uint8_t *SCP = QH + N * (K / 4);
+    uint16_t *DP = (uint16_t *)(SCP + N * (K / 16));
+    const int64_t items = N * (K / QK_K) * 13;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(q6k_compact_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, (const uint8_t *)raw, (int)N, (int)K, QL, QH, SCP,
+                       DP);
+    return launch_status();
+}
+
+BQ8_EXPORT bq8_status q6k_lmhead_top1_compact(const void *pack, int64_t N, int64_t K,
+                                              const float *x, int64_t M, int64_t row0,
+                                              int64_t rows, int32_t *ids, void *scratch,
+                                              int64_t scratch_bytes, void *stream)
+{
+    if (!pack || !x || !ids || !scratch)
+        return BQ8_ERR_NULL;
+    if (!top1_shape_ok(N, K) || rows < 1 || rows > TOP1_MAX_ROWS || M < 1 || row0 < 0 ||
+        row0 + rows > M || M * K >= (int64_t(1) << 31))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(pack, 16) || !aligned(x, 4) || !aligned(ids, 4) || !aligned(scratch, 16))
+        return BQ8_ERR_ALIGN;
+    if (scratch_bytes < q6k_lmhead_top1_scratch_bytes(N, K, rows))
+        return BQ8_ERR_SIZE;
+    return lmhead_run(pack, true, N, K, x, row0, rows, nullptr, 0, ids, nullptr, nullptr,
+                      scratch, (hipStream_t)stream);
+}
+
+BQ8_EXPORT bq8_status q6k_lmhead_candidate_max_compact(const void *pack, int64_t N, int64_t K,
+                                                       const float *x, int64_t M, int64_t row0,
+                                                       int64_t rows, const int32_t *cand_ids,
+                                                       int64_t ncand, int32_t *ids,
+                                                       float *top_vals, float *cand_scores,
+                                                       void *scratch, int64_t scratch_bytes,
+                                                       void *stream)
+{
+    return candidate_max(pack, true, N, K, x, M, row0, rows, cand_ids, ncand, ids, top_vals,
+                         cand_scores, scratch, scratch_bytes, stream);
 }
 
 BQ8_EXPORT const char *bq8_status_string(bq8_status status)

@@ -226,8 +226,9 @@ bq8_status q6k_pack_expand(const void *raw, int64_t N, int64_t K, void *pack, in
  *          M = 6, row0 = 1, rows = 5); 1 <= rows <= 8, row0 + rows <= M.
  * ids:     int32 [rows]; ids[r] is the greedy token id of row row0 + r.
  * scratch: device workspace of at least q6k_lmhead_top1_scratch_bytes(N, K,
- *          rows) bytes, 16-byte aligned (quantized rows and one key per
- *          workgroup and row); its contents on entry do not matter.  Three
+ *          rows) bytes, 16-byte aligned (quantized rows, their 16-value
+ *          sums and one key per workgroup and row); its contents on entry do
+ *          not matter.  Three
  *          kernels run in stream order: quantize, fused projection + per-
  *          workgroup reduction, final reduction.
  * Shape: 1 <= N < 2^31 - 1, K >= 256, K % 256 == 0, N*K < 2^40.
@@ -264,6 +265,42 @@ bq8_status q6k_lmhead_candidate_max(const void *pack, int64_t N, int64_t K, cons
                                     const int32_t *cand_ids, int64_t ncand, int32_t *ids,
                                     float *top_vals, float *cand_scores, void *scratch,
                                     int64_t scratch_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Compact Q6_K pack: the raw Q6_K bits, re-tiled, so the fused head streams
+ * 210 bytes per 256 weights instead of the expanded pack's 274 (the
+ * fused-head page keeps its 1,360,793,600-byte expanded pack beside the
+ * raw weights, "Memory and startup", and ranks persistent packs by time
+ * saved per GiB, "Transfer to DeepSeek and future lanes").  Layout, with
+ * the tiles of the expanded pack (n0, r, rows_t as there):
+ *   QL plane (N*K/2 bytes at 0): raw byte i (0..127) of superblock s of row
+ *       n at n0*(K/2) + ((8*s + i/16)*rows_t + r)*16 + i%16;
+ *   QH plane (N*K/4 bytes at N*K/2): raw byte 128 + i (i = 0..63) at
+ *       n0*(K/4) + ((4*s + i/16)*rows_t + r)*16 + i%16;
+ *   SC plane (N*K/16 bytes at N*K*3/4): the subscales, as the expanded SC;
+ *   D plane (N*K/128 bytes at N*K*13/16): the fp16 d, as the expanded D.
+ * q6k_compact_bytes: host; 210*N*K/256, or -1 if the shape is invalid
+ *   (1,042,944,000 for [248320 x 5120]).
+ * q6k_pack_compact: raw Q6_K [N][K/256] (2-byte aligned) -> pack (16-byte
+ *   aligned, pack_bytes == q6k_compact_bytes, fully overwritten).
+ * q6k_lmhead_top1_compact, q6k_lmhead_candidate_max_compact: the fused head
+ *   on the compact pack, with the arguments, scratch size and results of
+ *   q6k_lmhead_top1 and q6k_lmhead_candidate_max.  For the same raw weights
+ *   the logits are bitwise those of the expanded pack (the 6-bit codes are
+ *   rebuilt in registers and the -32 offset is applied to exact integer
+ *   dots), so ids, values and scores are identical.
+ * ---------------------------------------------------------------------- */
+int64_t q6k_compact_bytes(int64_t N, int64_t K);
+bq8_status q6k_pack_compact(const void *raw, int64_t N, int64_t K, void *pack, int64_t pack_bytes,
+                            void *stream);
+bq8_status q6k_lmhead_top1_compact(const void *pack, int64_t N, int64_t K, const float *x,
+                                   int64_t M, int64_t row0, int64_t rows, int32_t *ids,
+                                   void *scratch, int64_t scratch_bytes, void *stream);
+bq8_status q6k_lmhead_candidate_max_compact(const void *pack, int64_t N, int64_t K,
+                                            const float *x, int64_t M, int64_t row0,
+                                            int64_t rows, const int32_t *cand_ids, int64_t ncand,
+                                            int32_t *ids, float *top_vals, float *cand_scores,
+                                            void *scratch, int64_t scratch_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Verifier-layer glue between projections (a width-6 FFN block whose gate

@@ -38,7 +38,8 @@ def test_header_declares_expected_entry_points():
               "q4_0_ffn_stream", "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed",
               "q4_0_ffn_stream_packed", "q4_0_gate_up_silu_q8_1_packed",
               "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "rms_norm_q8_1_sum",
-              "q6k_lmhead_candidate_max"]:
+              "q6k_lmhead_candidate_max", "q6k_compact_bytes", "q6k_pack_compact",
+              "q6k_lmhead_top1_compact", "q6k_lmhead_candidate_max_compact"]:
         assert n in names
 
 
@@ -312,3 +313,27 @@ def test_candidate_max_validation(L):
     assert call(cand=A + 2) == ALIGN
     assert call(scores=A + 1) == ALIGN
     assert call(nbytes=need - 1) == SIZE
+
+
+def test_compact_q6k_validation(L):
+    import block_quantized_gemv_q8_amd as b
+
+    assert b.q6k_compact_bytes(248320, 5120) == 1_042_944_000
+    assert b.q6k_compact_bytes(1, 256) == 210
+    assert b.q6k_compact_bytes(4, 384) == -1
+    assert b.q6k_compact_bytes(0, 256) == -1
+    n = b.q6k_compact_bytes(248320, 5120)
+    assert L.q6k_pack_compact(None, 248320, 5120, A, n, None) == NULL
+    assert L.q6k_pack_compact(A, 248320, 5120 + 128, A, n, None) == SHAPE
+    assert L.q6k_pack_compact(A + 1, 248320, 5120, A, n, None) == ALIGN
+    assert L.q6k_pack_compact(A, 248320, 5120, A + 8, n, None) == ALIGN
+    assert L.q6k_pack_compact(A, 248320, 5120, A, n + 1, None) == SIZE
+    need = b.q6k_lmhead_top1_scratch_bytes(248320, 5120, 5)
+    t = L.q6k_lmhead_top1_compact
+    assert t(None, 248320, 5120, A, 6, 1, 5, A, A, need, None) == NULL
+    assert t(A, 248320, 5120, A, 6, 2, 5, A, A, need, None) == SHAPE
+    assert t(A + 8, 248320, 5120, A, 6, 1, 5, A, A, need, None) == ALIGN
+    assert t(A, 248320, 5120, A, 6, 1, 5, A, A, need - 1, None) == SIZE
+    c = L.q6k_lmhead_candidate_max_compact
+    assert c(A, 248320, 5120, A, 6, 1, 5, A, 2, A, None, A, A, need, None) == NULL
+    assert c(A, 248320, 5120, A, 6, 1, 5, A, 9, A, A, A, A, need, None) == SHAPE
