@@ -137,7 +137,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k)
 // are contiguous: quants int8 [nb][R][32], scales f32 [nb][R] (the fp16 d of
 // the block, widened exactly).  Also sets the nscores candidate scores to
 // NaN; the fused kernel overwrites those whose id names a vocabulary row.
-// With sx, also 32 x the sum of each 16-value half of every block's quants,
+// With sx, also -32 x the sum of each 16-value half of every block's quants,
 // int32 [nb][R][2] (the compact layout's -32 offset correction).
 __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restrict__ x, int R,
                                                             int nb, int8_t *__restrict__ xq8,
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restr
         if (j == 0)
             dx[(size_t)b * R + r] = h2f(f2h(d));
         if (sx && (j & 15) == 0)
-            sx[((size_t)b * R + r) * 2 + (j >> 4)] = 32 * hs;
+            sx[((size_t)b * R + r) * 2 + (j >> 4)] = -32 * hs;
     }
 }
 
@@ -175,9 +175,9 @@ __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restr
 // of (ncand = 0: no candidates).
 // COMPACT: the weight comes as the compact pack's ql (Q) and qh (QH) planes
 // instead of the expanded int8 quants; per 32-block the 6-bit codes 0..63
-// are rebuilt in registers, dotted as int8, and 32 x sum(x quants) of each
-// 16-value half (sx) is subtracted, which gives the expanded kernel's
-// integer exactly.
+// are rebuilt in registers and dotted as int8 into accumulators that start
+// at -32 x sum(x quants) of their 16-value half (sx), which gives the
+// expanded kernel's integer exactly.
 template <int R, bool COMPACT>
 __global__ __launch_bounds__(TOP1_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void
 q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ QH,
@@ -263,19 +263,15 @@ q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ QH,
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
                     const int *xb = reinterpret_cast<const int *>(xs + (bl * R + i) * QK);
-                    int sa = dot4(w[0], xb[0], 0);
+                    // codes 0..63 stand for q + 32
+                    int sa = dot4(w[0], xb[0], COMPACT ? xsum[(bl * R + i) * 2] : 0);
                     sa = dot4(w[1], xb[1], sa);
                     sa = dot4(w[2], xb[2], sa);
                     sa = dot4(w[3], xb[3], sa);
-                    int sbv = dot4(w[4], xb[4], 0);
+                    int sbv = dot4(w[4], xb[4], COMPACT ? xsum[(bl * R + i) * 2 + 1] : 0);
                     sbv = dot4(w[5], xb[5], sbv);
                     sbv = dot4(w[6], xb[6], sbv);
                     sbv = dot4(w[7], xb[7], sbv);
-                    if constexpr (COMPACT) {
-                        // codes 0..63 stand for q + 32
-                        sa -= xsum[(bl * R + i) * 2];
-                        sbv -= xsum[(bl * R + i) * 2 + 1];
-                    }
                     // |sa|, |sbv| <= 16 * 32 * 127 < 2^23: exact 24-bit products
                     const int I = __mul24(sa, sca) + __mul24(sbv, scb);
                     accsb[i] = fmaf((float)I, ds[bl * R + i], accsb[i]);
