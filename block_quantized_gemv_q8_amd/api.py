@@ -268,18 +268,21 @@ def q6k_pack_compact(raw: torch.Tensor, N: int, K: int, pack: torch.Tensor | Non
 
 def q6k_lmhead_candidate_max(pack: torch.Tensor, N: int, K: int, x: torch.Tensor, row0: int,
                              rows: int, cand_ids: torch.Tensor | None = None,
-                             scratch: torch.Tensor | None = None, compact: bool = False):
+                             scratch: torch.Tensor | None = None, compact: bool = False,
+                             ids: torch.Tensor | None = None, vals: torch.Tensor | None = None,
+                             scores: torch.Tensor | None = None):
     """(ids int32 [rows], top_vals f32 [rows], cand_scores f32 [rows][ncand]) of
-    rows row0.. of x through the pack; cand_ids int32 [rows][ncand] (or None)."""
+    rows row0.. of x through the pack; cand_ids int32 [rows][ncand] (or None).
+    ids, vals, scores may be given (preallocated outputs)."""
     M = x.shape[0]
     if x.shape[1] != K:
         raise ValueError("x must be [M][K]")
     ncand = 0 if cand_ids is None else cand_ids.shape[1]
     if cand_ids is not None and cand_ids.shape[0] != rows:
         raise ValueError("cand_ids must be [rows][ncand]")
-    ids = torch.empty((rows,), dtype=torch.int32, device=x.device)
-    vals = torch.empty((rows,), dtype=torch.float32, device=x.device)
-    scores = torch.empty((rows, ncand), dtype=torch.float32, device=x.device)
+    ids = _out(ids, (rows,), torch.int32, x.device, "ids")
+    vals = _out(vals, (rows,), torch.float32, x.device, "vals")
+    scores = _out(scores, (rows, ncand), torch.float32, x.device, "scores")
     need = q6k_lmhead_top1_scratch_bytes(N, K, rows)
     if scratch is None:
         scratch = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)

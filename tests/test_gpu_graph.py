@@ -86,23 +86,35 @@ def test_graph_of_packed_stream_and_top1():
     ids = torch.empty((5,), dtype=torch.int32, device=DEV)
     scratch = torch.empty((bq.q6k_lmhead_top1_scratch_bytes(Nv, Kv, 5),), dtype=torch.uint8,
                           device=DEV)
+    # candidate-max on the compact pack, all six rows, two candidates each
+    cpk = bq.q6k_pack_compact(raw, Nv, Kv)
+    cand = torch.tensor([[r, 2999 - r] for r in range(6)], dtype=torch.int32, device=DEV)
+    cids = torch.empty((6,), dtype=torch.int32, device=DEV)
+    cvals = torch.empty((6,), dtype=torch.float32, device=DEV)
+    cscores = torch.empty((6, 2), dtype=torch.float32, device=DEV)
+    scratch6 = torch.empty((bq.q6k_lmhead_top1_scratch_bytes(Nv, Kv, 6),), dtype=torch.uint8,
+                           device=DEV)
 
     def work_fn():
         bq.q4_0_ffn_stream(wg, wu, wd, x0, 1e-6, y=y, work=work, packed=True, ffn=F)
         bq.q6k_lmhead_top1(pack, Nv, Kv, xv, 1, 5, ids, scratch)
+        bq.q6k_lmhead_candidate_max(cpk, Nv, Kv, xv, 0, 6, cand, scratch6, compact=True,
+                                    ids=cids, vals=cvals, scores=cscores)
 
+    outs = (y, ids, cids, cvals, cscores)
     work_fn()
     torch.cuda.synchronize()
-    y_ref, ids_ref = y.clone(), ids.clone()
+    refs = [t.clone() for t in outs]
     g = _capture(work_fn)
     for rep in range(3):
         say(f"graph replay {rep}")
-        y.fill_(float("nan"))
-        ids.fill_(-7)
+        for t in outs:
+            t.fill_(-7)
         scratch.fill_(0xEE)                # the scratch's contents on entry must not matter
+        scratch6.fill_(0xEE)
         bq.q8_1_quantize(torch.randn((4, 256), device=DEV))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(y, y_ref)
-        assert torch.equal(ids, ids_ref)
+        for t, r in zip(outs, refs):
+            assert torch.equal(t, r)
