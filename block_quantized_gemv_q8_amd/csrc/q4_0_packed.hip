@@ -20,7 +20,12 @@
 //
 // The product is the one of q4_0_mmvq.hip (block-diagonal int8 MFMA, exact
 // per-block integer dots, d_w * d_x scaling and binary32 accumulation in a
-// fixed order); only where the operands come from differs.
+// fixed order); only where the operands come from differs.  Three launches
+// share its main loop (pk_accumulate): the product (q4_0_mmvq_packed), the
+// same product with K cut into ranges written as partial sums
+// (q4_0_mmvq_packed_split, for shapes with few row tiles), and the joint
+// gate/up launch with the SiLU*up + Q8_1 epilogue
+// (q4_0_gate_up_silu_q8_1_packed).
 #include "bq8_dev.h"
 
 namespace bq8 {

@@ -1,4 +1,5 @@
-// Q6_K expansion and the fused Q6_K LM-head projection with greedy top-1.
+// Q6_K expansion, the compact Q6_K pack, and the fused Q6_K LM-head
+// projection with greedy top-1 (and its candidate-max outputs) on either.
 //
 // "Q6_K M=6 fused DFlash top-1 production record":
 //   "Why this was slow" -- the Q6_K output tensor is expanded once into signed
@@ -37,6 +38,17 @@
 // an L2 write-back on this multi-XCD part and doubled the kernel time.  No
 // logit ever reaches memory, and max over integers makes the result
 // independent of scheduling.
+//
+// Candidate-max: the lane that computes a candidate's vocabulary row stores
+// that logit; the final kernel also decodes the winning key back to its
+// logit.  "Qwen3.6 27B AutoRound Handoff", "Current next-execution plan":
+// target-verified speculation needs the top ids and values and per-row
+// candidate scores.
+//
+// Compact pack (include/bq8.h): the raw Q6_K bytes re-tiled like the
+// expanded planes (ql, qh, subscales, scales); the same kernel rebuilds the
+// 6-bit codes in registers and gives bitwise the expanded pack's logits.
+// "Memory and startup": the expanded pack is kept beside the raw weights.
 #include "bq8_dev.h"
 
 namespace bq8 {
