@@ -59,10 +59,18 @@ def q4_0_bytes(N, K):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments dropped and whitespace
+    collapsed, so that a counter record stays valid across comment edits and
+    lapses with any change to the code itself."""
+    import re
+
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
