@@ -113,6 +113,38 @@ def test_mmvq_packed_equal_rows_and_guard_bytes():
     assert (yy[:, 100] == yy[:, 5]).all() and (yy[:, 149] == yy[:, 5]).all()
 
 
+# Wide shapes with a ragged last tile (256 to 512 tiles, one to two per CU):
+# every M class against the oracle, equal weight rows anywhere give bitwise
+# equal outputs, nothing is written past y, and a split into one range is the
+# whole product bit for bit.
+WIDE_SHAPES = [(4097, 1024), (4111, 512), (8191, 2560), (6000, 5120), (4100, 1536)]
+
+
+@pytest.mark.parametrize("N,K", WIDE_SHAPES)
+def test_mmvq_packed_wide_ragged(N, K):
+    w, x = synth.random_q4_0_case(3500 + N + K, N, K, 17)
+    copies = [15, 16, 17, 33, 34, 35, N // 2, N - 2, N - 1]
+    for r in copies:
+        w[r] = w[0]                   # equal rows in other tiles, at tile edges
+    xq = oracle.q8_1_quantize(x)
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
+    wp = bq.q4_0_pack(dev(w))
+    xqd = dev(xq)
+    for m in (1, 2, 3, 6, 8, 9, 16, 17):
+        say(f"q4_0_mmvq_packed wide ragged M={m} N={N} K={K}")
+        buf = torch.full((m * N + 64,), 12345.0, dtype=torch.float32, device=DEV)
+        y = buf[:m * N].view(m, N)
+        bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m, y)
+        b = host(buf)
+        assert (b[m * N:] == 12345.0).all()
+        yy = b[:m * N].reshape(m, N)
+        assert_close(yy, ref[:m], bound[:m], f"wide ragged m{m} N{N} K{K}")
+        for r in copies:
+            assert np.array_equal(yy[:, r].view(np.uint32), yy[:, 0].view(np.uint32)), r
+        one = host(bq.q4_0_mmvq_packed_split(wp, N, K, xqd[:m], m, 1))
+        assert np.array_equal(one[0].view(np.uint32), yy.view(np.uint32))
+
+
 def part_sum(parts):
     """Sum of partial rows in part order, in binary32 (the documented order)."""
     y = parts[0].copy()
