@@ -167,10 +167,7 @@ __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restr
     const float v = valid ? x[(size_t)blk * QK + j] : 0.0f;
     float d;
     const int q = q8_1_block_quant(v, d);
-    int hs = q; // sum over the lane's 16-value half
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1)
-        hs += __shfl_xor(hs, off, 16);
+    const int hs = row16_sum(q); // sum over the lane's 16-value half
     if (valid) {
         const int r = blk / nb, b = blk - r * nb;
         xq8[((size_t)b * R + r) * QK + j] = (int8_t)q;
