@@ -107,6 +107,52 @@ def time_calls(torch, fn, reps, warm=10):
     return t.ms * 1000.0 / reps
 
 
+def time_batches(torch, fn, per_batch, batches=10, warm=10):
+    """µs per call of fn(i) over `batches` batches of per_batch back-to-back
+    calls, each batch bracketed by its own HIP events (call indices run on
+    across batches, so rotating weights keep rotating): median, p10 and p90
+    of the batch means."""
+    for i in range(warm):
+        fn(i)
+    us = []
+    k = 0
+    for _ in range(batches):
+        with Timer(torch) as t:
+            for _ in range(per_batch):
+                fn(k)
+                k += 1
+        us.append(t.ms * 1000.0 / per_batch)
+    return {"median": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+            "p90": float(np.percentile(us, 90)), "batches": batches, "calls_per_batch": per_batch}
+
+
+def stats_us(st, nd=3):
+    return {"us_median": round(st["median"], nd), "us_p10": round(st["p10"], nd),
+            "us_p90": round(st["p90"], nd)}
+
+
+def hbm_probe(torch, bq, bufs, per_batch, batches=5):
+    """The read-only probe over the same buffers a kernel streams (rotating
+    through them like the kernel's calls): the fastest of a small sweep of
+    launch shapes, as µs per buffer read."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    best = None
+    for per_cu in (4, 8, 16):
+        wgs = cus * per_cu
+        out = torch.empty((4 * wgs,), dtype=torch.int32, device="cuda")
+        for unroll in (2, 4, 8):
+            st = time_batches(torch, lambda i: bq.hbm_read_probe(bufs[i % len(bufs)], wgs, unroll,
+                                                                 out), per_batch, batches)
+            if best is None or st["median"] < best[0]["median"]:
+                best = (st, {"workgroups": wgs, "threads_per_workgroup": 256, "unroll": unroll})
+    st, shape = best
+    return {"bytes_per_read": nbytes, **stats_us(st),
+            "GBps": round(nbytes / st["median"] / 1e3, 1),
+            "pct_hbm_peak": round(100 * nbytes / st["median"] / 1e3 / HBM_PEAK_GBS, 2),
+            "launch": shape, "buffers_rotated": len(bufs)}
+
+
 def capture(torch, fn, n):
     """A HIP graph of the calls fn(0) .. fn(n-1), captured on torch's capture
     stream (every library call enqueues on torch's current stream).  fn(0)
@@ -200,11 +246,11 @@ def time_down_sweep(torch, bq, synth, reps):
         xm = xq[:m]
         y = torch.empty((m, N), dtype=torch.float32, device="cuda")
         yp = torch.empty((P, m, N), dtype=torch.float32, device="cuda")
-        usp = time_calls(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % ROTATE], N, K, xm, m, y),
-                         reps)
-        uss = time_calls(torch, lambda i: bq.q4_0_mmvq_packed_split(wps[i % ROTATE], N, K, xm, m,
-                                                                    P, yp), reps)
-        us = time_calls(torch, lambda i: f(ws[i % ROTATE], xm, y), reps)
+        usp = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % ROTATE], N, K, xm, m, y),
+                           reps // 5, 5)["median"]
+        uss = time_batches(torch, lambda i: bq.q4_0_mmvq_packed_split(
+            wps[i % ROTATE], N, K, xm, m, P, yp), reps // 5, 5)["median"]
+        us = time_batches(torch, lambda i: f(ws[i % ROTATE], xm, y), reps // 5, 5)["median"]
         out[str(m)] = {"packed_us": round(usp, 3), "packed_GBps": round(wb / usp / 1e3, 1),
                        "packed_split_us": round(uss, 3),
                        "packed_split_GBps": round(wb / uss / 1e3, 1),
@@ -255,6 +301,73 @@ def time_stream(torch, bq, synth, passes, packed):
             "graph_GBps": round(wbytes / gmed / 1e6, 1)}
 
 
+SHARDS = 8
+ROTATE_BYTES = 600_000_000  # weight bytes in rotation: over twice the 256 MB last-level cache
+
+
+def time_shards(torch, bq, synth, per_batch=100):
+    """One GPU's share of the path under 8-way sharding, at its real shape:
+    the gate/up column shard (N = 17408/8 = 2176 of K = 5120: a plain packed
+    product and the joint gate/up launch), the down row shard (K = 17408/8 =
+    2176 of N = 5120, on the GGUF block layout: 2176 is not a multiple of
+    512, the packed layout's K granule) and the LM head's vocabulary shard
+    (248320/8 = 31040 rows, rows 1..5 projected, both packs).  Enough weight
+    copies rotate that every call reads its weight from HBM."""
+    M = 6
+    rng = np.random.default_rng(synth.FFN_UP["seed"])
+    K = synth.FFN_UP["K"]
+    Ns = synth.FFN_UP["N"] // SHARDS
+    sb = q4_0_bytes(Ns, K)
+    n = -(-ROTATE_BYTES // sb)
+    wps = [bq.q4_0_pack(synth.q4_0_weights_device(1000 + i, Ns, K)) for i in range(n)]
+    xq = bq.q8_1_quantize(torch.from_numpy(synth.normal_rows(rng, M, K)).to("cuda"))
+    y = torch.empty((M, Ns), dtype=torch.float32, device="cuda")
+    hq = torch.empty((M, Ns // 32 * 36), dtype=torch.uint8, device="cuda")
+    prod = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % n], Ns, K, xq, M, y),
+                        per_batch)
+    joint = time_batches(torch, lambda i: bq.q4_0_gate_up_silu_q8_1_packed(
+        wps[i % n], wps[(i + n // 2) % n], Ns, K, xq, M, hq), per_batch)
+    del wps
+    Nd, Kd = synth.DOWN_SWEEP["N"], synth.DOWN_SWEEP["K"] // SHARDS
+    db = q4_0_bytes(Nd, Kd)
+    nd = -(-ROTATE_BYTES // db)
+    wd = [synth.q4_0_weights_device(2000 + i, Nd, Kd) for i in range(nd)]
+    xqd = bq.q8_1_quantize(torch.from_numpy(synth.normal_rows(rng, M, Kd, 0.5)).to("cuda"))
+    yd = torch.empty((M, Nd), dtype=torch.float32, device="cuda")
+    down = time_batches(torch, lambda i: bq.q4_0_mmvq_m6(wd[i % nd], xqd, yd), per_batch)
+    del wd
+    Nv = synth.LM_HEAD["N"] // SHARDS
+    raws = [synth.q6k_raw_weights_device(3000 + i, Nv, K) for i in range(5)]
+    cpks = [bq.q6k_pack_compact(r, Nv, K) for r in raws]
+    packs = [bq.q6k_pack_expand(r, Nv, K) for r in raws]
+    del raws
+    x6 = torch.from_numpy(synth.normal_rows(rng, M, K)).to("cuda")
+    ids = torch.empty((5,), dtype=torch.int32, device="cuda")
+    scratch = torch.empty((bq.q6k_lmhead_top1_scratch_bytes(Nv, K, 5),), dtype=torch.uint8,
+                          device="cuda")
+    lmc = time_batches(torch, lambda i: bq.q6k_lmhead_top1(cpks[i % 5], Nv, K, x6, 1, 5, ids,
+                                                           scratch, compact=True), 20)
+    lme = time_batches(torch, lambda i: bq.q6k_lmhead_top1(packs[i % 5], Nv, K, x6, 1, 5, ids,
+                                                           scratch), 20)
+    cb, eb = cpks[0].numel(), packs[0].numel()
+    del cpks, packs
+
+    def line(st, nbytes, **kw):
+        return {**kw, "weight_bytes": nbytes, **stats_us(st),
+                "GBps": round(nbytes / st["median"] / 1e3, 1)}
+
+    return {"ways": SHARDS,
+            "gate_up_column_shard": {
+                "packed_product": line(prod, sb, N=Ns, K=K, M=M),
+                "joint_gate_up_silu_q8_1": line(joint, 2 * sb, N=Ns, K=K, M=M),
+                "copies_rotated": n},
+            "down_row_shard": {**line(down, db, N=Nd, K=Kd, M=M, layout="gguf (q4_0_mmvq_m6)"),
+                               "copies_rotated": nd},
+            "lm_head_vocab_shard": {
+                "N": Nv, "K": K, "rows": "1..5",
+                "compact": line(lmc, cb), "expanded": line(lme, eb), "copies_rotated": 5}}
+
+
 def cpu_baseline(synth, budget_s=10.0):
     """The oracle, as written, on the full ffn_up workload, repeated for
     about budget_s seconds of wall time on the host's cores."""
@@ -277,6 +390,40 @@ def cpu_baseline(synth, budget_s=10.0):
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} full ffn_up projections (Q8_1 quantize of [6][5120] + Q4_0 GEMV "
                       f"[17408x5120], M=6) in {el:.1f} s"}
+
+
+def cpu_one_thread(synth, budget_s=5.0):
+    """The same oracle sample on one host thread (the oracle's results do not
+    depend on its thread count)."""
+    import oracle
+
+    cfg = synth.FFN_UP
+    N, K, M = cfg["N"], cfg["K"], cfg["M"]
+    w, x = synth.ffn_up()
+    full = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            xq = oracle.q8_1_quantize(x)
+            oracle.q4_0_gemv(w, N, K, xq, M)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s and n >= 2:
+                break
+    finally:
+        oracle.set_num_threads(full)
+    return {"GBps": round(n * q4_0_bytes(N, K) / el / 1e9, 4), "threads": 1,
+            "ms_per_projection": round(1000 * el / n, 1), "projections": n}
+
+
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2**30, 1), "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None)}
 
 
 def pmc_traffic(record=PMC_RECORD):
@@ -378,18 +525,27 @@ def main():
     graph_step_us = t.ms * 1000.0 / args.steps
     log(f"bench: step as a replayed graph {graph_step_us:.3f} us")
     del g
+    step_b = time_batches(torch, lambda i: step_packed(bq, s, i), args.steps, 10)
     bq.q8_1_quantize(s["x"], s["xq"])
     reps = max(args.steps, 100)
-    packed_us = time_calls(torch, lambda i: bq.q4_0_mmvq_packed(
-        s["wps"][i % ROTATE], N, K, s["xq"], M, s["y"]), reps, warm=20)
+    # the roofline kernel: the median of 10 batch means, each batch 100
+    # back-to-back launches rotating the 12 weight copies
+    packed_b = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(
+        s["wps"][i % ROTATE], N, K, s["xq"], M, s["y"]), 100, 10, warm=20)
+    packed_us = packed_b["median"]
     achieved = wbytes / packed_us / 1e3
-    log(f"bench: q4_0_mmvq_packed M=6 {packed_us:.3f} us, {achieved:.1f} GB/s")
+    log(f"bench: q4_0_mmvq_packed M=6 {packed_us:.3f} us (p10 {packed_b['p10']:.3f}, p90 "
+        f"{packed_b['p90']:.3f}), {achieved:.1f} GB/s")
+    probe_ffn = hbm_probe(torch, bq, s["wps"], 100)
+    log(f"bench: HBM read probe over the same 12 packed copies {probe_ffn['us_median']:.3f} us, "
+        f"{probe_ffn['GBps']} GB/s ({probe_ffn['launch']})")
     std_us = time_calls(torch, lambda i: bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"]),
                         reps, warm=20)
     std_step_us = time_calls(torch, lambda i: step_standard(bq, s, i), reps, warm=20)
     log(f"bench: q4_0_mmvq_m6 (GGUF layout) {std_us:.3f} us; step {std_step_us:.3f} us")
     quant_us = time_calls(torch, lambda i: bq.q8_1_quantize(s["x"], s["xq"]), reps, warm=20)
-    joint_us = time_calls(torch, lambda i: gate_up_joint(bq, s, i), reps, warm=20)
+    joint_b = time_batches(torch, lambda i: gate_up_joint(bq, s, i), reps // 10, 10, warm=20)
+    joint_us = joint_b["median"]
     sep_us = time_calls(torch, lambda i: gate_up_separate(bq, s, i), reps, warm=20)
     sep_gguf_us = time_calls(torch, lambda i: gate_up_separate_gguf(bq, s, i), reps, warm=20)
     log(f"bench: gate/up + SiLU*up + Q8_1: joint {joint_us:.3f} us, separate {sep_us:.3f} us, "
@@ -398,7 +554,8 @@ def main():
 
     log("bench: lm_head setup")
     lm = setup_lm_head(torch, bq, synth)
-    lm_us = time_calls(torch, lambda i: lm_head_call(bq, lm), 50, warm=5)
+    lm_b = time_batches(torch, lambda i: lm_head_call(bq, lm), 10, 10, warm=5)
+    lm_us = lm_b["median"]
     pack_bytes = lm["pack"].numel()
     log(f"bench: lmhead_top1 {lm_us:.2f} us, {pack_bytes / lm_us / 1e3:.1f} GB/s")
     # head variants: all six target-side rows, and candidate-max (one drafted
@@ -414,17 +571,25 @@ def main():
     log(f"bench: lmhead rows 0..5 {lm6_us:.2f} us; candidate-max rows 1..5 {cm_us:.2f} us")
     # the compact pack (raw Q6_K bits re-tiled) of the same weights
     cpk = bq.q6k_pack_compact(lm["raw"], lm["N"], lm["K"])
-    lmc_us = time_calls(torch, lambda i: bq.q6k_lmhead_top1(
+    lmc_b = time_batches(torch, lambda i: bq.q6k_lmhead_top1(
         cpk, lm["N"], lm["K"], lm["x"], lm["row0"], lm["rows"], lm["ids"], lm["scratch"],
-        compact=True), 50, warm=5)
+        compact=True), 10, 10, warm=5)
+    lmc_us = lmc_b["median"]
     cpk_bytes = cpk.numel()
     log(f"bench: lmhead_top1 compact {lmc_us:.2f} us, {cpk_bytes / lmc_us / 1e3:.1f} GB/s")
+    probe_lm = hbm_probe(torch, bq, [cpk], 10)
+    log(f"bench: HBM read probe over the compact pack {probe_lm['us_median']:.2f} us, "
+        f"{probe_lm['GBps']} GB/s")
     del cpk
     del lm
 
     log("bench: down_sweep")
     sweep = time_down_sweep(torch, bq, synth, 100)
     log(f"bench: sweep {sweep}")
+
+    log("bench: 8-way shard shapes")
+    shards = time_shards(torch, bq, synth)
+    log(f"bench: shards {shards}")
 
     log("bench: stream (packed)")
     stream_p = time_stream(torch, bq, synth, 20, packed=True)
@@ -433,10 +598,11 @@ def main():
     stream_s = time_stream(torch, bq, synth, 10, packed=False)
     log(f"bench: stream gguf {stream_s['ms_median']:.3f} ms per pass")
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         cpu = cpu_baseline(synth)
+        cpu1 = cpu_one_thread(synth)
 
     traffic = pmc_traffic()
     out = {
@@ -459,8 +625,12 @@ def main():
             "N": N, "K": K, "M": M,
             "weight_bytes": wbytes,
             "step_us": round(step_us, 3),
+            "step_us_batches": stats_us(step_b),
             "step_graph_replay_us": round(graph_step_us, 3),
             "packed_mmvq_us": round(packed_us, 3),
+            "packed_mmvq_us_batches": stats_us(packed_b),
+            "hbm_read_probe": probe_ffn,
+            "pct_of_probe_mmvq": round(100 * probe_ffn["us_median"] / packed_us, 2),
             "quantize_us": round(quant_us, 3),
             "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
             "pct_hbm_peak_mmvq": round(100 * achieved / HBM_PEAK_GBS, 2),
@@ -469,6 +639,7 @@ def main():
                             "step_us": round(std_step_us, 3)},
             "gate_up_silu_q8_1": {
                 "joint_us": round(joint_us, 3),
+                "joint_us_batches": stats_us(joint_b),
                 "joint_GBps": round(2 * wbytes / joint_us / 1e3, 1),
                 "separate_packed_us": round(sep_us, 3),
                 "separate_gguf_us": round(sep_gguf_us, 3),
@@ -479,18 +650,25 @@ def main():
                         "to Q8_1: one joint launch vs two packed products + silu_mul_q8_1"},
             "lmhead_top1_us": round(min(lm_us, lmc_us), 2),
             "lmhead_top1_expanded_pack_us": round(lm_us, 2),
+            "lmhead_top1_expanded_pack_us_batches": stats_us(lm_b, 2),
             "lmhead_target_rows_0_5_us": round(lm6_us, 2),
-            "lmhead_top1_compact": {"us": round(lmc_us, 2), "pack_bytes": cpk_bytes,
-                                    "GBps": round(cpk_bytes / lmc_us / 1e3, 1)},
+            "lmhead_top1_compact": {"us": round(lmc_us, 2), **stats_us(lmc_b, 2),
+                                    "pack_bytes": cpk_bytes,
+                                    "GBps": round(cpk_bytes / lmc_us / 1e3, 1),
+                                    "hbm_read_probe": probe_lm,
+                                    "pct_of_probe": round(100 * probe_lm["us_median"] / lmc_us,
+                                                          2)},
             "lmhead_candidate_max_rows_1_5_us": round(cm_us, 2),
             "lmhead_expanded_pack_bytes": pack_bytes,
             "lmhead_expanded_GBps": round(pack_bytes / lm_us / 1e3, 1),
             "lmhead_expanded_pct_hbm_peak": round(100 * pack_bytes / lm_us / 1e3 / HBM_PEAK_GBS,
                                                   2),
             "down_sweep": sweep,
+            "shards_8_way": shards,
             "stream_64_layer_pass": stream_p,
             "stream_64_layer_pass_gguf_layout": stream_s,
-            "device": torch.cuda.get_device_name(0),
+            "device": device_info(torch),
+            "cpu_oracle_one_thread": cpu1,
         },
         "roofline": {
             "bound": "hbm",

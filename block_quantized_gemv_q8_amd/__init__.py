@@ -15,6 +15,7 @@ _API_NAMES = {
     "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed", "q4_0_gate_up_silu_q8_1_packed",
     "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "rms_norm_q8_1_sum",
     "q4_0_ffn_stream_layout", "q4_0_ffn_stream", "stream_weight_table", "stream_stages",
+    "hbm_read_probe",
 }
 
 

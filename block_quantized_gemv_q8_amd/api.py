@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.q4_0_gate_up_silu_q8_1_packed.restype = _ST
         L.q4_0_gate_up_silu_q8_1_packed.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P,
                                                     _P, _P]
+        L.bq8_hbm_read_probe.restype = _ST
+        L.bq8_hbm_read_probe.argtypes = [_P, _I64, _I64, _I64, _P, _P]
         L.q4_0_ffn_stream_layout.restype = _ST
         L.q4_0_ffn_stream_layout.argtypes = [_I64, _I64, _I64, ctypes.POINTER(_I64)]
         for f in (L.q4_0_ffn_stream, L.q4_0_ffn_stream_packed):
@@ -474,3 +476,15 @@ __all__ = ["Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "
            "q4_0_mmvq_packed", "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits",
            "q4_0_gate_up_silu_q8_1_packed", "q4_0_ffn_stream_layout", "q4_0_ffn_stream",
            "stream_weight_table", "stream_stages", "synth"]
+
+
+def hbm_read_probe(buf: torch.Tensor, workgroups: int, unroll: int,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """Read every byte of buf (a contiguous device tensor, a multiple of 16
+    bytes) once with 16-byte loads; returns the per-wave XOR words (uint32
+    [4 * workgroups] as int32), the only thing written."""
+    out = _out(out, (4 * workgroups,), torch.int32, buf.device, "out")
+    _check("bq8_hbm_read_probe", lib().bq8_hbm_read_probe(
+        _dev(buf, "buf"), buf.numel() * buf.element_size(), workgroups, unroll,
+        _dev(out, "out", torch.int32), _stream()))
+    return out

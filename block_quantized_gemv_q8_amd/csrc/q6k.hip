@@ -27,7 +27,11 @@
 // multiplies); the result, widened to binary32, is scaled by the row's d_x
 // into a per-superblock sum, and d_w scales that sum once per superblock.
 // The order of operations is the same for every row, so equal weight rows
-// give bitwise equal logits.  Each lane keeps, per activation row, a 64-bit
+// give bitwise equal logits.  Narrow vocabularies (under 2048 tiles, such as
+// one GPU's 31040-row shard) have too few tiles to fill the CUs one wave per
+// tile; there the waves of a workgroup share a tile, each summing one range
+// of its superblocks, and the range sums are added in range order in LDS.
+// Each lane keeps, per activation row, a 64-bit
 // key
 //     (order-preserving bits of the logit) << 32 | (0xFFFFFFFF - id)
 // whose maximum is the largest logit with the lowest id among ties.  Keys
@@ -122,6 +126,7 @@ constexpr int TOP1_THREADS = 256;
 constexpr int TOP1_WAVES = TOP1_THREADS / WAVE;
 constexpr int TOP1_MAX_GRID = 1024;
 constexpr int TOP1_MAX_ROWS = 8;
+constexpr int TOP1_SPLIT_MAX_WAVES = 16;
 
 __device__ __forceinline__ uint64_t make_key(float v, uint32_t id)
 {
@@ -178,10 +183,165 @@ __global__ __launch_bounds__(256) void q6k_top1_prep_kernel(const float *__restr
     }
 }
 
-// cand / ncand / scores: per activation row i, the logits of vocabulary rows
-// cand[i*ncand + c] (c < ncand) are written to scores[i*ncand + c] by the
-// one lane that computes them -- the same binary32 values the keys are made
-// of (ncand = 0: no candidates).
+// The logits of this lane's weight row of the 64-row tile at n0 (the last
+// row repeated in a ragged tile) over superblocks sb0 .. sb1 - 1 (sb1 >
+// sb0), for the R activation rows: acc[i] = sum over those superblocks of
+// d_w * (sum of the 16-value sub-block dots times their subscales), added
+// superblock by superblock in order.
+template <int R, bool COMPACT>
+__device__ __forceinline__ void q6k_tile_logits(const int8_t *__restrict__ Q,
+                                                const int8_t *__restrict__ QH,
+                                                const int8_t *__restrict__ SC,
+                                                const uint16_t *__restrict__ D, int N, int K,
+                                                int n0, int sb0, int sb1,
+                                                const int8_t *__restrict__ xq8,
+                                                const float *__restrict__ dx,
+                                                const int32_t *__restrict__ sx, float (&acc)[R])
+{
+    const int lane = threadIdx.x & 63;
+    const int nsb = K / QK_K;
+    const int rows_t = (N - n0 < PACK_TILE) ? N - n0 : PACK_TILE;
+    const int r = lane < rows_t ? lane : rows_t - 1; // ragged tile: repeat the last row
+    const int8_t *qt = Q + (size_t)n0 * (COMPACT ? K / 2 : K);
+    const int8_t *ht = COMPACT ? QH + (size_t)n0 * (K / 4) : nullptr;
+    const int8_t *st = SC + (size_t)n0 * (K / 16);
+    const uint16_t *dt = D + (size_t)n0 * nsb;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        acc[i] = 0.0f;
+
+    // expanded: pieces 16 sb + 8 half .. +7 of this lane's row (128
+    // quants); compact: ql pieces 8 sb + 4 half .. +3 in v[0..3], qh
+    // pieces 4 sb + 2 half .. +1 in v[4..5]
+    auto load_half = [&](u32x4(&v)[8], int sb, int half) {
+        if constexpr (COMPACT) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    qt + ((size_t)(sb * 8 + half * 4 + j) * rows_t + r) * 16));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                v[4 + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    ht + ((size_t)(sb * 4 + half * 2 + j) * rows_t + r) * 16));
+        } else {
+            const int c0 = sb * 16 + half * 8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    qt + ((size_t)(c0 + j) * rows_t + r) * 16));
+        }
+    };
+    // 32-blocks 4 half .. 4 half + 3 of the superblock, every activation row
+    auto compute_half = [&](const u32x4(&v)[8], int half, const u32x4 &scw,
+                            const int8_t *xs, const float *ds, const int32_t *xsum,
+                            float(&accsb)[R]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int bl = half * 4 + j;
+            const uint32_t scword = scw[bl >> 1];
+            const int sca = __builtin_amdgcn_sbfe(scword, 16 * (bl & 1), 8);
+            const int scb = __builtin_amdgcn_sbfe(scword, 16 * (bl & 1) + 8, 8);
+            // the block's 32 weights as 8 words of 4 signed bytes
+            int w[8];
+            if constexpr (COMPACT) {
+                // code of value l (0..31) of block 4 half + j: low (j < 2)
+                // or high nibble of ql byte 32 (j & 1) + l of the half,
+                // bits 2j..2j+1 of its qh byte l
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t qlw = v[2 * (j & 1) + (k >> 2)][k & 3];
+                    const uint32_t qhw = v[4 + (k >> 2)][k & 3];
+                    const uint32_t lo = ((j < 2) ? qlw : (qlw >> 4)) & 0x0F0F0F0Fu;
+                    w[k] = (int)(lo | (((qhw >> (2 * j)) & 0x03030303u) << 4));
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    w[k] = (int)v[2 * j + (k >> 2)][k & 3];
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const int *xb = reinterpret_cast<const int *>(xs + (bl * R + i) * QK);
+                // codes 0..63 stand for q + 32
+                int sa = dot4(w[0], xb[0], COMPACT ? xsum[(bl * R + i) * 2] : 0);
+                sa = dot4(w[1], xb[1], sa);
+                sa = dot4(w[2], xb[2], sa);
+                sa = dot4(w[3], xb[3], sa);
+                int sbv = dot4(w[4], xb[4], COMPACT ? xsum[(bl * R + i) * 2 + 1] : 0);
+                sbv = dot4(w[5], xb[5], sbv);
+                sbv = dot4(w[6], xb[6], sbv);
+                sbv = dot4(w[7], xb[7], sbv);
+                // |sa|, |sbv| <= 16 * 32 * 127 < 2^23: exact 24-bit products
+                const int I = __mul24(sa, sca) + __mul24(sbv, scb);
+                accsb[i] = fmaf((float)I, ds[bl * R + i], accsb[i]);
+            }
+        }
+    };
+
+    // Both halves of the next superblock are in flight while one is
+    // computed.  Loads are issued without branches (a wait-count join after
+    // a skipped load would make later waits conservative): after the last
+    // superblock of the range the prefetch repeats its addresses (cache
+    // hits, never used).
+    u32x4 va[8], vb[8];
+    load_half(va, sb0, 0);
+    load_half(vb, sb0, 1);
+    u32x4 scw = *reinterpret_cast<const u32x4 *>(st + ((size_t)sb0 * rows_t + r) * 16);
+    uint32_t dbits = dt[(size_t)sb0 * rows_t + r];
+    for (int sb = sb0; sb < sb1; ++sb) {
+        const int sbn = (sb + 1 < sb1) ? sb + 1 : sb;
+        const u32x4 scw_next =
+            *reinterpret_cast<const u32x4 *>(st + ((size_t)sbn * rows_t + r) * 16);
+        const uint32_t dbits_next = dt[(size_t)sbn * rows_t + r];
+        const int8_t *xs = xq8 + (size_t)sb * 8 * R * QK;
+        const float *ds = dx + (size_t)sb * 8 * R;
+        const int32_t *xsum = COMPACT ? sx + (size_t)sb * 8 * R * 2 : nullptr;
+        float accsb[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            accsb[i] = 0.0f;
+        compute_half(va, 0, scw, xs, ds, xsum, accsb);
+        load_half(va, sbn, 0);
+        compute_half(vb, 1, scw, xs, ds, xsum, accsb);
+        load_half(vb, sbn, 1);
+        const float dw = h2f(dbits);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            acc[i] = fmaf(accsb[i], dw, acc[i]);
+        scw = scw_next;
+        dbits = dbits_next;
+    }
+}
+
+// Folds the logits acc[i] of vocabulary row n_raw (< N) into the running
+// best keys of the R activation rows, and stores the candidate scores it
+// names: per activation row i, the logits of vocabulary rows cand[i*ncand +
+// c] (c < ncand) go to scores[i*ncand + c] from the one lane that computes
+// them -- the same binary32 values the keys are made of.
+template <int R>
+__device__ __forceinline__ void q6k_fold(const float (&acc)[R], int n_raw,
+                                         const int32_t *__restrict__ cand, int ncand,
+                                         float *__restrict__ scores, uint64_t (&best)[R])
+{
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const float v = acc[i];
+        if (!__builtin_isnan(v)) {
+            const uint64_t k = make_key(v, (uint32_t)n_raw);
+            best[i] = k > best[i] ? k : best[i];
+        }
+    }
+    for (int c = 0; c < ncand; ++c)
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            if (n_raw == cand[i * ncand + c])
+                scores[i * ncand + c] = acc[i];
+}
+
+// Greedy top-1 over the vocabulary, one wave per 64-row tile: lane l owns
+// weight row n0 + l and computes its logits over all of K, the wave keeps
+// the best key per activation row, and the workgroup's maximum goes to
+// slots[blockIdx.x][i] (cand / ncand / scores as in q6k_fold).
 // COMPACT: the weight comes as the compact pack's ql (Q) and qh (QH) planes
 // instead of the expanded int8 quants; per 32-block the 6-bit codes 0..63
 // are rebuilt in registers and dotted as int8 into accumulators that start
@@ -198,144 +358,18 @@ q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ QH,
     __shared__ uint64_t wave_best[TOP1_WAVES][R];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nsb = K / QK_K;
     const int ntiles = (N + PACK_TILE - 1) / PACK_TILE;
 
     uint64_t best[R];
 #pragma unroll
     for (int i = 0; i < R; ++i)
         best[i] = 0;
-
     for (int t = blockIdx.x * TOP1_WAVES + wave; t < ntiles; t += gridDim.x * TOP1_WAVES) {
         const int n0 = t * PACK_TILE;
-        const int rows_t = (N - n0 < PACK_TILE) ? N - n0 : PACK_TILE;
-        const int r = lane < rows_t ? lane : rows_t - 1; // ragged tile: repeat the last row
-        const int n_raw = n0 + lane;
-        const int8_t *qt = Q + (size_t)n0 * (COMPACT ? K / 2 : K);
-        const int8_t *ht = COMPACT ? QH + (size_t)n0 * (K / 4) : nullptr;
-        const int8_t *st = SC + (size_t)n0 * (K / 16);
-        const uint16_t *dt = D + (size_t)n0 * nsb;
         float acc[R];
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-            acc[i] = 0.0f;
-
-        // expanded: pieces 16 sb + 8 half .. +7 of this lane's row (128
-        // quants); compact: ql pieces 8 sb + 4 half .. +3 in v[0..3], qh
-        // pieces 4 sb + 2 half .. +1 in v[4..5]
-        auto load_half = [&](u32x4(&v)[8], int sb, int half) {
-            if constexpr (COMPACT) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                        qt + ((size_t)(sb * 8 + half * 4 + j) * rows_t + r) * 16));
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    v[4 + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                        ht + ((size_t)(sb * 4 + half * 2 + j) * rows_t + r) * 16));
-            } else {
-                const int c0 = sb * 16 + half * 8;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                        qt + ((size_t)(c0 + j) * rows_t + r) * 16));
-            }
-        };
-        // 32-blocks 4 half .. 4 half + 3 of the superblock, every activation row
-        auto compute_half = [&](const u32x4(&v)[8], int half, const u32x4 &scw,
-                                const int8_t *xs, const float *ds, const int32_t *xsum,
-                                float(&accsb)[R]) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int bl = half * 4 + j;
-                const uint32_t scword = scw[bl >> 1];
-                const int sca = __builtin_amdgcn_sbfe(scword, 16 * (bl & 1), 8);
-                const int scb = __builtin_amdgcn_sbfe(scword, 16 * (bl & 1) + 8, 8);
-                // the block's 32 weights as 8 words of 4 signed bytes
-                int w[8];
-                if constexpr (COMPACT) {
-                    // code of value l (0..31) of block 4 half + j: low (j < 2)
-                    // or high nibble of ql byte 32 (j & 1) + l of the half,
-                    // bits 2j..2j+1 of its qh byte l
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const uint32_t qlw = v[2 * (j & 1) + (k >> 2)][k & 3];
-                        const uint32_t qhw = v[4 + (k >> 2)][k & 3];
-                        const uint32_t lo = ((j < 2) ? qlw : (qlw >> 4)) & 0x0F0F0F0Fu;
-                        w[k] = (int)(lo | (((qhw >> (2 * j)) & 0x03030303u) << 4));
-                    }
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 8; ++k)
-                        w[k] = (int)v[2 * j + (k >> 2)][k & 3];
-                }
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const int *xb = reinterpret_cast<const int *>(xs + (bl * R + i) * QK);
-                    // codes 0..63 stand for q + 32
-                    int sa = dot4(w[0], xb[0], COMPACT ? xsum[(bl * R + i) * 2] : 0);
-                    sa = dot4(w[1], xb[1], sa);
-                    sa = dot4(w[2], xb[2], sa);
-                    sa = dot4(w[3], xb[3], sa);
-                    int sbv = dot4(w[4], xb[4], COMPACT ? xsum[(bl * R + i) * 2 + 1] : 0);
-                    sbv = dot4(w[5], xb[5], sbv);
-                    sbv = dot4(w[6], xb[6], sbv);
-                    sbv = dot4(w[7], xb[7], sbv);
-                    // |sa|, |sbv| <= 16 * 32 * 127 < 2^23: exact 24-bit products
-                    const int I = __mul24(sa, sca) + __mul24(sbv, scb);
-                    accsb[i] = fmaf((float)I, ds[bl * R + i], accsb[i]);
-                }
-            }
-        };
-
-        // Both halves of the next superblock are in flight while one is
-        // computed.  Loads are issued without branches (a wait-count join
-        // after a skipped load would make later waits conservative): after
-        // the last superblock the prefetch repeats its addresses (cache hits,
-        // never used).
-        u32x4 va[8], vb[8];
-        load_half(va, 0, 0);
-        load_half(vb, 0, 1);
-        u32x4 scw = *reinterpret_cast<const u32x4 *>(st + (size_t)r * 16);
-        uint32_t dbits = dt[r];
-        for (int sb = 0; sb < nsb; ++sb) {
-            const int sbn = (sb + 1 < nsb) ? sb + 1 : sb;
-            const u32x4 scw_next =
-                *reinterpret_cast<const u32x4 *>(st + ((size_t)sbn * rows_t + r) * 16);
-            const uint32_t dbits_next = dt[(size_t)sbn * rows_t + r];
-            const int8_t *xs = xq8 + (size_t)sb * 8 * R * QK;
-            const float *ds = dx + (size_t)sb * 8 * R;
-            const int32_t *xsum = COMPACT ? sx + (size_t)sb * 8 * R * 2 : nullptr;
-            float accsb[R];
-#pragma unroll
-            for (int i = 0; i < R; ++i)
-                accsb[i] = 0.0f;
-            compute_half(va, 0, scw, xs, ds, xsum, accsb);
-            load_half(va, sbn, 0);
-            compute_half(vb, 1, scw, xs, ds, xsum, accsb);
-            load_half(vb, sbn, 1);
-            const float dw = h2f(dbits);
-#pragma unroll
-            for (int i = 0; i < R; ++i)
-                acc[i] = fmaf(accsb[i], dw, acc[i]);
-            scw = scw_next;
-            dbits = dbits_next;
-        }
-        if (n_raw < N) {
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const float v = acc[i];
-                if (!__builtin_isnan(v)) {
-                    const uint64_t k = make_key(v, (uint32_t)n_raw);
-                    best[i] = k > best[i] ? k : best[i];
-                }
-            }
-            for (int c = 0; c < ncand; ++c)
-#pragma unroll
-                for (int i = 0; i < R; ++i)
-                    if (n_raw == cand[i * ncand + c])
-                        scores[i * ncand + c] = acc[i];
-        }
+        q6k_tile_logits<R, COMPACT>(Q, QH, SC, D, N, K, n0, 0, K / QK_K, xq8, dx, sx, acc);
+        if (n0 + lane < N)
+            q6k_fold(acc, n0 + lane, cand, ncand, scores, best);
     }
 
 #pragma unroll
@@ -351,6 +385,62 @@ q6k_top1_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ QH,
         for (int w = 0; w < TOP1_WAVES; ++w)
             k = wave_best[w][threadIdx.x] > k ? wave_best[w][threadIdx.x] : k;
         slots[(size_t)blockIdx.x * R + threadIdx.x] = k;
+    }
+}
+
+// The same top-1 with every tile's superblocks cut into S ranges, for
+// vocabularies too narrow to give each CU enough waves with whole tiles (a
+// 31040-row shard of the 248320-row head has 485 tiles).  The workgroup's S
+// waves share one tile at a time; wave w computes superblocks w*nsb/S ..
+// (w+1)*nsb/S - 1 (S <= nsb, so no range is empty), the S partial logits
+// are added in range order in LDS, and wave 0 folds the sums into its keys
+// and candidate scores.  slots[blockIdx.x][i] as in q6k_top1_kernel.
+template <int R, bool COMPACT>
+__global__ __launch_bounds__(TOP1_SPLIT_MAX_WAVES * WAVE) __attribute__((amdgpu_waves_per_eu(4)))
+void q6k_top1_split_kernel(const int8_t *__restrict__ Q, const int8_t *__restrict__ QH,
+                           const int8_t *__restrict__ SC, const uint16_t *__restrict__ D, int N,
+                           int K, const int8_t *__restrict__ xq8, const float *__restrict__ dx,
+                           const int32_t *__restrict__ sx, uint64_t *__restrict__ slots,
+                           const int32_t *__restrict__ cand, int ncand,
+                           float *__restrict__ scores)
+{
+    __shared__ float part[TOP1_SPLIT_MAX_WAVES][R][WAVE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+    const int nsb = K / QK_K;
+    const int ntiles = (N + PACK_TILE - 1) / PACK_TILE;
+    const int sb0 = wave * nsb / S, sb1 = (wave + 1) * nsb / S;
+
+    uint64_t best[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        best[i] = 0;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int n0 = t * PACK_TILE;
+        float acc[R];
+        q6k_tile_logits<R, COMPACT>(Q, QH, SC, D, N, K, n0, sb0, sb1, xq8, dx, sx, acc);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            part[wave][i][lane] = acc[i];
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                for (int w = 1; w < S; ++w)
+                    acc[i] += part[w][i][lane];
+            if (n0 + lane < N)
+                q6k_fold(acc, n0 + lane, cand, ncand, scores, best);
+        }
+        __syncthreads(); // part is rewritten by the next tile
+    }
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const uint64_t k = wave_max_u64(best[i]);
+            if (lane == 0)
+                slots[(size_t)blockIdx.x * R + i] = k;
+        }
     }
 }
 
@@ -400,10 +490,37 @@ __global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_final_kernel(
     }
 }
 
-static int64_t top1_grid(int64_t N)
+// Superblock ranges per tile: 1 (one wave per whole tile) when the
+// vocabulary has at least TOP1_SPLIT_BELOW tiles (the 248320-row head has
+// 3880), else the smallest divisor S of the superblock count (2 <= S <= 16)
+// that gives at least TOP1_SPLIT_WAVES waves, or the largest such divisor
+// (1 if there is none).  A 31040-row shard at K = 5120 takes S = 10.
+constexpr int64_t TOP1_SPLIT_BELOW = 2048;
+constexpr int64_t TOP1_SPLIT_WAVES = 4096;
+
+static int top1_splits(int64_t N, int64_t K)
+{
+    const int64_t tiles = (N + WAVE - 1) / WAVE, nsb = K / QK_K;
+    if (tiles >= TOP1_SPLIT_BELOW)
+        return 1;
+    int best = 1;
+    for (int d = 2; d <= TOP1_SPLIT_MAX_WAVES && d <= nsb; ++d) {
+        if (nsb % d != 0)
+            continue;
+        best = d;
+        if (tiles * d >= TOP1_SPLIT_WAVES)
+            break;
+    }
+    return best;
+}
+
+// Workgroups of the fused kernel (= key slots per activation row): one per
+// four tiles, or one per tile when the tiles are split, at most
+// TOP1_MAX_GRID.
+static int64_t top1_grid(int64_t N, int64_t K)
 {
     const int64_t tiles = (N + WAVE - 1) / WAVE;
-    int64_t g = (tiles + TOP1_WAVES - 1) / TOP1_WAVES;
+    int64_t g = top1_splits(N, K) > 1 ? tiles : (tiles + TOP1_WAVES - 1) / TOP1_WAVES;
     return g > TOP1_MAX_GRID ? TOP1_MAX_GRID : g;
 }
 
@@ -425,10 +542,14 @@ template <int R, bool COMPACT>
 static void launch_top1(const int8_t *Q, const int8_t *QH, const int8_t *SC, const uint16_t *D,
                         int N, int K, const int8_t *xq8, const float *dx, const int32_t *sx,
                         uint64_t *slots, int32_t *ids, float *vals, const int32_t *cand,
-                        int ncand, float *scores, int grid, hipStream_t s)
+                        int ncand, float *scores, int grid, int splits, hipStream_t s)
 {
-    hipLaunchKernelGGL((q6k_top1_kernel<R, COMPACT>), dim3(grid), dim3(TOP1_THREADS), 0, s, Q, QH,
-                       SC, D, N, K, xq8, dx, sx, slots, cand, ncand, scores);
+    if (splits > 1)
+        hipLaunchKernelGGL((q6k_top1_split_kernel<R, COMPACT>), dim3(grid), dim3(WAVE * splits),
+                           0, s, Q, QH, SC, D, N, K, xq8, dx, sx, slots, cand, ncand, scores);
+    else
+        hipLaunchKernelGGL((q6k_top1_kernel<R, COMPACT>), dim3(grid), dim3(TOP1_THREADS), 0, s, Q,
+                           QH, SC, D, N, K, xq8, dx, sx, slots, cand, ncand, scores);
     hipLaunchKernelGGL(q6k_top1_final_kernel<R>, dim3(1), dim3(TOP1_THREADS), 0, s, slots, grid,
                        ids, vals);
 }
@@ -437,13 +558,13 @@ template <bool COMPACT>
 static void launch_top1_rows(int rows, const int8_t *Q, const int8_t *QH, const int8_t *SC,
                              const uint16_t *D, int N, int K, const int8_t *xq8, const float *dx,
                              const int32_t *sx, uint64_t *slots, int32_t *ids, float *vals,
-                             const int32_t *cand, int ncand, float *scores, int grid,
+                             const int32_t *cand, int ncand, float *scores, int grid, int splits,
                              hipStream_t s)
 {
 #define BQ8_TOP1_CASE(r)                                                                           \
     case r:                                                                                        \
         launch_top1<r, COMPACT>(Q, QH, SC, D, N, K, xq8, dx, sx, slots, ids, vals, cand, ncand,    \
-                                scores, grid, s);                                                  \
+                                scores, grid, splits, s);                                          \
         break;
     switch (rows) {
         BQ8_TOP1_CASE(1)
@@ -480,7 +601,8 @@ static bq8_status lmhead_run(const void *pack, bool compact, int64_t N, int64_t 
         (uint64_t *)(base + xq8_area(K, rows) + dx_area(K, rows) + sx_area(K, rows));
     const int nb = (int)(K / QK);
     const int nblocks = (int)rows * nb;
-    const int grid = (int)top1_grid(N);
+    const int grid = (int)top1_grid(N, K);
+    const int splits = top1_splits(N, K);
     const int nc = (int)ncand;
     (void)hipGetLastError();
     hipLaunchKernelGGL(q6k_top1_prep_kernel, dim3((nblocks * 32 + 255) / 256), dim3(256), 0, s,
@@ -491,10 +613,10 @@ static bq8_status lmhead_run(const void *pack, bool compact, int64_t N, int64_t 
     const int n = (int)N, k = (int)K, r = (int)rows;
     if (compact)
         launch_top1_rows<true>(r, Q, QH, SC, D, n, k, xq8, dx, sx, slots, ids, vals, cand, nc,
-                               scores, grid, s);
+                               scores, grid, splits, s);
     else
         launch_top1_rows<false>(r, Q, QH, SC, D, n, k, xq8, dx, sx, slots, ids, vals, cand, nc,
-                                scores, grid, s);
+                                scores, grid, splits, s);
     return launch_status();
 }
 
@@ -579,7 +701,7 @@ BQ8_EXPORT int64_t q6k_lmhead_top1_scratch_bytes(int64_t N, int64_t K, int64_t r
     if (!top1_shape_ok(N, K) || rows < 1 || rows > TOP1_MAX_ROWS)
         return -1;
     return xq8_area(K, rows) + dx_area(K, rows) + sx_area(K, rows) +
-           top1_grid(N) * rows * (int64_t)sizeof(uint64_t);
+           top1_grid(N, K) * rows * (int64_t)sizeof(uint64_t);
 }
 
 BQ8_EXPORT bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, const float *x,

@@ -230,7 +230,10 @@ bq8_status q6k_pack_expand(const void *raw, int64_t N, int64_t K, void *pack, in
  *          sums and one key per workgroup and row); its contents on entry do
  *          not matter.  Three
  *          kernels run in stream order: quantize, fused projection + per-
- *          workgroup reduction, final reduction.
+ *          workgroup reduction, final reduction.  Below 2048 64-row tiles
+ *          (N < 131009) each tile's K is cut into ranges computed by the
+ *          waves of one workgroup and added in range order, so that narrow
+ *          vocabularies (a 31040-row shard) still fill the CUs.
  * Shape: 1 <= N < 2^31 - 1, K >= 256, K % 256 == 0, N*K < 2^40.
  * Tie rule: among equal maximal logits the lowest id wins; -0 equals +0.
  * Equal weight rows give bitwise equal logits, so planted duplicate rows
@@ -378,6 +381,24 @@ bq8_status q4_0_ffn_stream_packed(const void *const *w_gate, const void *const *
                                   const void *const *w_down, int64_t layers, int64_t M,
                                   int64_t hidden, int64_t ffn, const float *x0, float eps,
                                   float *y, void *work, int64_t work_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement: a read-only HBM probe.
+ *
+ * Not a step of the method: the streaming ceiling that the weight-streaming
+ * kernels are compared with, beside the 8 TB/s nominal peak of MI355X.
+ * Reads bytes of buf (device, 16-byte aligned, bytes a multiple of 16) once
+ * with 16-byte nontemporal loads, the way the products read their weights,
+ * on `workgroups` workgroups of 256 threads with `unroll` (1, 2, 4 or 8)
+ * loads in flight per thread, and writes one XOR of every 32-bit word read
+ * per wave: out (device, caller-owned) receives 4 * workgroups uint32 words.
+ * Asynchronous on stream; nothing else is written.
+ * Errors: null pointers -> NULL; bytes < 16 or not a multiple of 16,
+ *   workgroups outside 1..2^20, another unroll -> SHAPE; buf not 16-byte or
+ *   out not 4-byte aligned -> ALIGN.
+ * ---------------------------------------------------------------------- */
+bq8_status bq8_hbm_read_probe(const void *buf, int64_t bytes, int64_t workgroups, int64_t unroll,
+                              uint32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

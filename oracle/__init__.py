@@ -89,6 +89,7 @@ def _declare(L):
     L.orc_silu_mul.argtypes = [_P, _P, _I64, _P]
     L.orc_rms_norm.argtypes = [_P, _I64, _I64, ctypes.c_double, _P]
     L.orc_num_threads.restype = ctypes.c_int
+    L.orc_set_num_threads.argtypes = [ctypes.c_int]
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -314,6 +315,11 @@ def rms_norm(y, eps: float) -> np.ndarray:
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the loops over output rows (results do not change)."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ------------------------------------------------------------ comparators

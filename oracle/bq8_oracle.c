@@ -705,3 +705,15 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the loops over output rows; each row's sum stays in one
+ * thread in its fixed order, so results do not depend on it. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

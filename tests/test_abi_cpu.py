@@ -39,7 +39,8 @@ def test_header_declares_expected_entry_points():
               "q4_0_ffn_stream_packed", "q4_0_gate_up_silu_q8_1_packed",
               "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "rms_norm_q8_1_sum",
               "q6k_lmhead_candidate_max", "q6k_compact_bytes", "q6k_pack_compact",
-              "q6k_lmhead_top1_compact", "q6k_lmhead_candidate_max_compact"]:
+              "q6k_lmhead_top1_compact", "q6k_lmhead_candidate_max_compact",
+              "bq8_hbm_read_probe"]:
         assert n in names
 
 
@@ -337,3 +338,18 @@ def test_compact_q6k_validation(L):
     c = L.q6k_lmhead_candidate_max_compact
     assert c(A, 248320, 5120, A, 6, 1, 5, A, 2, A, None, A, A, need, None) == NULL
     assert c(A, 248320, 5120, A, 6, 1, 5, A, 9, A, A, A, A, need, None) == SHAPE
+
+
+def test_hbm_read_probe_validation(L):
+    P = 1 << 12                       # fake, aligned: never dereferenced
+    f = L.bq8_hbm_read_probe
+    assert f(None, 1024, 4, 4, P, None) == NULL
+    assert f(P, 1024, 4, 4, None, None) == NULL
+    assert f(P, 8, 4, 4, P, None) == SHAPE             # under 16 bytes
+    assert f(P, 1032, 4, 4, P, None) == SHAPE          # not a multiple of 16
+    assert f(P, 1024, 0, 4, P, None) == SHAPE          # no workgroup
+    assert f(P, 1024, (1 << 20) + 1, 4, P, None) == SHAPE
+    for u in (0, 3, 16):
+        assert f(P, 1024, 4, u, P, None) == SHAPE
+    assert f(P + 8, 1024, 4, 4, P, None) == ALIGN
+    assert f(P, 1024, 4, 4, P + 2, None) == ALIGN
