@@ -93,25 +93,14 @@ __device__ __forceinline__ int swizzle_xor16(int v)
 __device__ __forceinline__ float as_f(int v) { return __builtin_bit_cast(float, v); }
 __device__ __forceinline__ int as_i(float v) { return __builtin_bit_cast(int, v); }
 
-// max over each 32-lane group, for N independent values side by side
-template <int N>
-__device__ __forceinline__ void group32_max(float (&a)[N])
+// max over each 32-lane group
+__device__ __forceinline__ float group32_max(float a)
 {
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        a[i] = fmaxf(a[i], as_f(dpp_move<DPP_SWAP1>(as_i(a[i]))));
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        a[i] = fmaxf(a[i], as_f(dpp_move<DPP_SWAP2>(as_i(a[i]))));
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        a[i] = fmaxf(a[i], as_f(dpp_move<DPP_HALF_MIRROR>(as_i(a[i]))));
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        a[i] = fmaxf(a[i], as_f(dpp_move<DPP_MIRROR>(as_i(a[i]))));
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        a[i] = fmaxf(a[i], as_f(swizzle_xor16(as_i(a[i]))));
+    a = fmaxf(a, as_f(dpp_move<DPP_SWAP1>(as_i(a))));
+    a = fmaxf(a, as_f(dpp_move<DPP_SWAP2>(as_i(a))));
+    a = fmaxf(a, as_f(dpp_move<DPP_HALF_MIRROR>(as_i(a))));
+    a = fmaxf(a, as_f(dpp_move<DPP_MIRROR>(as_i(a))));
+    return fmaxf(a, as_f(swizzle_xor16(as_i(a))));
 }
 
 // integer sum over each row of 16 lanes
@@ -124,81 +113,45 @@ __device__ __forceinline__ int row16_sum(int s)
     return s;
 }
 
-// Quantize N 32-value Q8_1 blocks held by the 32 adjacent lanes of a group,
-// value v[i] of block i in this lane (lane32 = lane index within the group),
-// side by side.  Arithmetic in binary32: amax over the block, d = amax / 127
-// (correctly rounded division), q = x / d rounded half away from zero and
-// clamped to +-127 (d == 0 gives q = 0).  q[i] receives this lane's quant,
-// d[i] the binary32 scale (the block stores it rounded to fp16).
-template <int N>
-__device__ __forceinline__ void q8_1_blocks_quant(const float (&v)[N], float (&d)[N], int (&q)[N])
-{
-    float a[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        a[i] = fabsf(v[i]);
-    group32_max(a);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        d[i] = a[i] / 127.0f;
-        const bool live = d[i] != 0.0f;
-        int qi = (int)roundf(v[i] / (live ? d[i] : 1.0f));
-        qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
-        q[i] = live ? qi : 0;
-    }
-}
-
+// Quantize one 32-value Q8_1 block held one value per lane by 32 adjacent
+// lanes (lane32 = lane index within the group).  Arithmetic in binary32:
+// amax over the block, d = amax / 127 (correctly rounded division),
+// q = x / d rounded half away from zero and clamped to +-127 (d == 0 gives
+// q = 0).  Returns this lane's quant; `d` receives the binary32 scale (the
+// block stores it rounded to fp16).
 __device__ __forceinline__ int q8_1_block_quant(float v, float &d)
 {
-    const float vv[1] = {v};
-    float dd[1];
-    int q[1];
-    q8_1_blocks_quant(vv, dd, q);
-    d = dd[0];
-    return q[0];
+    const float a = group32_max(fabsf(v));
+    d = a / 127.0f;
+    int q = 0;
+    if (d != 0.0f) {
+        q = (int)roundf(v / d);
+        q = q > 127 ? 127 : (q < -127 ? -127 : q);
+    }
+    return q;
 }
 
-// The Q8_1 blocks of q8_1_blocks_quant: every lane writes its quant, lane 0
+// The Q8_1 block of q8_1_block_quant: every lane writes its quant, lane 0
 // of the group writes d and s = d * sum(q) (binary32 product, then fp16).
-// blk[i] points at block i's 36 output bytes; blocks with valid[i] false
-// are computed and not stored.
-template <int N>
-__device__ __forceinline__ void q8_1_blocks_store(const float (&v)[N], int lane32,
-                                                  const bool (&valid)[N], uint8_t *const (&blk)[N])
+// `blk` points at the block's 36 output bytes.
+__device__ __forceinline__ void q8_1_block_store(float v, int lane32, bool valid, uint8_t *blk)
 {
-    float d[N];
-    int q[N];
-    q8_1_blocks_quant(v, d, q);
-    int s[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        s[i] = row16_sum(q[i]);
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        s[i] += swizzle_xor16(s[i]);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        if (!valid[i])
-            continue;
-        blk[i][4 + lane32] = (uint8_t)(int8_t)q[i];
+    float d;
+    const int q = q8_1_block_quant(v, d);
+    int s = row16_sum(q);
+    s += swizzle_xor16(s);
+    if (valid) {
+        blk[4 + lane32] = (uint8_t)(int8_t)q;
         if (lane32 == 0) {
-            float sf = d[i] * (float)s[i];
+            float sf = d * (float)s;
             // s is the binary32 product rounded to fp16.  Without this
             // barrier the compiler turns multiply-then-convert into one
             // v_fma_mixlo_f16, which rounds the exact product to fp16 once
             // and differs from the twice-rounded value in rare ties.
             __asm__ volatile("" : "+v"(sf));
-            *reinterpret_cast<uint32_t *>(blk[i]) = f2h(d[i]) | (f2h(sf) << 16);
+            *reinterpret_cast<uint32_t *>(blk) = f2h(d) | (f2h(sf) << 16);
         }
     }
-}
-
-__device__ __forceinline__ void q8_1_block_store(float v, int lane32, bool valid, uint8_t *blk)
-{
-    const float vv[1] = {v};
-    const bool ok[1] = {valid};
-    uint8_t *const b[1] = {blk};
-    q8_1_blocks_store(vv, lane32, ok, b);
 }
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
