@@ -27,7 +27,7 @@
 // multiplies); the result, widened to binary32, is scaled by the row's d_x
 // into a per-superblock sum, and d_w scales that sum once per superblock.
 // The order of operations is the same for every row, so equal weight rows
-// give bitwise equal logits.  Narrow vocabularies (under 2048 tiles, such as
+// give bitwise equal logits.  Narrow vocabularies (under 3600 tiles, such as
 // one GPU's 31040-row shard) have too few tiles to fill the CUs one wave per
 // tile; there the waves of a workgroup share a tile, each summing one range
 // of its superblocks, and the range sums are added in range order in LDS.
@@ -492,10 +492,14 @@ __global__ __launch_bounds__(TOP1_THREADS) void q6k_top1_final_kernel(
 
 // Superblock ranges per tile: 1 (one wave per whole tile) when the
 // vocabulary has at least TOP1_SPLIT_BELOW tiles (the 248320-row head has
-// 3880), else the smallest divisor S of the superblock count (2 <= S <= 16)
-// that gives at least TOP1_SPLIT_WAVES waves, or the largest such divisor
-// (1 if there is none).  A 31040-row shard at K = 5120 takes S = 10.
-constexpr int64_t TOP1_SPLIT_BELOW = 2048;
+// 3880), else the smallest divisor S >= 4 of the superblock count (S <= 16)
+// that gives at least TOP1_SPLIT_WAVES waves, or the largest divisor up to
+// 16 (1 if there is none).  Measured at K = 5120 with rows 1..5 (µs per call,
+// expanded pack, unsplit -> split): 31040 rows 135 -> 46 (S = 10), 65536 rows
+// 146 -> 67, 131000 rows 162 -> 121, 229376 rows 211 -> 204 (S = 4); at
+// 248320 rows the unsplit kernel is faster (220 against 228 with S = 4).
+// Two ranges measured worse than four at every width.
+constexpr int64_t TOP1_SPLIT_BELOW = 3600;
 constexpr int64_t TOP1_SPLIT_WAVES = 4096;
 
 static int top1_splits(int64_t N, int64_t K)
@@ -508,7 +512,7 @@ static int top1_splits(int64_t N, int64_t K)
         if (nsb % d != 0)
             continue;
         best = d;
-        if (tiles * d >= TOP1_SPLIT_WAVES)
+        if (d >= 4 && tiles * d >= TOP1_SPLIT_WAVES)
             break;
     }
     return best;

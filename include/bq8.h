@@ -230,8 +230,8 @@ bq8_status q6k_pack_expand(const void *raw, int64_t N, int64_t K, void *pack, in
  *          sums and one key per workgroup and row); its contents on entry do
  *          not matter.  Three
  *          kernels run in stream order: quantize, fused projection + per-
- *          workgroup reduction, final reduction.  Below 2048 64-row tiles
- *          (N < 131009) each tile's K is cut into ranges computed by the
+ *          workgroup reduction, final reduction.  Below 3600 64-row tiles
+ *          (N < 230337) each tile's K is cut into ranges computed by the
  *          waves of one workgroup and added in range order, so that narrow
  *          vocabularies (a 31040-row shard) still fill the CUs.
  * Shape: 1 <= N < 2^31 - 1, K >= 256, K % 256 == 0, N*K < 2^40.

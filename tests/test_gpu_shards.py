@@ -14,7 +14,9 @@ Bars as everywhere: products within |gpu - oracle| <= 1e-5 * sum_b |t_b| +
 oracle's logit where two rows nearly tie; the joint launch's Q8_1 output
 bitwise equal to the standalone SiLU*up requant of its own g and u.
 
-Also the read-only HBM probe that bench.py reports as the streaming ceiling:
+Also the head at two wider vocabularies that split each tile's K into four
+ranges (one at more tiles than workgroups), and the read-only HBM probe that
+bench.py reports as the streaming ceiling:
 it reads every 32-bit word of its buffer exactly once, so the XOR of its
 outputs is the XOR of the buffer's words, for every launch shape.
 """
@@ -118,3 +120,29 @@ def test_hbm_read_probe_reads_every_word_once(nbytes):
         out = host(bq.hbm_read_probe(bd, wgs, unroll))
         assert out.shape == (4 * wgs,)
         assert np.bitwise_xor.reduce(out.view(np.uint32)) == want
+
+
+# Widths that split each tile's K into four ranges: 70001 rows (1094 tiles,
+# one per workgroup, a ragged last tile) and 200000 rows (3125 tiles, more
+# than the 1024 workgroups, so each workgroup walks several tiles).
+@pytest.mark.parametrize("N", [70001, 200000])
+def test_lm_head_split_widths(N):
+    K = synth.LM_HEAD["K"]
+    say(f"lm head N={N} K={K} rows 1..5 (four superblock ranges per tile)")
+    rng = np.random.default_rng(8500 + N % 1000)
+    raw = synth.q6k_raw_weights(rng, N, K)
+    x = synth.normal_rows(rng, 6, K)
+    raw[N - 1] = raw[3]               # equal rows: the lower id must win a tie
+    oid, logits, bound, _ = oracle.q6k_lmhead_top1(oracle.q6k_pack_expand(raw, N, K), N, K, x, 1, 5)
+    rawd, xd = dev(raw), dev(x)
+    ids_e = host(bq.q6k_lmhead_top1(bq.q6k_pack_expand(rawd, N, K), N, K, xd, 1, 5))
+    ids_c = host(bq.q6k_lmhead_top1(bq.q6k_pack_compact(rawd, N, K), N, K, xd, 1, 5,
+                                    compact=True))
+    say(f"ids gpu {list(ids_e)} oracle {list(oid)}")
+    assert (ids_c == ids_e).all()
+    assert (ids_e != N - 1).all()
+    for r, (g, o) in enumerate(zip(ids_e, oid)):
+        if g != o:
+            assert 0 <= g < N
+            gap = logits[r, o] - logits[r, g]
+            assert gap <= REL * (bound[r, o] + bound[r, g]) + 2 * ABS, (r, g, o, gap)
