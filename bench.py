@@ -1,6 +1,6 @@
 """Benchmark of the width-6 verifier projection on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 200]
+    python bench.py [--gpus 1] [--steps 2000] [--warmup 2000]
 
 A step is one verifier projection of the ffn_up workload: Q8_1 quantization
 of the six f32 activation rows [6][5120] followed by the Q4_0 x Q8_1
@@ -481,8 +481,8 @@ def profile_target(torch, bq, synth, target, reps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--profile-target", default=None)
     ap.add_argument("--reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
