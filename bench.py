@@ -418,6 +418,20 @@ def cpu_one_thread(synth, budget_s=5.0):
             "ms_per_projection": round(1000 * el / n, 1), "projections": n}
 
 
+def host_info():
+    """The host the oracle is timed on: CPU model and logical CPUs."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count()}
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
@@ -669,6 +683,7 @@ def main():
             "stream_64_layer_pass_gguf_layout": stream_s,
             "device": device_info(torch),
             "cpu_oracle_one_thread": cpu1,
+            "host": host_info(),
         },
         "roofline": {
             "bound": "hbm",
