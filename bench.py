@@ -27,7 +27,7 @@ oracle's CPU throughput on a bounded sample.
 
 Profiling helpers (one kernel family per process, for rocprofv3):
     python bench.py --profile-target \\
-        packed_m6|mmvq_m6|gate_up|lmhead_top1|lmhead_compact|down_sweep|stream|stream_packed|copy
+        packed_m6|mmvq_m6|gate_up|lmhead_top1|lmhead_compact|down_sweep|stream|stream_packed|copy|probe
         [--reps R]
 """
 from __future__ import annotations
@@ -464,6 +464,17 @@ def profile_target(torch, bq, synth, target, reps):
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copy: {reps} x {n} bytes")
+        return
+    if target == "probe":
+        # the read probe at the launch shape bench.py finds fastest over the 12
+        # packed ffn_up copies: 8 workgroups per CU, 8 loads in flight per thread
+        s = setup_ffn_up(torch, bq, synth)
+        wgs = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+        out = torch.empty((4 * wgs,), dtype=torch.int32, device="cuda")
+        for i in range(reps):
+            bq.hbm_read_probe(s["wps"][i % ROTATE], wgs, 8, out)
+        torch.cuda.synchronize()
+        log(f"probe: {reps} reads of {s['wps'][0].numel()} bytes")
         return
     if target in ("packed_m6", "mmvq_m6", "gate_up"):
         s = setup_ffn_up(torch, bq, synth)
