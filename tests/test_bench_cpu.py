@@ -1,0 +1,33 @@
+"""bench.py's contract on the host: more than one GPU is refused with a message
+before any GPU work, and the counter-record key ignores comments but not code."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    import bench
+
+    csrc = tmp_path / "block_quantized_gemv_q8_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    base = "int f(int a) { return a + 1; } // one\n/* two */\n"
+    for rel in bench.KERNEL_SOURCES:
+        (tmp_path / rel).write_text(base)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    for rel in bench.KERNEL_SOURCES:
+        (tmp_path / rel).write_text("int f(int a)  {\n  return a + 1;\n} // changed\n")
+    assert bench.kernel_source_hash() == h0
+    (tmp_path / bench.KERNEL_SOURCES[0]).write_text("int f(int a) { return a + 2; }\n")
+    assert bench.kernel_source_hash() != h0
