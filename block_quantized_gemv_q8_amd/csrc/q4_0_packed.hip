@@ -286,9 +286,13 @@ __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
             }
             __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));
             // no prefetch past the wave's last chunk: a repeated chunk would
-            // be fetched from HBM again (the weight loads are nontemporal)
+            // be fetched from HBM again (the weight loads are nontemporal).
+            // The loads go out at raised wave priority, so that other waves'
+            // compute on the SIMD does not hold them back.
+            __builtin_amdgcn_s_setprio(3);
             if (k + 1 < mine)
                 issue(c0 + wave + S * (k + 1), (k + 1) & 1, wn, dn);
+            __builtin_amdgcn_s_setprio(0);
             compute(k & 1, wc, dc);
         }
     }
