@@ -437,7 +437,7 @@ def device_info(torch):
     return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
             "compute_units": p.multi_processor_count,
             "memory_GiB": round(p.total_memory / 2**30, 1), "torch": torch.__version__,
-            "hip": getattr(torch.version, "hip", None)}
+            "hip": getattr(torch.version, "hip", None), "numpy": np.__version__}
 
 
 def pmc_traffic(record=PMC_RECORD):
