@@ -45,7 +45,8 @@ def assert_close(gpu, ref, bound, what):
                            f"{tuple(np.argwhere(bad)[0])}")
 
 
-SHAPES = [(16, 512), (37, 1024), (200, 512), (1000, 1536), (16390, 512), (33, 5120)]
+SHAPES = [(1, 512), (5, 1024), (16, 512), (37, 1024), (200, 512), (1000, 1536), (16390, 512),
+          (33, 5120)]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
