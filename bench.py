@@ -179,12 +179,15 @@ def setup_ffn_up(torch, bq, synth):
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     u = torch.empty((M, N), dtype=torch.float32, device="cuda")
     hq = torch.empty((M, N // 32 * 36), dtype=torch.uint8, device="cuda")
-    return dict(N=N, K=K, M=M, ws=ws, wps=wps, x=xd, xq=xq, y=y, u=u, hq=hq)
+    # the product's workspace: the CU-balanced launch (q4_0_mmvq_packed_ws)
+    pws = bq.q4_0_mmvq_packed_workspace()
+    return dict(N=N, K=K, M=M, ws=ws, wps=wps, pws=pws, x=xd, xq=xq, y=y, u=u, hq=hq)
 
 
 def step_packed(bq, s, i):
     bq.q8_1_quantize(s["x"], s["xq"])
-    bq.q4_0_mmvq_packed(s["wps"][i % ROTATE], s["N"], s["K"], s["xq"], s["M"], s["y"])
+    bq.q4_0_mmvq_packed(s["wps"][i % ROTATE], s["N"], s["K"], s["xq"], s["M"], s["y"],
+                        ws=s["pws"])
 
 
 def step_standard(bq, s, i):
@@ -200,8 +203,10 @@ def gate_up_joint(bq, s, i):
 
 
 def gate_up_separate(bq, s, i):
-    bq.q4_0_mmvq_packed(s["wps"][i % ROTATE], s["N"], s["K"], s["xq"], s["M"], s["y"])
-    bq.q4_0_mmvq_packed(s["wps"][(i + 6) % ROTATE], s["N"], s["K"], s["xq"], s["M"], s["u"])
+    bq.q4_0_mmvq_packed(s["wps"][i % ROTATE], s["N"], s["K"], s["xq"], s["M"], s["y"],
+                        ws=s["pws"])
+    bq.q4_0_mmvq_packed(s["wps"][(i + 6) % ROTATE], s["N"], s["K"], s["xq"], s["M"], s["u"],
+                        ws=s["pws"])
     bq.silu_mul_q8_1(s["y"], s["u"], s["hq"])
 
 
@@ -240,18 +245,23 @@ def time_down_sweep(torch, bq, synth, reps):
     xq = bq.q8_1_quantize(torch.from_numpy(x).to("cuda"))
     wb = q4_0_bytes(N, K)
     P = bq.q4_0_mmvq_packed_splits(N, K)
-    out = {"packed_split_ranges": P}
+    pw = bq.q4_0_mmvq_packed_workspace()
+    out = {"packed_split_ranges": P, "packed_launch": "q4_0_mmvq_packed_ws"}
     for m in cfg["Ms"]:
         f = getattr(bq, f"q4_0_mmvq_m{m}")
         xm = xq[:m]
         y = torch.empty((m, N), dtype=torch.float32, device="cuda")
         yp = torch.empty((P, m, N), dtype=torch.float32, device="cuda")
-        usp = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % ROTATE], N, K, xm, m, y),
+        usp = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % ROTATE], N, K, xm, m, y,
+                                                                ws=pw), reps // 5, 5)["median"]
+        # every tile whole (the launch without a workspace)
+        usw = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % ROTATE], N, K, xm, m, y),
                            reps // 5, 5)["median"]
         uss = time_batches(torch, lambda i: bq.q4_0_mmvq_packed_split(
             wps[i % ROTATE], N, K, xm, m, P, yp), reps // 5, 5)["median"]
         us = time_batches(torch, lambda i: f(ws[i % ROTATE], xm, y), reps // 5, 5)["median"]
         out[str(m)] = {"packed_us": round(usp, 3), "packed_GBps": round(wb / usp / 1e3, 1),
+                       "packed_whole_tiles_us": round(usw, 3),
                        "packed_split_us": round(uss, 3),
                        "packed_split_GBps": round(wb / uss / 1e3, 1),
                        "gguf_us": round(us, 3), "gguf_GBps": round(wb / us / 1e3, 1)}
@@ -323,7 +333,8 @@ def time_shards(torch, bq, synth, per_batch=100):
     xq = bq.q8_1_quantize(torch.from_numpy(synth.normal_rows(rng, M, K)).to("cuda"))
     y = torch.empty((M, Ns), dtype=torch.float32, device="cuda")
     hq = torch.empty((M, Ns // 32 * 36), dtype=torch.uint8, device="cuda")
-    prod = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % n], Ns, K, xq, M, y),
+    pw = bq.q4_0_mmvq_packed_workspace()
+    prod = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % n], Ns, K, xq, M, y, ws=pw),
                         per_batch)
     joint = time_batches(torch, lambda i: bq.q4_0_gate_up_silu_q8_1_packed(
         wps[i % n], wps[(i + n // 2) % n], Ns, K, xq, M, hq), per_batch)
@@ -553,10 +564,12 @@ def main():
     step_b = time_batches(torch, lambda i: step_packed(bq, s, i), args.steps, 10)
     bq.q8_1_quantize(s["x"], s["xq"])
     reps = max(args.steps, 100)
-    # the roofline kernel: the median of 10 batch means, each batch 100
-    # back-to-back launches rotating the 12 weight copies
+    # the roofline kernel: the median of 20 batch means, each batch 100
+    # back-to-back launches rotating the 12 weight copies, after 1000 untimed
+    # launches of the kernel alone (its first milliseconds after the step
+    # phase run a few percent slower than its steady state)
     packed_b = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(
-        s["wps"][i % ROTATE], N, K, s["xq"], M, s["y"]), 100, 10, warm=20)
+        s["wps"][i % ROTATE], N, K, s["xq"], M, s["y"], ws=s["pws"]), 100, 20, warm=1000)
     packed_us = packed_b["median"]
     achieved = wbytes / packed_us / 1e3
     log(f"bench: q4_0_mmvq_packed M=6 {packed_us:.3f} us (p10 {packed_b['p10']:.3f}, p90 "
@@ -651,6 +664,8 @@ def main():
             "weight_bytes": wbytes,
             "step_us": round(step_us, 3),
             "step_us_batches": stats_us(step_b),
+            "product_launch": "q4_0_mmvq_packed_ws; at M <= 8 it runs every 16-row tile "
+                              "whole (the q4_0_mmvq_packed launch)",
             "step_graph_replay_us": round(graph_step_us, 3),
             "packed_mmvq_us": round(packed_us, 3),
             "packed_mmvq_us_batches": stats_us(packed_b),

@@ -93,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.q4_0_pack.argtypes = [_P, _I64, _I64, _P, _I64, _P]
         L.q4_0_mmvq_packed.restype = _ST
         L.q4_0_mmvq_packed.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
+        L.q4_0_mmvq_packed_ws_bytes.restype = _I64
+        L.q4_0_mmvq_packed_ws_bytes.argtypes = []
+        L.q4_0_mmvq_packed_ws.restype = _ST
+        L.q4_0_mmvq_packed_ws.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _I64, _P]
         L.q4_0_mmvq_packed_split.restype = _ST
         L.q4_0_mmvq_packed_split.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _P, _P]
         L.q4_0_mmvq_packed_splits.restype = _I64
@@ -359,13 +363,40 @@ def q4_0_pack(w: torch.Tensor, wp: torch.Tensor | None = None) -> torch.Tensor:
 
 
 def q4_0_mmvq_packed(wp: torch.Tensor, N: int, K: int, xq: torch.Tensor, M: int,
-                     y: torch.Tensor | None = None) -> torch.Tensor:
-    """y f32 [M][N] = packed Q4_0 weight times the M Q8_1 rows of xq."""
+                     y: torch.Tensor | None = None, ws: torch.Tensor | None = None
+                     ) -> torch.Tensor:
+    """y f32 [M][N] = packed Q4_0 weight times the M Q8_1 rows of xq.  With a
+    workspace ws (from q4_0_mmvq_packed_workspace) the launch balances the
+    tiles over the CUs (q4_0_mmvq_packed_ws): the tiles past the last
+    multiple of the CU count are summed in K ranges, so their outputs differ
+    from the plain launch's in binary32 rounding only."""
     y = _out(y, (M, N), torch.float32, wp.device, "y")
-    _check("q4_0_mmvq_packed", lib().q4_0_mmvq_packed(
-        _dev(wp, "wp", torch.uint8), N, K, _dev(xq, "xq", torch.uint8), M,
-        _dev(y, "y", torch.float32), _stream()))
+    if ws is None:
+        _check("q4_0_mmvq_packed", lib().q4_0_mmvq_packed(
+            _dev(wp, "wp", torch.uint8), N, K, _dev(xq, "xq", torch.uint8), M,
+            _dev(y, "y", torch.float32), _stream()))
+    else:
+        _check("q4_0_mmvq_packed_ws", lib().q4_0_mmvq_packed_ws(
+            _dev(wp, "wp", torch.uint8), N, K, _dev(xq, "xq", torch.uint8), M,
+            _dev(y, "y", torch.float32), _dev(ws, "ws", torch.uint8), ws.numel(), _stream()))
     return y
+
+
+def q4_0_mmvq_packed_ws_bytes() -> int:
+    """Workspace bytes q4_0_mmvq_packed_ws needs on the current device."""
+    n = int(lib().q4_0_mmvq_packed_ws_bytes())
+    if n < 0:
+        raise Bq8Error("q4_0_mmvq_packed_ws_bytes", 5, "no current HIP device")
+    return n
+
+
+def q4_0_mmvq_packed_workspace(device=None) -> torch.Tensor:
+    """A zeroed workspace for q4_0_mmvq_packed_ws on device (the current one
+    by default).  One per stream: calls that overlap in time must not share
+    one."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    with torch.cuda.device(device):
+        return torch.zeros(q4_0_mmvq_packed_ws_bytes(), dtype=torch.uint8, device=device)
 
 
 def q4_0_mmvq_packed_splits(N: int, K: int) -> int:

@@ -115,9 +115,10 @@ struct PkShape {
 // rows_t rows; chunk c of tile i starts at tile[i] + c * chunk_stride bytes
 // and its scales at dtile[i] + (c/2) * dgroup_stride elements (+4 for odd
 // c).  The wave sums chunks c0 + wave, c0 + wave + S, ... below c0 + nc.  The activations are staged once per chunk and each A operand feeds NT
-// MFMAs.  ring is this wave's LDS (PkShape<M>::WAVE_LDS bytes).
-// acc[i][s][x] (lanes l < 32 after pk_pair_sum) is the sum for weight row
-// l%16 of tile i and activation row 8s + 4*(l/16) + x, 16x the exact value.
+// MFMAs.  ring is this wave's LDS (at least PkShape<M>::WAVE_LDS bytes).
+// acc[i][s][x] of lanes l and l + 32 are the two blocks' shares of the sum
+// for weight row l%16 of tile i and activation row 8s + 4*(l/16) + x, 16x
+// the exact value.
 template <int M, int NT>
 __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
                                               const uint16_t *const (&dtile)[NT], int rows_t,
@@ -298,76 +299,149 @@ __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
     }
 }
 
-// Adds the two blocks of each pair (lanes l and l + 32) into lanes l < 32,
-// then waits for every load of the wave (no DMA may still be writing the LDS
-// the caller reuses next).
-template <int NT, int MS>
-__device__ __forceinline__ void pk_pair_sum(float (&acc)[NT][MS][4])
+// LDS bytes per wave: its ring, which after the wave's last chunk holds its
+// sums -- float [NT][2][MS*4][32], half h = lane / 32 holding lane 32h + l's
+// sums, the two blocks of each pair.  Only the wave itself touches its ring,
+// and its last chunk's reads and copies are done before it writes there, so
+// no barrier is needed before the write.
+template <int M, int NT>
+constexpr int pk_wave_stride()
 {
+    constexpr int sums = NT * 2 * PkShape<M>::MS * 4 * 32 * 4;
+    return PkShape<M>::WAVE_LDS > sums ? PkShape<M>::WAVE_LDS : sums;
+}
+
+template <int NT, int MS>
+__device__ __forceinline__ void pk_store_partials(const float (&acc)[NT][MS][4], uint8_t *ring,
+                                                  int lane)
+{
+    constexpr int SLOTS = MS * 4;
+    float *p = reinterpret_cast<float *>(ring);
+    const int half = lane >> 5, l = lane & 31;
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
         for (int s = 0; s < MS; ++s)
 #pragma unroll
             for (int x = 0; x < 4; ++x)
-                acc[i][s][x] += __shfl_xor(acc[i][s][x], 32, 64);
-    __builtin_amdgcn_s_waitcnt(0);
+                p[((i * 2 + half) * SLOTS + s * 4 + x) * 32 + l] = acc[i][s][x];
+}
+
+// Wave v's sum for one (tile, slot, lane) with its pair added, lane l then
+// l + 32, as one value.
+template <int NT, int MS>
+__device__ __forceinline__ float pk_partial_sum(const uint8_t *smem, int stride, int v, int i,
+                                                int slot, int l)
+{
+    constexpr int SLOTS = MS * 4;
+    const float *p = reinterpret_cast<const float *>(smem + (size_t)v * stride) +
+                     (i * 2 * SLOTS + slot) * 32 + l;
+    return p[0] + p[SLOTS * 32];
 }
 
 // y[m][n] for one 16-row tile; the tile's S waves take its 8-block chunks
-// round-robin and their sums are added in wave order.  With nsplit > 1 the
-// chunks of each tile are cut into nsplit consecutive ranges (range p =
-// chunks p*nch/nsplit .. (p+1)*nch/nsplit - 1), workgroup p*tiles + t takes
-// range p of tile t, and its sums go to y + p*M*N.
+// round-robin and their sums are added in wave order.  Workgroup b works in
+// one of three ways:
+//   nsplit > 1: range p = b / tiles of tile b % tiles (chunks p*C/nsplit ..
+//     (p+1)*C/nsplit - 1 of the C = nb/8), its sums to y + p*M*N;
+//   b < whole: the whole tile b, its sums to y;
+//   otherwise (CU balance, nsplit = 1): range j % P of tile whole + j / P,
+//     j = b - whole, with the tile's chunks cut into P ranges as above.  The
+//     tiles past the last multiple of the CU count are cut this way so that
+//     every CU gets the same work.  Their workgroups come last: the whole
+//     tiles, the longer work, start first.  A cut range's sums go to
+//     ws_sum[j][SLOTS*32]; the workgroup then counts itself in
+//     ws_count[j / P], and the one that brings the count to P adds the P
+//     range sums in range order, writes y and sets the count back to 0 for
+//     the next call.
+// The range sums and the count are agent-scope atomic stores, loads and adds
+// (global_store / global_load with the device-scope bit, global_atomic_add),
+// coherent across the XCDs' L2 caches without an L2 write-back: each writer
+// waits for its stores to complete (vmcnt(0)) before it counts itself, and
+// the last workgroup issues its loads after its count has returned.
 template <int M>
-__global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(const uint8_t *__restrict__ QS,
-                                                                const uint16_t *__restrict__ D,
-                                                                int N, int nb, int nsplit,
-                                                                const uint8_t *__restrict__ xq,
-                                                                float *__restrict__ y)
+__global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
+    const uint8_t *__restrict__ QS, const uint16_t *__restrict__ D, int N, int nb, int nsplit,
+    int P, int whole, const uint8_t *__restrict__ xq, float *__restrict__ y,
+    float *__restrict__ ws_sum, uint32_t *__restrict__ ws_count)
 {
-    using SH = PkShape<M>;
-    constexpr int MS = SH::MS;
+    constexpr int MS = PkShape<M>::MS;
+    constexpr int SLOTS = MS * 4;
+    constexpr int STRIDE = pk_wave_stride<M, 1>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
     const int tiles = (N + PK_TILE - 1) / PK_TILE;
-    const int part = blockIdx.x / tiles;
-    const int n0 = (blockIdx.x - part * tiles) * PK_TILE;
-    const int rows_t = (N - n0 < PK_TILE) ? N - n0 : PK_TILE;
     const int nch = nb / PK_CB;
-    const int c0 = (int)((int64_t)part * nch / nsplit);
-    const int c1 = (int)((int64_t)(part + 1) * nch / nsplit);
-    y += (size_t)part * M * N;
+    int t, c0 = 0, c1 = nch, j = -1;
+    if (nsplit > 1) {
+        const int p = blockIdx.x / tiles;
+        t = blockIdx.x - p * tiles;
+        c0 = (int)((int64_t)p * nch / nsplit);
+        c1 = (int)((int64_t)(p + 1) * nch / nsplit);
+        y += (size_t)p * M * N;
+    } else if ((int)blockIdx.x < whole) {
+        t = blockIdx.x;
+    } else {
+        j = blockIdx.x - whole;
+        const int p = j % P;
+        t = whole + j / P;
+        c0 = (int)((int64_t)p * nch / P);
+        c1 = (int)((int64_t)(p + 1) * nch / P);
+    }
+    const int n0 = t * PK_TILE;
+    const int rows_t = (N - n0 < PK_TILE) ? N - n0 : PK_TILE;
     const uint8_t *tile[1] = {QS + (size_t)n0 * nb * 16};
     const uint16_t *dtile[1] = {D + (size_t)n0 * nb};
     float acc[1][MS][4];
     pk_accumulate<M, 1>(tile, dtile, rows_t, (size_t)8 * rows_t * 16, (size_t)2 * rows_t * 8, nb,
-                        c0, c1 - c0, xq, smem + (size_t)wave * SH::WAVE_LDS, acc);
-    pk_pair_sum(acc);
+                        c0, c1 - c0, xq, smem + (size_t)wave * STRIDE, acc);
+    pk_store_partials<1, MS>(acc, smem + (size_t)wave * STRIDE, lane);
     __syncthreads();
-    constexpr int SLOTS = MS * 4;
-    float *partial = reinterpret_cast<float *>(smem); // [S][SLOTS][32]
-    if (lane < 32) {
-#pragma unroll
-        for (int s = 0; s < MS; ++s)
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                partial[(wave * SLOTS + s * 4 + x) * 32 + lane] = acc[0][s][x];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x) {
+    // output (slot, l): activation row 8s + 4*(l/16) + x, weight row n0 + l%16
+    auto wave_sum = [&](int idx) {
         const int slot = idx >> 5, l = idx & 31;
-        const int s = slot >> 2, x = slot & 3;
-        const int m = 8 * s + 4 * (l >> 4) + x;
-        const int nn = n0 + (l & 15);
         float sacc = 0.0f;
         for (int v = 0; v < S; ++v)
-            sacc += partial[(v * SLOTS + slot) * 32 + l];
+            sacc += pk_partial_sum<1, MS>(smem, STRIDE, v, 0, slot, l);
+        return sacc;
+    };
+    auto store_y = [&](int idx, float sacc) {
+        const int slot = idx >> 5, l = idx & 31;
+        const int m = 8 * (slot >> 2) + 4 * (l >> 4) + (slot & 3);
+        const int nn = n0 + (l & 15);
         if (m < M && nn < N)
             y[(size_t)m * N + nn] = sacc * 0.0625f;
+    };
+    if (j < 0) {
+        for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x)
+            store_y(idx, wave_sum(idx));
+        return;
     }
+    float *rsum = ws_sum + (size_t)(j - j % P) * SLOTS * 32; // the tile's P range sums
+    for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x)
+        __hip_atomic_store(rsum + (size_t)(j % P) * SLOTS * 32 + idx, wave_sum(idx),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // the partial sums have been read: wave 0's first LDS word carries the verdict
+    int *last = reinterpret_cast<int *>(smem);
+    if (threadIdx.x == 0)
+        *last = __hip_atomic_fetch_add(ws_count + j / P, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1);
+    __syncthreads();
+    if (!*last)
+        return;
+    for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x) {
+        float sacc = 0.0f;
+        for (int p = 0; p < P; ++p)
+            sacc += __hip_atomic_load(rsum + (size_t)p * SLOTS * 32 + idx, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        store_y(idx, sacc);
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(ws_count + j / P, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Gate and up projections of one Q8_1 activation with the SiLU(gate) * up
@@ -389,8 +463,8 @@ __global__ __launch_bounds__(512) void q4_0_gate_up_packed_kernel(
     const uint8_t *__restrict__ xq, float *__restrict__ g, float *__restrict__ u,
     float *__restrict__ h, uint8_t *__restrict__ hq)
 {
-    using SH = PkShape<M>;
-    constexpr int MS = SH::MS;
+    constexpr int MS = PkShape<M>::MS;
+    constexpr int STRIDE = pk_wave_stride<M, 4>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -403,20 +477,8 @@ __global__ __launch_bounds__(512) void q4_0_gate_up_packed_kernel(
                                 DU + (size_t)n0 * nb, DU + (size_t)(n0 + PK_TILE) * nb};
     float acc[4][MS][4];
     pk_accumulate<M, 4>(tile, dtile, PK_TILE, (size_t)8 * PK_TILE * 16, (size_t)2 * PK_TILE * 8,
-                        nb, 0, nb / PK_CB, xq, smem + (size_t)wave * SH::WAVE_LDS, acc);
-    pk_pair_sum(acc);
-    __syncthreads();
-    constexpr int SLOTS = MS * 4;
-    float *partial = reinterpret_cast<float *>(smem); // [S][4][SLOTS][32]
-    if (lane < 32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int s = 0; s < MS; ++s)
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    partial[((wave * 4 + i) * SLOTS + s * 4 + x) * 32 + lane] = acc[i][s][x];
-    }
+                        nb, 0, nb / PK_CB, xq, smem + (size_t)wave * STRIDE, acc);
+    pk_store_partials<4, MS>(acc, smem + (size_t)wave * STRIDE, lane);
     __syncthreads();
     // one 32-lane group per activation row m: lane c is column n0 + c
     const int groups = blockDim.x >> 5;
@@ -430,8 +492,8 @@ __global__ __launch_bounds__(512) void q4_0_gate_up_packed_kernel(
         const int l = 16 * ((mc >> 2) & 1) + (c & 15);
         float sg = 0.0f, su = 0.0f;
         for (int v = 0; v < S; ++v) {
-            sg += partial[((v * 4 + half) * SLOTS + slot) * 32 + l];
-            su += partial[((v * 4 + 2 + half) * SLOTS + slot) * 32 + l];
+            sg += pk_partial_sum<4, MS>(smem, STRIDE, v, half, slot, l);
+            su += pk_partial_sum<4, MS>(smem, STRIDE, v, 2 + half, slot, l);
         }
         const float gv = sg * 0.0625f, uv = su * 0.0625f;
         const float hv = gv / (1.0f + expf(-gv)) * uv;
@@ -484,20 +546,68 @@ static int packed_waves(int64_t wgs, int64_t chunks, int M, int64_t wave_lds, in
     return (int)(s < 1 ? 1 : s);
 }
 
+// K ranges a CU-count remainder tile is cut into: four, never more than
+// the tile's C chunks.
+static int packed_parts(int64_t C)
+{
+    return (int)(C < 4 ? C : 4);
+}
+
+// Compute units of the current device (queried once per device).
+static int64_t device_cus()
+{
+    static int64_t cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return -1;
+    if (cached[dev] <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            return -1;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
+// Workspace of the balanced product: ws_count (one uint32 per remainder
+// tile, fewer than CUs of them) in the first pk_ws_count_bytes(cus) bytes,
+// then ws_sum, PK_WS_TILE_FLOATS floats per remainder tile (P * SLOTS * 32
+// at most: 4 ranges, 12 slots at M = 17).
+constexpr int64_t PK_WS_TILE_FLOATS = 4 * 12 * 32;
+static int64_t pk_ws_count_bytes(int64_t cus) { return (cus * 4 + 255) / 256 * 256; }
+static int64_t pk_ws_bytes(int64_t cus)
+{
+    return pk_ws_count_bytes(cus) + cus * PK_WS_TILE_FLOATS * (int64_t)sizeof(float);
+}
+
+// ws == NULL: every tile in one workgroup.  Else, for M >= 9, the tiles
+// beyond the last multiple of the CU count are cut into P K ranges each.
+// There the per-tile compute is large enough for the balance to pay (ffn_up
+// M = 17: 18.6 against 21.4 us; down M = 9 / 12 / 17: 16.0 / 16.8 / 22.0
+// against 18.5 / 19.9 / 27.2 us).  At M = 6 the ranges' meeting in the
+// workspace cost more than the balance saved (ffn_up: 11.42 against
+// 11.19 us uncut, 11.01 us for the cut launch with the meeting left out),
+// and at M = 1 the cut launch won on ffn_up but lost on down (11.95 against
+// 11.24 us).
 template <int M>
 static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const void *xq, int nsplit,
-                                float *y, hipStream_t stream)
+                                float *y, void *ws, int64_t cus, hipStream_t stream)
 {
-    using SH = PkShape<M>;
     const int nb = (int)(K / QK);
+    const int64_t C = nb / PK_CB;
     const int64_t tiles = (N + PK_TILE - 1) / PK_TILE;
+    const int P = packed_parts(C);
+    const int64_t wave_lds = pk_wave_stride<M, 1>();
     const int64_t limit = packed_lds_limit();
-    const int s = packed_waves(tiles * nsplit, nb / PK_CB / nsplit, M, SH::WAVE_LDS, limit);
-    const int64_t ring = (int64_t)s * SH::WAVE_LDS;
-    const int64_t partial = (int64_t)s * SH::MS * 4 * 32 * (int64_t)sizeof(float);
-    const int64_t lds = ring > partial ? ring : partial;
+    const int s = packed_waves(tiles * nsplit, C / nsplit, M, wave_lds, limit);
+    const int64_t lds = (int64_t)s * wave_lds;
     if (lds > limit)
         return BQ8_ERR_SHAPE;
+    int64_t whole = tiles;
+    if (ws && nsplit == 1 && M >= 9)
+        whole = tiles - tiles % cus;
+    const int64_t grid = nsplit > 1 ? tiles * nsplit : whole + (tiles - whole) * P;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute((const void *)q4_0_mmvq_packed_kernel<M>,
@@ -507,10 +617,14 @@ static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const v
     }
     const uint8_t *QS = wp;
     const uint16_t *D = reinterpret_cast<const uint16_t *>(wp + N * nb * 16);
+    uint32_t *ws_count = static_cast<uint32_t *>(ws);
+    float *ws_sum = ws ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
+                                                   pk_ws_count_bytes(cus))
+                       : nullptr;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((q4_0_mmvq_packed_kernel<M>), dim3((unsigned)(tiles * nsplit)),
-                       dim3(WAVE * s), (size_t)lds, stream, QS, D, (int)N, nb, nsplit,
-                       (const uint8_t *)xq, y);
+    hipLaunchKernelGGL((q4_0_mmvq_packed_kernel<M>), dim3((unsigned)grid), dim3(WAVE * s),
+                       (size_t)lds, stream, QS, D, (int)N, nb, nsplit, P, (int)whole,
+                       (const uint8_t *)xq, y, ws_sum, ws_count);
     return launch_status();
 }
 
@@ -536,14 +650,11 @@ static bq8_status gate_up_launch(const uint8_t *wg, const uint8_t *wu, int64_t N
                                  const void *xq, float *g, float *u, float *h, void *hq,
                                  hipStream_t stream)
 {
-    using SH = PkShape<M>;
     const int nb = (int)(K / QK);
     const int64_t groups = N / (2 * PK_TILE);
     const int64_t limit = packed_lds_limit();
-    const int s = gate_up_waves(groups, nb, M, SH::WAVE_LDS, limit);
-    const int64_t ring = (int64_t)s * SH::WAVE_LDS;
-    const int64_t partial = (int64_t)s * 4 * SH::MS * 4 * 32 * (int64_t)sizeof(float);
-    const int64_t lds = ring > partial ? ring : partial;
+    const int s = gate_up_waves(groups, nb, M, pk_wave_stride<M, 4>(), limit);
+    const int64_t lds = (int64_t)s * pk_wave_stride<M, 4>();
     if (lds > limit)
         return BQ8_ERR_SHAPE;
     static bool attr_set = false;
@@ -586,37 +697,46 @@ static int packed_default_splits(int64_t N, int64_t K)
 }
 
 static bq8_status packed_product(const void *wp, int64_t N, int64_t K, const void *xq, int64_t M,
-                                 int nsplit, float *y, void *stream)
+                                 int nsplit, float *y, void *ws, int64_t ws_bytes, void *stream)
 {
     if (!wp || !xq || !y)
         return BQ8_ERR_NULL;
+
     if (!packed_shape_ok(N, K) || M < 1 || M > 17 || M * K >= (int64_t(1) << 31) || nsplit < 1 ||
         nsplit > MAX_SPLIT || nsplit > K / QK / PK_CB ||
         (int64_t)nsplit * M * N >= (int64_t(1) << 40) ||
         (int64_t)nsplit * ((N + PK_TILE - 1) / PK_TILE) >= (int64_t(1) << 31))
         return BQ8_ERR_SHAPE;
-    if (!aligned(wp, 16) || !aligned(xq, 4) || !aligned(y, 4))
+    if (!aligned(wp, 16) || !aligned(xq, 4) || !aligned(y, 4) || !aligned(ws, 256))
         return BQ8_ERR_ALIGN;
+    int64_t cus = 0;
+    if (ws) {
+        cus = device_cus();
+        if (cus <= 0)
+            return BQ8_ERR_HIP;
+        if (ws_bytes < pk_ws_bytes(cus))
+            return BQ8_ERR_SIZE;
+    }
     const uint8_t *p = (const uint8_t *)wp;
     hipStream_t s = (hipStream_t)stream;
     switch (M) {
-    case 1: return packed_launch<1>(p, N, K, xq, nsplit, y, s);
-    case 2: return packed_launch<2>(p, N, K, xq, nsplit, y, s);
-    case 3: return packed_launch<3>(p, N, K, xq, nsplit, y, s);
-    case 4: return packed_launch<4>(p, N, K, xq, nsplit, y, s);
-    case 5: return packed_launch<5>(p, N, K, xq, nsplit, y, s);
-    case 6: return packed_launch<6>(p, N, K, xq, nsplit, y, s);
-    case 7: return packed_launch<7>(p, N, K, xq, nsplit, y, s);
-    case 8: return packed_launch<8>(p, N, K, xq, nsplit, y, s);
-    case 9: return packed_launch<9>(p, N, K, xq, nsplit, y, s);
-    case 10: return packed_launch<10>(p, N, K, xq, nsplit, y, s);
-    case 11: return packed_launch<11>(p, N, K, xq, nsplit, y, s);
-    case 12: return packed_launch<12>(p, N, K, xq, nsplit, y, s);
-    case 13: return packed_launch<13>(p, N, K, xq, nsplit, y, s);
-    case 14: return packed_launch<14>(p, N, K, xq, nsplit, y, s);
-    case 15: return packed_launch<15>(p, N, K, xq, nsplit, y, s);
-    case 16: return packed_launch<16>(p, N, K, xq, nsplit, y, s);
-    default: return packed_launch<17>(p, N, K, xq, nsplit, y, s);
+    case 1: return packed_launch<1>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 2: return packed_launch<2>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 3: return packed_launch<3>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 4: return packed_launch<4>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 5: return packed_launch<5>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 6: return packed_launch<6>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 7: return packed_launch<7>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 8: return packed_launch<8>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 9: return packed_launch<9>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 10: return packed_launch<10>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 11: return packed_launch<11>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 12: return packed_launch<12>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 13: return packed_launch<13>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 14: return packed_launch<14>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 15: return packed_launch<15>(p, N, K, xq, nsplit, y, ws, cus, s);
+    case 16: return packed_launch<16>(p, N, K, xq, nsplit, y, ws, cus, s);
+    default: return packed_launch<17>(p, N, K, xq, nsplit, y, ws, cus, s);
     }
 }
 
@@ -655,7 +775,22 @@ BQ8_EXPORT bq8_status q4_0_pack(const void *w, int64_t N, int64_t K, void *wp, i
 BQ8_EXPORT bq8_status q4_0_mmvq_packed(const void *wp, int64_t N, int64_t K, const void *xq,
                                        int64_t M, float *y, void *stream)
 {
-    return packed_product(wp, N, K, xq, M, 1, y, stream);
+    return packed_product(wp, N, K, xq, M, 1, y, nullptr, 0, stream);
+}
+
+BQ8_EXPORT int64_t q4_0_mmvq_packed_ws_bytes(void)
+{
+    const int64_t cus = device_cus();
+    return cus > 0 ? pk_ws_bytes(cus) : -1;
+}
+
+BQ8_EXPORT bq8_status q4_0_mmvq_packed_ws(const void *wp, int64_t N, int64_t K, const void *xq,
+                                          int64_t M, float *y, void *ws, int64_t ws_bytes,
+                                          void *stream)
+{
+    if (!ws)
+        return BQ8_ERR_NULL;
+    return packed_product(wp, N, K, xq, M, 1, y, ws, ws_bytes, stream);
 }
 
 BQ8_EXPORT int64_t q4_0_mmvq_packed_splits(int64_t N, int64_t K)
@@ -671,7 +806,7 @@ BQ8_EXPORT bq8_status q4_0_mmvq_packed_split(const void *wp, int64_t N, int64_t 
 {
     if (nsplit < 1 || nsplit > MAX_SPLIT)
         return BQ8_ERR_SHAPE;
-    return packed_product(wp, N, K, xq, M, (int)nsplit, ypart, stream);
+    return packed_product(wp, N, K, xq, M, (int)nsplit, ypart, nullptr, 0, stream);
 }
 
 BQ8_EXPORT bq8_status q4_0_gate_up_silu_q8_1_packed(const void *wg, const void *wu, int64_t N,

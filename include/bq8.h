@@ -151,14 +151,35 @@ bq8_status q4_0_mmvq(const void *w, int64_t N, int64_t K, const void *xq, int64_
  *   load time.
  * q4_0_mmvq_packed: y[m][n] = sum_k W[n][k] X[m][k] as q4_0_mmvq_m<M>, for
  *   M = 1..17, from the packed weight; xq, y as there.  Results equal the
- *   standard-layout entry points up to the binary32 summation order.
+ *   standard-layout entry points up to the binary32 summation order, which
+ *   is fixed: results are reproducible bit for bit, and equal weight rows
+ *   give bitwise equal outputs.
+ * q4_0_mmvq_packed_ws: the same product, launched so that every CU gets the
+ *   same work where that pays (M >= 9; for M <= 8 it is q4_0_mmvq_packed,
+ *   bit for bit): each 16-row tile past the largest
+ *   multiple of the CU count is cut into P = min(4, K/256) ranges of K
+ *   (range p = chunks
+ *   floor(p*C/P) .. floor((p+1)*C/P) - 1 of the C = K/256 chunks of 8
+ *   blocks), computed by separate workgroups whose range sums meet in the
+ *   workspace and are added in range order.  Outputs of those tiles equal
+ *   q4_0_mmvq_packed's up to the binary32 summation order, the others bit
+ *   for bit; results are reproducible bit for bit.
+ *   ws: device memory, 256-byte aligned, ws_bytes >= q4_0_mmvq_packed_ws_bytes();
+ *   caller-owned.  Zero-fill it once before its first use: every call that
+ *   completes leaves it ready for the next (its counters back at zero).
+ *   Calls that overlap in time (e.g. on different streams) must not share
+ *   a workspace.  ws NULL -> BQ8_ERR_NULL, ws_bytes too small ->
+ *   BQ8_ERR_SIZE, ws misaligned -> BQ8_ERR_ALIGN.
+ * q4_0_mmvq_packed_ws_bytes: host; the workspace q4_0_mmvq_packed_ws needs
+ *   on the current device (about 6 KB per CU), or -1 without a device.
  * q4_0_mmvq_packed_split: the same product with K cut into nsplit ranges of
  *   8-block chunks (range p = chunks floor(p*C/nsplit) .. floor((p+1)*C/
  *   nsplit) - 1 of the C = K/256 chunks), each computed by its own
  *   workgroups, so that a shape with few 16-row tiles still fills every CU.
  *   ypart: f32 [nsplit][M][N], 4-byte aligned; ypart[p] holds range p's
  *   sums, and y = ypart[0] + ypart[1] + ... in that order (binary32; see
- *   rms_norm_q8_1_sum).  1 <= nsplit <= 8, nsplit <= K/256.
+ *   rms_norm_q8_1_sum).  nsplit = 1 gives q4_0_mmvq_packed's bits.
+ *   1 <= nsplit <= 8, nsplit <= K/256.
  * q4_0_mmvq_packed_splits: host; the nsplit the packed stream uses for an
  *   [N][K] projection (enough ranges for at least 1024 workgroups, at most
  *   8), or -1 if the shape is invalid.  1 for [17408 x 5120], 4 for
@@ -170,6 +191,9 @@ bq8_status q4_0_pack(const void *w, int64_t N, int64_t K, void *wp, int64_t wp_b
                      void *stream);
 bq8_status q4_0_mmvq_packed(const void *wp, int64_t N, int64_t K, const void *xq, int64_t M,
                             float *y, void *stream);
+bq8_status q4_0_mmvq_packed_ws(const void *wp, int64_t N, int64_t K, const void *xq, int64_t M,
+                               float *y, void *ws, int64_t ws_bytes, void *stream);
+int64_t q4_0_mmvq_packed_ws_bytes(void);
 bq8_status q4_0_mmvq_packed_split(const void *wp, int64_t N, int64_t K, const void *xq,
                                   int64_t M, int64_t nsplit, float *ypart, void *stream);
 int64_t q4_0_mmvq_packed_splits(int64_t N, int64_t K);

@@ -40,7 +40,7 @@ def test_header_declares_expected_entry_points():
               "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "rms_norm_q8_1_sum",
               "q6k_lmhead_candidate_max", "q6k_compact_bytes", "q6k_pack_compact",
               "q6k_lmhead_top1_compact", "q6k_lmhead_candidate_max_compact",
-              "bq8_hbm_read_probe"]:
+              "bq8_hbm_read_probe", "q4_0_mmvq_packed_ws", "q4_0_mmvq_packed_ws_bytes"]:
         assert n in names
 
 
@@ -237,6 +237,14 @@ def test_packed_q4_0_queries_and_validation(L):
     assert L.q4_0_mmvq_packed(A, 17408, 5376, A, 6, A, None) == SHAPE  # K % 512 != 0
     assert L.q4_0_mmvq_packed(A + 8, 17408, 5120, A, 6, A, None) == ALIGN
     assert L.q4_0_mmvq_packed(A, 17408, 5120, A + 2, 6, A, None) == ALIGN
+    # the balanced launch: the same checks first, then its workspace's
+    ws = 1 << 20
+    assert L.q4_0_mmvq_packed_ws(A, 17408, 5120, A, 6, A, None, ws, None) == NULL
+    assert L.q4_0_mmvq_packed_ws(None, 17408, 5120, A, 6, A, A, ws, None) == NULL
+    assert L.q4_0_mmvq_packed_ws(A, 17408, 5120, A, 18, A, A, ws, None) == SHAPE
+    assert L.q4_0_mmvq_packed_ws(A, 17408, 5376, A, 6, A, A, ws, None) == SHAPE
+    assert L.q4_0_mmvq_packed_ws(A + 8, 17408, 5120, A, 6, A, A, ws, None) == ALIGN
+    assert L.q4_0_mmvq_packed_ws(A, 17408, 5120, A, 6, A, A + 128, ws, None) == ALIGN
 
 
 def test_gate_up_silu_validation(L):

@@ -227,3 +227,87 @@ def test_rms_norm_q8_1_sum(P, M, K):
     y2 = torch.empty_like(y)
     assert bq.rms_norm_q8_1_sum(dev(parts), 1e-6, y=y2, want_xq=False) is None
     assert torch.equal(y2, y)
+
+
+# The balanced launch (q4_0_mmvq_packed_ws): for M >= 9 the tiles past the
+# last multiple of the CU count are cut into min(4, K/256) ranges of K whose
+# sums meet in the workspace (M <= 8: no tile is cut).  Outputs of the other tiles are bitwise the plain
+# launch's; the cut tiles' are within the oracle's tolerance; results repeat
+# bit for bit.  Shapes: fewer tiles than CUs (every tile cut), a remainder
+# with a ragged last tile, the full ffn_up and down shapes.  One workspace
+# serves every shape and M in turn, and its counters are back at zero after
+# each call.
+WS_SMALL = [(1, 512), (37, 1024), (150, 1024), (4097, 1024), (6000, 5120)]
+WS_FULL = [(17408, 5120), (5120, 17408)]
+
+
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _ws_count_bytes():
+    return (_cus() * 4 + 255) // 256 * 256
+
+
+def _whole_rows(N, M):
+    if M <= 8:
+        return N
+    tiles = (N + 15) // 16
+    return min(N, 16 * (tiles - tiles % _cus()))
+
+
+def test_mmvq_packed_ws_small():
+    ws = bq.q4_0_mmvq_packed_workspace()
+    assert ws.numel() == bq.q4_0_mmvq_packed_ws_bytes()
+    for N, K in WS_SMALL:
+        w, x = synth.random_q4_0_case(5100 + N + K, N, K, 17)
+        xq = oracle.q8_1_quantize(x)
+        ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
+        wp, xqd = bq.q4_0_pack(dev(w)), dev(xq)
+        for m in (1, 2, 6, 8, 9, 17):
+            r0 = _whole_rows(N, m)
+            say(f"q4_0_mmvq_packed_ws N={N} K={K} M={m} (rows {r0}.. cut into K ranges)")
+            plain = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
+            yw = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m, ws=ws))
+            assert_close(yw, ref[:m], bound[:m], f"ws N{N} K{K} m{m}")
+            assert np.array_equal(yw[:, :r0].view(np.uint32), plain[:, :r0].view(np.uint32))
+            again = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m, ws=ws))
+            assert np.array_equal(again.view(np.uint32), yw.view(np.uint32))
+            assert not host(ws[:_ws_count_bytes()]).any()
+
+
+@pytest.mark.parametrize("N,K", WS_FULL)
+def test_mmvq_packed_ws_full(N, K):
+    ws = bq.q4_0_mmvq_packed_workspace()
+    wd = synth.q4_0_weights_device(5200 + N, N, K)
+    r0 = _whole_rows(N, 17)
+    w_cut = host(wd[r0:])                       # the cut tiles' rows, for the oracle
+    wp = bq.q4_0_pack(wd)
+    xqd = bq.q8_1_quantize(torch.randn((17, K), device=DEV))
+    xq = host(xqd)
+    ref, bound = oracle.q4_0_gemv(w_cut, N - r0, K, xq, 17)
+    for m in (1, 6, 9, 17):
+        say(f"q4_0_mmvq_packed_ws full N={N} K={K} M={m} (rows {r0}.. cut)")
+        plain = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
+        yw = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m, ws=ws))
+        whole = _whole_rows(N, m)
+        assert np.array_equal(yw[:, :whole].view(np.uint32), plain[:, :whole].view(np.uint32))
+        assert_close(yw[:, r0:], ref[:m], bound[:m], f"ws full cut rows m{m}")
+        again = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m, ws=ws))
+        assert np.array_equal(again.view(np.uint32), yw.view(np.uint32))
+        assert not host(ws[:_ws_count_bytes()]).any()
+
+
+def test_mmvq_packed_ws_rejects_small_or_misaligned_workspace():
+    N, K, M = 37, 1024, 6
+    w, x = synth.random_q4_0_case(5300, N, K, M)
+    wp, xqd = bq.q4_0_pack(dev(w)), bq.q8_1_quantize(dev(x))
+    ws = bq.q4_0_mmvq_packed_workspace()
+    y = torch.full((M, N), 7.0, device=DEV)
+    with pytest.raises(bq.Bq8Error) as e:
+        bq.q4_0_mmvq_packed(wp, N, K, xqd, M, y, ws=ws[:ws.numel() - 1])
+    assert e.value.status == 4
+    with pytest.raises(bq.Bq8Error) as e:
+        bq.q4_0_mmvq_packed(wp, N, K, xqd, M, y, ws=ws[16:])
+    assert e.value.status == 3
+    assert (host(y) == 7.0).all()
