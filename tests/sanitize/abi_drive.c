@@ -45,6 +45,10 @@ int main(void)
     EXPECT(q4_0_pack_bytes(17408, 5000), -1);
     EXPECT(q4_0_pack(A, 16, 512, A, q4_0_pack_bytes(16, 512) - 1, NULL), BQ8_ERR_SIZE);
     EXPECT(q4_0_mmvq_packed(A, 16, 500, A, 6, A, NULL), BQ8_ERR_SHAPE);
+    EXPECT(q4_0_mmvq_packed_ws(A, 16, 512, A, 6, A, NULL, 1 << 20, NULL), BQ8_ERR_NULL);
+    EXPECT(q4_0_mmvq_packed_ws(A, 16, 500, A, 6, A, A, 1 << 20, NULL), BQ8_ERR_SHAPE);
+    EXPECT(q4_0_mmvq_packed_ws(A, 16, 512, A, 6, A, (char *)A + 128, 1 << 20, NULL),
+           BQ8_ERR_ALIGN);
     EXPECT(q4_0_mmvq_packed_splits(5120, 17408), 4);
     EXPECT(q4_0_mmvq_packed_split(A, 16, 512, A, 6, 9, A, NULL), BQ8_ERR_SHAPE);
     EXPECT(q4_0_gate_up_silu_q8_1_packed(A, A, 48, 512, A, 6, NULL, NULL, NULL, A, NULL),
