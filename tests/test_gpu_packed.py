@@ -311,3 +311,28 @@ def test_mmvq_packed_ws_rejects_small_or_misaligned_workspace():
         bq.q4_0_mmvq_packed(wp, N, K, xqd, M, y, ws=ws[16:])
     assert e.value.status == 3
     assert (host(y) == 7.0).all()
+
+
+def test_mmvq_packed_ws_two_streams_own_workspaces():
+    """Two streams, each with its own workspace, run cut launches (M = 17,
+    tiles past the last multiple of the CU count) at the same time: every
+    result equals the single-stream result bit for bit."""
+    N, K, M = 16 * (_cus() + 37), 2048, 17
+    w, x = synth.random_q4_0_case(5400, N, K, M)
+    wp, xqd = bq.q4_0_pack(dev(w)), bq.q8_1_quantize(dev(x))
+    want = host(bq.q4_0_mmvq_packed(wp, N, K, xqd, M, ws=bq.q4_0_mmvq_packed_workspace()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    spaces = [bq.q4_0_mmvq_packed_workspace() for _ in streams]
+    outs = [[torch.empty((M, N), device=DEV) for _ in range(6)] for _ in streams]
+    torch.cuda.synchronize()
+    say(f"q4_0_mmvq_packed_ws on two streams N={N} K={K} M={M}")
+    for k in range(6):
+        for s, ws, o in zip(streams, spaces, outs):
+            with torch.cuda.stream(s):
+                bq.q4_0_mmvq_packed(wp, N, K, xqd, M, o[k], ws=ws)
+    torch.cuda.synchronize()
+    for o in outs:
+        for y in o:
+            assert np.array_equal(host(y).view(np.uint32), want.view(np.uint32))
+    for ws in spaces:
+        assert not host(ws[:_ws_count_bytes()]).any()
