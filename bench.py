@@ -199,7 +199,7 @@ def gate_up_joint(bq, s, i):
     """Joint gate/up + SiLU*up + Q8_1 on the ffn_up shape: gate is packed copy
     i, up copy i + 6 (two different 50 MB weights per launch)."""
     bq.q4_0_gate_up_silu_q8_1_packed(s["wps"][i % ROTATE], s["wps"][(i + 6) % ROTATE], s["N"],
-                                     s["K"], s["xq"], s["M"], s["hq"])
+                                     s["K"], s["xq"], s["M"], s["hq"], ws=s["pws"])
 
 
 def gate_up_separate(bq, s, i):
@@ -337,7 +337,7 @@ def time_shards(torch, bq, synth, per_batch=100):
     prod = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % n], Ns, K, xq, M, y, ws=pw),
                         per_batch)
     joint = time_batches(torch, lambda i: bq.q4_0_gate_up_silu_q8_1_packed(
-        wps[i % n], wps[(i + n // 2) % n], Ns, K, xq, M, hq), per_batch)
+        wps[i % n], wps[(i + n // 2) % n], Ns, K, xq, M, hq, ws=pw), per_batch)
     del wps
     Nd, Kd = synth.DOWN_SWEEP["N"], synth.DOWN_SWEEP["K"] // SHARDS
     db = q4_0_bytes(Nd, Kd)
@@ -687,7 +687,8 @@ def main():
                 "traffic": pmc_traffic(PMC_RECORD_GATE_UP),
                 "algorithmic_weight_bytes": 2 * wbytes,
                 "what": "gate [17408x5120] + up [17408x5120] Q4_0, M=6, SiLU(g)*u requantized "
-                        "to Q8_1: one joint launch vs two packed products + silu_mul_q8_1"},
+                        "to Q8_1: one joint launch (CU-balanced, q4_0_gate_up_silu_q8_1_packed_ws) "
+                        "vs two packed products + silu_mul_q8_1"},
             "lmhead_top1_us": round(min(lm_us, lmc_us), 2),
             "lmhead_top1_expanded_pack_us": round(lm_us, 2),
             "lmhead_top1_expanded_pack_us_batches": stats_us(lm_b, 2),

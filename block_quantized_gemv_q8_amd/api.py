@@ -106,6 +106,9 @@ def lib() -> ctypes.CDLL:
         L.q4_0_gate_up_silu_q8_1_packed.restype = _ST
         L.q4_0_gate_up_silu_q8_1_packed.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P,
                                                     _P, _P]
+        L.q4_0_gate_up_silu_q8_1_packed_ws.restype = _ST
+        L.q4_0_gate_up_silu_q8_1_packed_ws.argtypes = [_P, _P, _I64, _I64, _P, _I64, _P, _P, _P,
+                                                       _P, _P, _I64, _P]
         L.bq8_hbm_read_probe.restype = _ST
         L.bq8_hbm_read_probe.argtypes = [_P, _I64, _I64, _I64, _P, _P]
         L.q4_0_ffn_stream_layout.restype = _ST
@@ -417,16 +420,25 @@ def q4_0_mmvq_packed_split(wp: torch.Tensor, N: int, K: int, xq: torch.Tensor, M
 def q4_0_gate_up_silu_q8_1_packed(wg: torch.Tensor, wu: torch.Tensor, N: int, K: int,
                                   xq: torch.Tensor, M: int, hq: torch.Tensor | None = None,
                                   g: torch.Tensor | None = None, u: torch.Tensor | None = None,
-                                  h: torch.Tensor | None = None) -> torch.Tensor:
+                                  h: torch.Tensor | None = None,
+                                  ws: torch.Tensor | None = None) -> torch.Tensor:
     """hq = Q8_1(SiLU(W_gate X) * (W_up X)) in one launch, from the packed gate
     and up weights (q4_0_pack of Q4_0 [N][K] each) and the M Q8_1 rows of xq.
-    g, u, h, if given (f32 [M][N]), receive the two products and SiLU(g)*u."""
+    g, u, h, if given (f32 [M][N]), receive the two products and SiLU(g)*u.
+    With a workspace ws (q4_0_mmvq_packed_workspace) the launch balances the
+    32-column groups over the CUs (q4_0_gate_up_silu_q8_1_packed_ws)."""
     hq = _out(hq, (M, N // QK * Q8_1_BYTES), torch.uint8, wg.device, "hq")
     opt = [None if t is None else _dev(_out(t, (M, N), torch.float32, wg.device, name), name)
            for t, name in ((g, "g"), (u, "u"), (h, "h"))]
-    _check("q4_0_gate_up_silu_q8_1_packed", lib().q4_0_gate_up_silu_q8_1_packed(
-        _dev(wg, "wg", torch.uint8), _dev(wu, "wu", torch.uint8), N, K,
-        _dev(xq, "xq", torch.uint8), M, *opt, _dev(hq, "hq", torch.uint8), _stream()))
+    if ws is None:
+        _check("q4_0_gate_up_silu_q8_1_packed", lib().q4_0_gate_up_silu_q8_1_packed(
+            _dev(wg, "wg", torch.uint8), _dev(wu, "wu", torch.uint8), N, K,
+            _dev(xq, "xq", torch.uint8), M, *opt, _dev(hq, "hq", torch.uint8), _stream()))
+    else:
+        _check("q4_0_gate_up_silu_q8_1_packed_ws", lib().q4_0_gate_up_silu_q8_1_packed_ws(
+            _dev(wg, "wg", torch.uint8), _dev(wu, "wu", torch.uint8), N, K,
+            _dev(xq, "xq", torch.uint8), M, *opt, _dev(hq, "hq", torch.uint8),
+            _dev(ws, "ws", torch.uint8), ws.numel(), _stream()))
     return hq
 
 

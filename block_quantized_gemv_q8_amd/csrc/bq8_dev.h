@@ -156,6 +156,11 @@ __device__ __forceinline__ void q8_1_block_store(float v, int lane32, bool valid
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Leading bytes of a packed-launch workspace (q4_0_mmvq_packed_ws,
+// q4_0_gate_up_silu_q8_1_packed_ws) that hold its counters, one uint32 per
+// CU rounded up to 256 bytes; range sums follow.
+inline int64_t pk_ws_count_bytes(int64_t cus) { return (cus * 4 + 255) / 256 * 256; }
+
 inline bq8_status launch_status()
 {
     return hipGetLastError() == hipSuccess ? BQ8_OK : BQ8_ERR_HIP;

@@ -23,6 +23,14 @@ namespace bq8 {
 
 static int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
+// Clears the workspace's counters at the start of a pass (a kernel, not a
+// memset, so that the pass can be captured in a HIP graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *__restrict__ p, int n)
+{
+    for (int i = threadIdx.x; i < n; i += blockDim.x)
+        p[i] = 0u;
+}
+
 // Offsets of the stage buffers inside the caller's workspace; `parts`
 // holds the packed path's split down-projection sums (up to eight partial
 // [M][hidden] rows), internal to the pass.
@@ -61,7 +69,9 @@ BQ8_EXPORT bq8_status q4_0_ffn_stream_layout(int64_t M, int64_t hidden, int64_t 
     offsets[1] = L.g;
     offsets[2] = L.u;
     offsets[3] = L.hq;
-    offsets[4] = L.total;
+    // on a device, room for the joint launches' workspace after the stages
+    const int64_t wsb = q4_0_mmvq_packed_ws_bytes();
+    offsets[4] = L.total + (wsb > 0 ? align256(wsb) : 0);
     return BQ8_OK;
 }
 
@@ -104,15 +114,40 @@ static bq8_status ffn_stream(proj_fn proj, bool joint, int64_t align_k,
     if (P < 1)
         return BQ8_ERR_SHAPE;
 
+    // packed path: if the work area also holds the workspace, the joint
+    // launches balance their 32-column groups over the CUs; its counters
+    // are cleared here once, and every completed launch leaves them clear
+    void *ws = nullptr;
+    int64_t wsb = 0;
+    int cus = 0, dev = 0;
+    if (joint && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0) {
+        wsb = q4_0_mmvq_packed_ws_bytes();
+        if (wsb > 0 && work_bytes >= L.total + align256(wsb))
+            ws = base + L.total;
+    }
+
     // Everything below was validated above; a nonzero status can only be a
     // launch failure, reported as is.
+    if (ws) {
+        const int words = (int)(pk_ws_count_bytes(cus) / 4);
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream,
+                           static_cast<uint32_t *>(ws), words);
+        if (hipGetLastError() != hipSuccess)
+            return BQ8_ERR_HIP;
+    }
     bq8_status st = q8_1_quantize(x0, M, hidden, xq, stream);
     for (int64_t l = 0; l < layers && st == BQ8_OK; ++l) {
         if (l > 0 && joint)
             st = rms_norm_q8_1_sum(parts, P, M, hidden, eps, nullptr, nullptr, xq, stream);
         if (l > 0 && !joint)
             st = rms_norm_q8_1(y, M, hidden, eps, nullptr, xq, stream);
-        if (st == BQ8_OK && joint)
+        if (st == BQ8_OK && joint && ws)
+            st = q4_0_gate_up_silu_q8_1_packed_ws(w_gate[l], w_up[l], ffn, hidden, xq, M,
+                                                  nullptr, nullptr, nullptr, hq, ws, wsb, stream);
+        if (st == BQ8_OK && joint && !ws)
             st = q4_0_gate_up_silu_q8_1_packed(w_gate[l], w_up[l], ffn, hidden, xq, M, nullptr,
                                                nullptr, nullptr, hq, stream);
         if (st == BQ8_OK && !joint)

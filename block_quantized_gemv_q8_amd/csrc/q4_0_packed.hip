@@ -339,6 +339,45 @@ __device__ __forceinline__ float pk_partial_sum(const uint8_t *smem, int stride,
     return p[0] + p[SLOTS * 32];
 }
 
+// The meeting's reads: the P range sums at p, p + stride, ... (agent-scope
+// atomic loads, all issued before the first add; P <= 4), added in range
+// order from +0.
+__device__ __forceinline__ float pk_range_sum(const float *p, size_t stride, int P)
+{
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        v[r] = __hip_atomic_load(p + (size_t)(r < P ? r : 0) * stride, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    float sacc = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (r < P)
+            sacc += v[r];
+    return sacc;
+}
+
+// Two such sums, all 2P loads issued first.
+__device__ __forceinline__ void pk_range_sum2(const float *p, const float *q, size_t stride,
+                                              int P, float &sp, float &sq)
+{
+    float v[4], w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const size_t o = (size_t)(r < P ? r : 0) * stride;
+        v[r] = __hip_atomic_load(p + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w[r] = __hip_atomic_load(q + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    sp = 0.0f;
+    sq = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (r < P) {
+            sp += v[r];
+            sq += w[r];
+        }
+}
+
 // y[m][n] for one 16-row tile; the tile's S waves take its 8-block chunks
 // round-robin and their sums are added in wave order.  Workgroup b works in
 // one of three ways:
@@ -433,15 +472,45 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
     __syncthreads();
     if (!*last)
         return;
-    for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x) {
-        float sacc = 0.0f;
-        for (int p = 0; p < P; ++p)
-            sacc += __hip_atomic_load(rsum + (size_t)p * SLOTS * 32 + idx, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-        store_y(idx, sacc);
-    }
+    for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x)
+        store_y(idx, pk_range_sum(rsum + idx, SLOTS * 32, P));
     if (threadIdx.x == 0)
         __hip_atomic_store(ws_count + j / P, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The joint launch's epilogue for 32-column group grp (columns n0 .. n0+31):
+// one 32-lane group per activation row m, lane c is column n0 + c;
+// sums(half, slot, l, sg, su) gives the gate and up tiles' sums (tiles
+// 2grp + half of each) at the accumulator position of (m, c).
+template <int M, typename Sum>
+__device__ __forceinline__ void gate_up_epilogue(Sum sum, int N, int n0, int grp,
+                                                 float *__restrict__ g, float *__restrict__ u,
+                                                 float *__restrict__ h, uint8_t *__restrict__ hq)
+{
+    const int groups = blockDim.x >> 5;
+    const int c = threadIdx.x & 31;
+    const int half = c >> 4; // tile 2grp + half of each matrix
+    for (int m0 = 0; m0 < M; m0 += groups) {
+        const int m = m0 + (int)(threadIdx.x >> 5);
+        const bool valid = m < M;
+        const int mc = valid ? m : M - 1;
+        const int slot = (mc >> 3) * 4 + (mc & 3);
+        const int l = 16 * ((mc >> 2) & 1) + (c & 15);
+        float sg, su;
+        sum(half, slot, l, sg, su);
+        const float gv = sg * 0.0625f, uv = su * 0.0625f;
+        const float hv = gv / (1.0f + expf(-gv)) * uv;
+        const size_t o = (size_t)mc * N + n0 + c;
+        if (valid) {
+            if (g)
+                g[o] = gv;
+            if (u)
+                u[o] = uv;
+            if (h)
+                h[o] = hv;
+        }
+        q8_1_block_store(hv, c, valid, hq + ((size_t)mc * (N / QK) + grp) * Q8_1_BYTES);
+    }
 }
 
 // Gate and up projections of one Q8_1 activation with the SiLU(gate) * up
@@ -456,20 +525,41 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
 // u and h never reach memory unless asked for.  Per column and row, g and u
 // are the sums of the plain product (same per-wave order, waves added in
 // order), h = g / (1 + exp(-g)) * u in binary32, then the Q8_1 block of h.
+//
+// CU balance (ws_sum != NULL): workgroups b < whole own group b as above;
+// the groups past the last multiple of the CU count are cut into P K ranges
+// (range r = chunks r*C/P .. (r+1)*C/P - 1), workgroup whole + j taking range
+// j % P of group whole + j / P.  A range's four tiles' sums go to
+// ws_sum[j][4][SLOTS*32] as agent-scope atomic stores; the workgroup waits
+// for them (vmcnt(0)) and counts itself in ws_count[j / P]; the one that
+// brings the count to P adds the P ranges' sums in range order, runs the
+// epilogue above on them and sets the count back to 0 (the meeting of
+// q4_0_mmvq_packed_kernel).
 template <int M>
 __global__ __launch_bounds__(512) void q4_0_gate_up_packed_kernel(
     const uint8_t *__restrict__ QG, const uint16_t *__restrict__ DG,
-    const uint8_t *__restrict__ QU, const uint16_t *__restrict__ DU, int N, int nb,
-    const uint8_t *__restrict__ xq, float *__restrict__ g, float *__restrict__ u,
-    float *__restrict__ h, uint8_t *__restrict__ hq)
+    const uint8_t *__restrict__ QU, const uint16_t *__restrict__ DU, int N, int nb, int P,
+    int whole, const uint8_t *__restrict__ xq, float *__restrict__ g, float *__restrict__ u,
+    float *__restrict__ h, uint8_t *__restrict__ hq, float *__restrict__ ws_sum,
+    uint32_t *__restrict__ ws_count)
 {
     constexpr int MS = PkShape<M>::MS;
+    constexpr int SLOTS = MS * 4;
     constexpr int STRIDE = pk_wave_stride<M, 4>();
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
-    const int n0 = blockIdx.x * 2 * PK_TILE;
+    const int nch = nb / PK_CB;
+    int grp = blockIdx.x, c0 = 0, c1 = nch, j = -1;
+    if ((int)blockIdx.x >= whole) {
+        j = blockIdx.x - whole;
+        const int r = j % P;
+        grp = whole + j / P;
+        c0 = (int)((int64_t)r * nch / P);
+        c1 = (int)((int64_t)(r + 1) * nch / P);
+    }
+    const int n0 = grp * 2 * PK_TILE;
     const size_t tb = (size_t)PK_TILE * nb * 16; // nibble bytes of one full tile
     const size_t t0 = (size_t)n0 * nb * 16;
     const uint8_t *tile[4] = {QG + t0, QG + t0 + tb, QU + t0, QU + t0 + tb};
@@ -477,38 +567,49 @@ __global__ __launch_bounds__(512) void q4_0_gate_up_packed_kernel(
                                 DU + (size_t)n0 * nb, DU + (size_t)(n0 + PK_TILE) * nb};
     float acc[4][MS][4];
     pk_accumulate<M, 4>(tile, dtile, PK_TILE, (size_t)8 * PK_TILE * 16, (size_t)2 * PK_TILE * 8,
-                        nb, 0, nb / PK_CB, xq, smem + (size_t)wave * STRIDE, acc);
+                        nb, c0, c1 - c0, xq, smem + (size_t)wave * STRIDE, acc);
     pk_store_partials<4, MS>(acc, smem + (size_t)wave * STRIDE, lane);
     __syncthreads();
-    // one 32-lane group per activation row m: lane c is column n0 + c
-    const int groups = blockDim.x >> 5;
-    const int c = threadIdx.x & 31;
-    const int half = c >> 4; // tile 2p + half of each matrix
-    for (int m0 = 0; m0 < M; m0 += groups) {
-        const int m = m0 + (int)(threadIdx.x >> 5);
-        const bool valid = m < M;
-        const int mc = valid ? m : M - 1;
-        const int slot = (mc >> 3) * 4 + (mc & 3);
-        const int l = 16 * ((mc >> 2) & 1) + (c & 15);
-        float sg = 0.0f, su = 0.0f;
-        for (int v = 0; v < S; ++v) {
-            sg += pk_partial_sum<4, MS>(smem, STRIDE, v, half, slot, l);
-            su += pk_partial_sum<4, MS>(smem, STRIDE, v, 2 + half, slot, l);
-        }
-        const float gv = sg * 0.0625f, uv = su * 0.0625f;
-        const float hv = gv / (1.0f + expf(-gv)) * uv;
-        const size_t o = (size_t)mc * N + n0 + c;
-        if (valid) {
-            if (g)
-                g[o] = gv;
-            if (u)
-                u[o] = uv;
-            if (h)
-                h[o] = hv;
-        }
-        q8_1_block_store(hv, c, valid,
-                         hq + ((size_t)mc * (N / QK) + blockIdx.x) * Q8_1_BYTES);
+    // tile i's sum over this workgroup's waves at (slot, l)
+    auto wave_sum = [&](int i, int slot, int l) {
+        float sacc = 0.0f;
+        for (int v = 0; v < S; ++v)
+            sacc += pk_partial_sum<4, MS>(smem, STRIDE, v, i, slot, l);
+        return sacc;
+    };
+    if (j < 0) {
+        gate_up_epilogue<M>(
+            [&](int half, int slot, int l, float &sg, float &su) {
+                sg = wave_sum(half, slot, l);
+                su = wave_sum(2 + half, slot, l);
+            },
+            N, n0, grp, g, u, h, hq);
+        return;
     }
+    float *rsum = ws_sum + (size_t)(j - j % P) * 4 * SLOTS * 32; // the group's P ranges
+    for (int idx = threadIdx.x; idx < 4 * SLOTS * 32; idx += blockDim.x) {
+        const int i = idx / (SLOTS * 32), slot = (idx >> 5) % SLOTS, l = idx & 31;
+        __hip_atomic_store(rsum + (size_t)(j % P) * 4 * SLOTS * 32 + idx, wave_sum(i, slot, l),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // the partial sums have been read: wave 0's first LDS word carries the verdict
+    int *last = reinterpret_cast<int *>(smem);
+    if (threadIdx.x == 0)
+        *last = __hip_atomic_fetch_add(ws_count + j / P, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1);
+    __syncthreads();
+    if (!*last)
+        return;
+    gate_up_epilogue<M>(
+        [&](int half, int slot, int l, float &sg, float &su) {
+            const float *p = rsum + (size_t)half * SLOTS * 32 + slot * 32 + l;
+            pk_range_sum2(p, p + (size_t)2 * SLOTS * 32, (size_t)4 * SLOTS * 32, P, sg, su);
+        },
+        N, n0, grp, g, u, h, hq);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(ws_count + j / P, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Largest dynamic LDS a workgroup may use on the current device (queried
@@ -570,12 +671,12 @@ static int64_t device_cus()
     return cached[dev];
 }
 
-// Workspace of the balanced product: ws_count (one uint32 per remainder
-// tile, fewer than CUs of them) in the first pk_ws_count_bytes(cus) bytes,
-// then ws_sum, PK_WS_TILE_FLOATS floats per remainder tile (P * SLOTS * 32
-// at most: 4 ranges, 12 slots at M = 17).
-constexpr int64_t PK_WS_TILE_FLOATS = 4 * 12 * 32;
-static int64_t pk_ws_count_bytes(int64_t cus) { return (cus * 4 + 255) / 256 * 256; }
+// Workspace of the balanced launches: ws_count (one uint32 per cut tile or
+// 32-column group, fewer than CUs of them) in the first
+// pk_ws_count_bytes(cus) bytes, then ws_sum, PK_WS_TILE_FLOATS floats per
+// cut tile or group (P * 4 * SLOTS * 32 at most: 4 ranges, the joint
+// launch's 4 tiles, 12 slots at M = 17; the product uses a quarter).
+constexpr int64_t PK_WS_TILE_FLOATS = 4 * 4 * 12 * 32;
 static int64_t pk_ws_bytes(int64_t cus)
 {
     return pk_ws_count_bytes(cus) + cus * PK_WS_TILE_FLOATS * (int64_t)sizeof(float);
@@ -647,8 +748,8 @@ static int gate_up_waves(int64_t groups, int nb, int M, int64_t wave_lds, int64_
 
 template <int M>
 static bq8_status gate_up_launch(const uint8_t *wg, const uint8_t *wu, int64_t N, int64_t K,
-                                 const void *xq, float *g, float *u, float *h, void *hq,
-                                 hipStream_t stream)
+                                 const void *xq, float *g, float *u, float *h, void *hq, void *ws,
+                                 int64_t cus, hipStream_t stream)
 {
     const int nb = (int)(K / QK);
     const int64_t groups = N / (2 * PK_TILE);
@@ -665,11 +766,24 @@ static bq8_status gate_up_launch(const uint8_t *wg, const uint8_t *wu, int64_t N
         attr_set = true;
     }
     const size_t dplane = (size_t)N * nb * 16;
+    // with a workspace and at least as many groups as CUs, the groups past
+    // the last multiple of the CU count are cut into P K ranges each (ffn
+    // shape, M = 6 / 1 / 9 / 17: 22.4 / 21.5 / 28.1 / 34.5 us uncut, 20.6 /
+    // 19.9 / 26.1 / 31.6 us cut).  With fewer groups than CUs every group
+    // would be cut, and the meeting outweighs the balance (the 8-way shard,
+    // 68 groups: 9.5 us uncut, 12.3 us cut).
+    const int P = packed_parts(nb / PK_CB);
+    const int64_t whole = ws && groups >= cus ? groups - groups % cus : groups;
+    const int64_t grid = whole + (groups - whole) * P;
+    uint32_t *ws_count = static_cast<uint32_t *>(ws);
+    float *ws_sum = ws ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
+                                                   pk_ws_count_bytes(cus))
+                       : nullptr;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((q4_0_gate_up_packed_kernel<M>), dim3((unsigned)groups), dim3(WAVE * s),
+    hipLaunchKernelGGL((q4_0_gate_up_packed_kernel<M>), dim3((unsigned)grid), dim3(WAVE * s),
                        (size_t)lds, stream, wg, reinterpret_cast<const uint16_t *>(wg + dplane), wu,
-                       reinterpret_cast<const uint16_t *>(wu + dplane), (int)N, nb,
-                       (const uint8_t *)xq, g, u, h, (uint8_t *)hq);
+                       reinterpret_cast<const uint16_t *>(wu + dplane), (int)N, nb, P, (int)whole,
+                       (const uint8_t *)xq, g, u, h, (uint8_t *)hq, ws_sum, ws_count);
     return launch_status();
 }
 
@@ -809,10 +923,9 @@ BQ8_EXPORT bq8_status q4_0_mmvq_packed_split(const void *wp, int64_t N, int64_t 
     return packed_product(wp, N, K, xq, M, (int)nsplit, ypart, nullptr, 0, stream);
 }
 
-BQ8_EXPORT bq8_status q4_0_gate_up_silu_q8_1_packed(const void *wg, const void *wu, int64_t N,
-                                                    int64_t K, const void *xq, int64_t M,
-                                                    float *g, float *u, float *h, void *hq,
-                                                    void *stream)
+static bq8_status gate_up_product(const void *wg, const void *wu, int64_t N, int64_t K,
+                                  const void *xq, int64_t M, float *g, float *u, float *h,
+                                  void *hq, void *ws, int64_t ws_bytes, void *stream)
 {
     if (!wg || !wu || !xq || !hq)
         return BQ8_ERR_NULL;
@@ -820,27 +933,54 @@ BQ8_EXPORT bq8_status q4_0_gate_up_silu_q8_1_packed(const void *wg, const void *
         M * K >= (int64_t(1) << 31) || M * N >= (int64_t(1) << 31))
         return BQ8_ERR_SHAPE;
     if (!aligned(wg, 16) || !aligned(wu, 16) || !aligned(xq, 4) || !aligned(hq, 4) ||
-        (g && !aligned(g, 4)) || (u && !aligned(u, 4)) || (h && !aligned(h, 4)))
+        (g && !aligned(g, 4)) || (u && !aligned(u, 4)) || (h && !aligned(h, 4)) ||
+        !aligned(ws, 256))
         return BQ8_ERR_ALIGN;
+    int64_t cus = 0;
+    if (ws) {
+        cus = device_cus();
+        if (cus <= 0)
+            return BQ8_ERR_HIP;
+        if (ws_bytes < pk_ws_bytes(cus))
+            return BQ8_ERR_SIZE;
+    }
     const uint8_t *a = (const uint8_t *)wg, *b = (const uint8_t *)wu;
     hipStream_t s = (hipStream_t)stream;
     switch (M) {
-    case 1: return gate_up_launch<1>(a, b, N, K, xq, g, u, h, hq, s);
-    case 2: return gate_up_launch<2>(a, b, N, K, xq, g, u, h, hq, s);
-    case 3: return gate_up_launch<3>(a, b, N, K, xq, g, u, h, hq, s);
-    case 4: return gate_up_launch<4>(a, b, N, K, xq, g, u, h, hq, s);
-    case 5: return gate_up_launch<5>(a, b, N, K, xq, g, u, h, hq, s);
-    case 6: return gate_up_launch<6>(a, b, N, K, xq, g, u, h, hq, s);
-    case 7: return gate_up_launch<7>(a, b, N, K, xq, g, u, h, hq, s);
-    case 8: return gate_up_launch<8>(a, b, N, K, xq, g, u, h, hq, s);
-    case 9: return gate_up_launch<9>(a, b, N, K, xq, g, u, h, hq, s);
-    case 10: return gate_up_launch<10>(a, b, N, K, xq, g, u, h, hq, s);
-    case 11: return gate_up_launch<11>(a, b, N, K, xq, g, u, h, hq, s);
-    case 12: return gate_up_launch<12>(a, b, N, K, xq, g, u, h, hq, s);
-    case 13: return gate_up_launch<13>(a, b, N, K, xq, g, u, h, hq, s);
-    case 14: return gate_up_launch<14>(a, b, N, K, xq, g, u, h, hq, s);
-    case 15: return gate_up_launch<15>(a, b, N, K, xq, g, u, h, hq, s);
-    case 16: return gate_up_launch<16>(a, b, N, K, xq, g, u, h, hq, s);
-    default: return gate_up_launch<17>(a, b, N, K, xq, g, u, h, hq, s);
+    case 1: return gate_up_launch<1>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 2: return gate_up_launch<2>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 3: return gate_up_launch<3>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 4: return gate_up_launch<4>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 5: return gate_up_launch<5>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 6: return gate_up_launch<6>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 7: return gate_up_launch<7>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 8: return gate_up_launch<8>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 9: return gate_up_launch<9>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 10: return gate_up_launch<10>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 11: return gate_up_launch<11>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 12: return gate_up_launch<12>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 13: return gate_up_launch<13>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 14: return gate_up_launch<14>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 15: return gate_up_launch<15>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    case 16: return gate_up_launch<16>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
+    default: return gate_up_launch<17>(a, b, N, K, xq, g, u, h, hq, ws, cus, s);
     }
+}
+
+BQ8_EXPORT bq8_status q4_0_gate_up_silu_q8_1_packed(const void *wg, const void *wu, int64_t N,
+                                                    int64_t K, const void *xq, int64_t M,
+                                                    float *g, float *u, float *h, void *hq,
+                                                    void *stream)
+{
+    return gate_up_product(wg, wu, N, K, xq, M, g, u, h, hq, nullptr, 0, stream);
+}
+
+BQ8_EXPORT bq8_status q4_0_gate_up_silu_q8_1_packed_ws(const void *wg, const void *wu, int64_t N,
+                                                       int64_t K, const void *xq, int64_t M,
+                                                       float *g, float *u, float *h, void *hq,
+                                                       void *ws, int64_t ws_bytes, void *stream)
+{
+    if (!ws)
+        return BQ8_ERR_NULL;
+    return gate_up_product(wg, wu, N, K, xq, M, g, u, h, hq, ws, ws_bytes, stream);
 }

@@ -170,8 +170,9 @@ bq8_status q4_0_mmvq(const void *w, int64_t N, int64_t K, const void *xq, int64_
  *   Calls that overlap in time (e.g. on different streams) must not share
  *   a workspace.  ws NULL -> BQ8_ERR_NULL, ws_bytes too small ->
  *   BQ8_ERR_SIZE, ws misaligned -> BQ8_ERR_ALIGN.
- * q4_0_mmvq_packed_ws_bytes: host; the workspace q4_0_mmvq_packed_ws needs
- *   on the current device (about 6 KB per CU), or -1 without a device.
+ * q4_0_mmvq_packed_ws_bytes: host; the workspace q4_0_mmvq_packed_ws and
+ *   q4_0_gate_up_silu_q8_1_packed_ws need on the current device (about
+ *   24 KB per CU), or -1 without a device.  One workspace serves both.
  * q4_0_mmvq_packed_split: the same product with K cut into nsplit ranges of
  *   8-block chunks (range p = chunks floor(p*C/nsplit) .. floor((p+1)*C/
  *   nsplit) - 1 of the C = K/256 chunks), each computed by its own
@@ -214,12 +215,25 @@ int64_t q4_0_mmvq_packed_splits(int64_t N, int64_t K);
  *   depend on whether they are given.  hq is bitwise the Q8_1 of the h
  *   computed here; g and u equal q4_0_mmvq_packed's up to the binary32
  *   summation order.
+ * q4_0_gate_up_silu_q8_1_packed_ws: the same launch balanced over the CUs
+ *   when N/32 is at least the CU count (else it is the plain launch, bit for
+ *   bit): each 32-column group past the largest multiple of the CU count is cut
+ *   into P = min(4, K/256) ranges of K computed by separate workgroups,
+ *   whose range sums meet in the workspace (as q4_0_mmvq_packed_ws) and are
+ *   added in range order before the epilogue.  For those groups g and u
+ *   equal q4_0_gate_up_silu_q8_1_packed's up to the binary32 summation
+ *   order, the others bit for bit; hq is the Q8_1 of the h computed here.
+ *   ws, ws_bytes and their errors as q4_0_mmvq_packed_ws.
  * Shape: M = 1..17, N % 32 == 0, 32 <= N < 2^31, K as q4_0_mmvq_packed,
  *   M*K < 2^31, M*N < 2^31.
  * ---------------------------------------------------------------------- */
 bq8_status q4_0_gate_up_silu_q8_1_packed(const void *wg, const void *wu, int64_t N, int64_t K,
                                          const void *xq, int64_t M, float *g, float *u, float *h,
                                          void *hq, void *stream);
+bq8_status q4_0_gate_up_silu_q8_1_packed_ws(const void *wg, const void *wu, int64_t N,
+                                            int64_t K, const void *xq, int64_t M, float *g,
+                                            float *u, float *h, void *hq, void *ws,
+                                            int64_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Q6_K expansion (run once, at load time).  The fused-head page expands the
@@ -384,7 +398,9 @@ bq8_status rms_norm_q8_1_sum(const float *yparts, int64_t nparts, int64_t M, int
  *   32 <= ffn <= 2^26, M*ffn < 2^31, 1 <= layers <= 2^20, eps > 0.
  * Every layer's pointers are checked before anything is enqueued.
  * q4_0_ffn_stream_layout: host; writes the four stage offsets and the total
- *   workspace size to offsets[0..4].
+ *   work-area size to offsets[0..4].  On a device the total also has room,
+ *   after the stages, for the workspace of q4_0_mmvq_packed_ws_bytes(),
+ *   which the packed pass below uses.
  * ---------------------------------------------------------------------- */
 bq8_status q4_0_ffn_stream_layout(int64_t M, int64_t hidden, int64_t ffn, int64_t *offsets);
 bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *const *w_up,
@@ -399,7 +415,11 @@ bq8_status q4_0_ffn_stream(const void *const *w_gate, const void *const *w_up,
  *   parts = q4_0_mmvq_packed_split(w_down[l], hq, P)
  * with P = q4_0_mmvq_packed_splits(hidden, ffn), and after the last layer
  * y = the sum of its parts (rms_norm_q8_1_sum with only y).  y is written
- * only by that last step; the g and u stage buffers are not written.
+ * only by that last step; the g and u stage buffers are not written.  When
+ * work_bytes also covers the workspace (the layout's total on a device), the
+ * joint launches are q4_0_gate_up_silu_q8_1_packed_ws on it, its counters
+ * cleared once at the start of the pass by a kernel; with a work area that
+ * holds the stages only, they are q4_0_gate_up_silu_q8_1_packed.
  * hidden and ffn must also be multiples of 512. */
 bq8_status q4_0_ffn_stream_packed(const void *const *w_gate, const void *const *w_up,
                                   const void *const *w_down, int64_t layers, int64_t M,

@@ -40,7 +40,8 @@ def test_header_declares_expected_entry_points():
               "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "rms_norm_q8_1_sum",
               "q6k_lmhead_candidate_max", "q6k_compact_bytes", "q6k_pack_compact",
               "q6k_lmhead_top1_compact", "q6k_lmhead_candidate_max_compact",
-              "bq8_hbm_read_probe", "q4_0_mmvq_packed_ws", "q4_0_mmvq_packed_ws_bytes"]:
+              "bq8_hbm_read_probe", "q4_0_mmvq_packed_ws", "q4_0_mmvq_packed_ws_bytes",
+              "q4_0_gate_up_silu_q8_1_packed_ws"]:
         assert n in names
 
 
@@ -270,6 +271,12 @@ def test_gate_up_silu_validation(L):
     assert call(g=A + 2) == ALIGN
     assert call(u=A + 1) == ALIGN
     assert call(h=A + 3) == ALIGN
+    # the balanced launch: its workspace is required and 256-byte aligned
+    ws = 1 << 24
+    J = L.q4_0_gate_up_silu_q8_1_packed_ws
+    assert J(A, A, 17408, 5120, A, 6, None, None, None, A, None, ws, None) == NULL
+    assert J(A, A, 17400, 5120, A, 6, None, None, None, A, A, ws, None) == SHAPE
+    assert J(A, A, 17408, 5120, A, 6, None, None, None, A, A + 128, ws, None) == ALIGN
 
 
 def test_split_product_and_summed_rms_validation(L):

@@ -51,14 +51,15 @@ def assert_close(gpu, ref, bound, what):
                            f"{tuple(np.argwhere(bad)[0])}")
 
 
-def run_case(wg, wu, x, N, K, M):
-    """Joint kernel with every optional output, checked stage by stage."""
+def run_case(wg, wu, x, N, K, M, ws=None):
+    """Joint kernel with every optional output, checked stage by stage (the
+    CU-balanced launch through workspace ws if given)."""
     xq = oracle.q8_1_quantize(x)
     pg, pu, xqd = bq.q4_0_pack(dev(wg)), bq.q4_0_pack(dev(wu)), dev(xq)
     g = torch.empty((M, N), dtype=torch.float32, device=DEV)
     u = torch.empty_like(g)
     h = torch.empty_like(g)
-    hq = host(bq.q4_0_gate_up_silu_q8_1_packed(pg, pu, N, K, xqd, M, g=g, u=u, h=h))
+    hq = host(bq.q4_0_gate_up_silu_q8_1_packed(pg, pu, N, K, xqd, M, g=g, u=u, h=h, ws=ws))
     gg, ug, hg = host(g), host(u), host(h)
 
     ref_g, bound_g = oracle.q4_0_gemv(wg, N, K, xq, M)
@@ -76,7 +77,7 @@ def run_case(wg, wu, x, N, K, M):
     assert np.array_equal(host(h2).view(np.uint32), hg.view(np.uint32))
     assert (hq2 == hq).all()
     # no optional outputs: same hq
-    hq3 = host(bq.q4_0_gate_up_silu_q8_1_packed(pg, pu, N, K, xqd, M))
+    hq3 = host(bq.q4_0_gate_up_silu_q8_1_packed(pg, pu, N, K, xqd, M, ws=ws))
     assert (hq3 == hq).all()
     return gg, ug, hg, hq
 
@@ -114,3 +115,58 @@ def test_gate_up_silu_zero_activation():
         assert not gg[m].any() and not ug[m].any() and not hg[m].any()
         assert not hq[m].any()   # d = s = 0, every quant 0
 
+
+
+# The CU-balanced launch (q4_0_gate_up_silu_q8_1_packed_ws): with at least
+# as many 32-column groups as CUs, the groups past the last multiple of the
+# CU count are cut into min(4, K/256) ranges of K that meet in the workspace
+# (fewer groups: nothing is cut).  Every bar above holds for it; the
+# uncut groups' g, u and hq are bitwise the plain launch's; results repeat
+# bit for bit; the workspace's counters are back at zero after each call.
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _ws_shapes():
+    c = _cus()
+    return [(6, 64, 512), (17, 1024, 1536), (6, 32 * (c + 37), 2048), (9, 32 * (c + 5), 4608),
+            (1, 32 * (2 * c + 3), 1024)]
+
+
+@pytest.mark.parametrize("case", range(5))
+def test_gate_up_silu_ws(case):
+    M, N, K = _ws_shapes()[case]
+    say(f"gate_up_silu_ws M={M} N={N} K={K}")
+    wg, x = synth.random_q4_0_case(6500 + M + N + K, N, K, M)
+    wu, _ = synth.random_q4_0_case(6600 + M + N + K, N, K, 1)
+    _check_ws(wg, wu, x, N, K, M)
+
+
+@pytest.mark.parametrize("M", [6, 17])
+def test_gate_up_silu_ws_full_ffn_shape(M):
+    N, K = synth.FFN_UP["N"], synth.FFN_UP["K"]
+    say(f"gate_up_silu_ws full ffn shape M={M}")
+    wu, x = synth.ffn_up(M=max(M, 6))
+    wg, _ = synth.random_q4_0_case(6700, N, K, 1)
+    _check_ws(wg, wu, x[:M], N, K, M)
+
+
+def _check_ws(wg, wu, x, N, K, M):
+    ws = bq.q4_0_mmvq_packed_workspace()
+    count_bytes = (_cus() * 4 + 255) // 256 * 256
+    gg, ug, hg, hq = run_case(wg, wu, x, N, K, M, ws=ws)
+    assert not host(ws[:count_bytes]).any()
+    groups = N // 32
+    whole = groups - groups % _cus() if groups >= _cus() else groups
+    pg, pu = bq.q4_0_pack(dev(wg)), bq.q4_0_pack(dev(wu))
+    xqd = dev(oracle.q8_1_quantize(x))
+    g = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    u = torch.empty_like(g)
+    hq_p = host(bq.q4_0_gate_up_silu_q8_1_packed(pg, pu, N, K, xqd, M, g=g, u=u))
+    c = 32 * whole
+    assert np.array_equal(gg[:, :c].view(np.uint32), host(g)[:, :c].view(np.uint32))
+    assert np.array_equal(ug[:, :c].view(np.uint32), host(u)[:, :c].view(np.uint32))
+    assert (hq.reshape(M, groups, 36)[:, :whole] == hq_p.reshape(M, groups, 36)[:, :whole]).all()
+    again = host(bq.q4_0_gate_up_silu_q8_1_packed(pg, pu, N, K, xqd, M, ws=ws))
+    assert (again == hq).all()
+    assert not host(ws[:count_bytes]).any()

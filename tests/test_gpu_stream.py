@@ -132,15 +132,17 @@ def test_stream_full_shape_last_layer_stages():
 
 
 def composed_packed(wg, wu, wd, x0, eps, hidden, ffn):
-    """The packed stream's steps, one C-ABI call each."""
+    """The packed stream's steps, one C-ABI call each (its joint launches are
+    the CU-balanced ones, through a workspace, as in the stream)."""
     xq = bq.q8_1_quantize(x0)
     M = x0.shape[0]
     P = bq.q4_0_mmvq_packed_splits(hidden, ffn)
+    ws = bq.q4_0_mmvq_packed_workspace()
     parts = None
     for l in range(len(wg)):
         if l > 0:
             xq = bq.rms_norm_q8_1_sum(parts, eps)
-        hq = bq.q4_0_gate_up_silu_q8_1_packed(wg[l], wu[l], ffn, hidden, xq, M)
+        hq = bq.q4_0_gate_up_silu_q8_1_packed(wg[l], wu[l], ffn, hidden, xq, M, ws=ws)
         parts = bq.q4_0_mmvq_packed_split(wd[l], hidden, ffn, hq, M, P)
     y = torch.empty((M, hidden), dtype=torch.float32, device=DEV)
     bq.rms_norm_q8_1_sum(parts, eps, y=y, want_xq=False)
@@ -187,7 +189,8 @@ def test_packed_stream_full_shape_last_layer_stages():
     u, h = torch.empty_like(g), torch.empty_like(g)
     hq = host(bq.q4_0_gate_up_silu_q8_1_packed(pg[-1], pu[-1], F, H,
                                                torch.from_numpy(st["xq"]).to(DEV), M,
-                                               g=g, u=u, h=h))
+                                               g=g, u=u, h=h,
+                                               ws=bq.q4_0_mmvq_packed_workspace()))
     gg, ug, hg = host(g), host(u), host(h)
     _gemv_check(wg[-1], st["xq"], M, gg, "gate")
     _gemv_check(wu[-1], st["xq"], M, ug, "up")
