@@ -53,6 +53,15 @@ int main(void)
     EXPECT(q4_0_mmvq_packed_split(A, 16, 512, A, 6, 9, A, NULL), BQ8_ERR_SHAPE);
     EXPECT(q4_0_gate_up_silu_q8_1_packed(A, A, 48, 512, A, 6, NULL, NULL, NULL, A, NULL),
            BQ8_ERR_SHAPE); /* N % 32 != 0 */
+    EXPECT(q4_0_gate_up_silu_q8_1_packed_ws(A, A, 64, 512, A, 6, NULL, NULL, NULL, A, NULL,
+                                            1 << 24, NULL),
+           BQ8_ERR_NULL);
+    EXPECT(q4_0_gate_up_silu_q8_1_packed_ws(A, A, 48, 512, A, 6, NULL, NULL, NULL, A, A, 1 << 24,
+                                            NULL),
+           BQ8_ERR_SHAPE);
+    EXPECT(q4_0_gate_up_silu_q8_1_packed_ws(A, A, 64, 512, A, 6, NULL, NULL, NULL, A,
+                                            (char *)A + 128, 1 << 24, NULL),
+           BQ8_ERR_ALIGN);
 
     /* Q6_K packs and the head */
     EXPECT(q6k_pack_bytes(248320, 5120), 1360793600);
