@@ -12,6 +12,7 @@
    unpinned: one requantization flip moves outputs by more than the
    tolerance.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -199,3 +200,44 @@ def test_packed_stream_full_shape_last_layer_stages():
     assert (oracle.q8_1_quantize(hg) == hq).all()
     assert (hq == st["hq"]).all()
     _gemv_check(wd[-1], st["hq"], M, host(y), "down")
+
+
+def test_packed_stream_stage_only_work_area_runs_unbalanced():
+    """A work area that holds the stages but not the workspace: the pass runs
+    the plain joint launch, and equals the composed calls made that way."""
+    # ffn a multiple of 512 (the packed down projection's K) with 16 more
+    # 32-column groups than CUs, so that the balanced pass cuts 16 groups
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    M, hidden, ffn, layers = 6, 512, 512 * (cus // 16 + 1), 2
+    say(f"packed stream, stage-only work area M={M} hidden={hidden} ffn={ffn}")
+    wg = [bq.q4_0_pack(synth.q4_0_weights_device(960 + 3 * l, ffn, hidden)) for l in range(layers)]
+    wu = [bq.q4_0_pack(synth.q4_0_weights_device(961 + 3 * l, ffn, hidden)) for l in range(layers)]
+    wd = [bq.q4_0_pack(synth.q4_0_weights_device(962 + 3 * l, hidden, ffn)) for l in range(layers)]
+    x0 = torch.from_numpy(synth.stream_x0(M, hidden, seed=79)).to(DEV)
+    total = bq.q4_0_ffn_stream_layout(M, hidden, ffn)["total"]
+    stages = total - (bq.q4_0_mmvq_packed_ws_bytes() + 255) // 256 * 256
+    work = torch.empty((stages,), dtype=torch.uint8, device=DEV)
+    y = torch.empty((M, hidden), dtype=torch.float32, device=DEV)
+    L = bq.lib()
+    st = L.q4_0_ffn_stream_packed(bq.stream_weight_table(wg), bq.stream_weight_table(wu),
+                                  bq.stream_weight_table(wd), layers, M, hidden, ffn,
+                                  x0.data_ptr(), ctypes.c_float(EPS), y.data_ptr(),
+                                  work.data_ptr(), stages,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    # composed with the plain joint launch
+    xq = bq.q8_1_quantize(x0)
+    P = bq.q4_0_mmvq_packed_splits(hidden, ffn)
+    parts = None
+    for l in range(layers):
+        if l > 0:
+            xq = bq.rms_norm_q8_1_sum(parts, EPS)
+        hq = bq.q4_0_gate_up_silu_q8_1_packed(wg[l], wu[l], ffn, hidden, xq, M)
+        parts = bq.q4_0_mmvq_packed_split(wd[l], hidden, ffn, hq, M, P)
+    y_ref = torch.empty_like(y)
+    bq.rms_norm_q8_1_sum(parts, EPS, y=y_ref, want_xq=False)
+    assert torch.equal(y, y_ref)
+    # and the balanced pass (full work area) differs only by rounding in the
+    # cut groups, which can move an h code by one step
+    y_bal, _ = bq.q4_0_ffn_stream(wg, wu, wd, x0, EPS, packed=True, ffn=ffn)
+    assert (y_bal - y).abs().max() <= 1e-3 * y.abs().max()
