@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROTATE = 12
+WARMUP_MIN_S = 0.3  # untimed steps before the timed region, at least this long
 PMC_RECORD = os.path.join(ROOT, "profiles", "pmc_q4_0_mmvq_packed_m6_ffn_up.json")
 PMC_RECORD_GATE_UP = os.path.join(ROOT, "profiles", "pmc_q4_0_gate_up_silu_q8_1_packed_m6_ffn.json")
 KERNEL_SOURCES = ["block_quantized_gemv_q8_amd/csrc/q4_0_packed.hip",
@@ -545,11 +546,20 @@ def main():
     s = setup_ffn_up(torch, bq, synth)
     N, K, M = s["N"], s["K"], s["M"]
     wbytes = q4_0_bytes(N, K)
-    for i in range(args.warmup):
-        step_packed(bq, s, i)
+    # untimed warm-up: --warmup steps, then more until WARMUP_MIN_S of wall
+    # time has passed (the first short region after a pause runs slow, and
+    # the driver's --warmup 5 is a few tens of microseconds)
+    warm_steps = 0
+    t0 = time.perf_counter()
+    while warm_steps < args.warmup or time.perf_counter() - t0 < WARMUP_MIN_S:
+        for _ in range(20):
+            step_packed(bq, s, warm_steps)
+            warm_steps += 1
+        if warm_steps % 200 == 0:
+            torch.cuda.synchronize()
     with Timer(torch) as t:
         for i in range(args.steps):
-            step_packed(bq, s, i)
+            step_packed(bq, s, warm_steps + i)
     step_us = t.ms * 1000.0 / args.steps
     value = wbytes / step_us / 1e3  # GB/s
     log(f"bench: step (quantize + packed M=6) {step_us:.3f} us, {value:.1f} GB/s")
@@ -663,6 +673,8 @@ def main():
             "N": N, "K": K, "M": M,
             "weight_bytes": wbytes,
             "step_us": round(step_us, 3),
+            "warmup_steps_run": warm_steps,
+            "warmup_min_s": WARMUP_MIN_S,
             "step_us_batches": stats_us(step_b),
             "product_launch": "q4_0_mmvq_packed_ws; at M <= 8 it runs every 16-row tile "
                               "whole (the q4_0_mmvq_packed launch)",

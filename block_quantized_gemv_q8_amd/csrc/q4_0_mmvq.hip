@@ -522,7 +522,7 @@ static bq8_status mmvq_launch(const void *w, int64_t N, int64_t K, const void *x
         N * (K / QK) * Q4_0_BYTES >= (int64_t(1) << 40) || K > (int64_t(1) << 26) ||
         (int64_t)M * K >= (int64_t(1) << 31))
         return BQ8_ERR_SHAPE;
-    if (!aligned(w, 16) || !aligned(xq, 4) || !aligned(y, 4))
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(y, 4))
         return BQ8_ERR_ALIGN;
     const int nb = (int)(K / QK);
     const bool al = (K % 256 == 0);

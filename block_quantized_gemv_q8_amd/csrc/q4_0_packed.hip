@@ -821,7 +821,7 @@ static bq8_status packed_product(const void *wp, int64_t N, int64_t K, const voi
         (int64_t)nsplit * M * N >= (int64_t(1) << 40) ||
         (int64_t)nsplit * ((N + PK_TILE - 1) / PK_TILE) >= (int64_t(1) << 31))
         return BQ8_ERR_SHAPE;
-    if (!aligned(wp, 16) || !aligned(xq, 4) || !aligned(y, 4) || !aligned(ws, 256))
+    if (!aligned(wp, 16) || !aligned(xq, 16) || !aligned(y, 4) || !aligned(ws, 256))
         return BQ8_ERR_ALIGN;
     int64_t cus = 0;
     if (ws) {
@@ -932,7 +932,7 @@ static bq8_status gate_up_product(const void *wg, const void *wu, int64_t N, int
     if (!packed_shape_ok(N, K) || N % (2 * PK_TILE) != 0 || M < 1 || M > 17 ||
         M * K >= (int64_t(1) << 31) || M * N >= (int64_t(1) << 31))
         return BQ8_ERR_SHAPE;
-    if (!aligned(wg, 16) || !aligned(wu, 16) || !aligned(xq, 4) || !aligned(hq, 4) ||
+    if (!aligned(wg, 16) || !aligned(wu, 16) || !aligned(xq, 16) || !aligned(hq, 4) ||
         (g && !aligned(g, 4)) || (u && !aligned(u, 4)) || (h && !aligned(h, 4)) ||
         !aligned(ws, 256))
         return BQ8_ERR_ALIGN;

@@ -101,7 +101,8 @@ bq8_status q8_1_quantize(const float *x, int64_t M, int64_t K, void *xq, void *s
  *   y[m][n] = sum_k W[n][k] * X[m][k]
  * with W the dequantized Q4_0 weight and X the dequantized Q8_1 rows.
  * w:  Q4_0 [N][K/32] blocks of 18 bytes, row-major, 16-byte aligned.
- * xq: Q8_1 [M][K/32] (from q8_1_quantize), 4-byte aligned.
+ * xq: Q8_1 [M][K/32] (from q8_1_quantize), 16-byte aligned (the kernels
+ *     copy it into LDS in 16-byte pieces).
  * y:  f32 [M][N] row-major, 4-byte aligned; fully overwritten.
  * Shape: 1 <= N < 2^31, 32 <= K <= 2^26, K % 32 == 0, N*K/32*18 < 2^40.
  * Each weight byte is read from memory once per call whatever M is.
@@ -209,7 +210,7 @@ int64_t q4_0_mmvq_packed_splits(int64_t N, int64_t K);
  *   h = g / (1 + exp(-g)) * u               (binary32, as silu_mul_q8_1)
  *   hq = Q8_1(h)                            (as silu_mul_q8_1)
  * wg, wu: q4_0_pack of the gate and up weights, each Q4_0 [N][K]; 16-byte
- *   aligned.  xq: Q8_1 [M][K/32], 4-byte aligned.  hq: Q8_1 [M][N/32],
+ *   aligned.  xq: Q8_1 [M][K/32], 16-byte aligned.  hq: Q8_1 [M][N/32],
  *   4-byte aligned, fully overwritten.  g, u, h: optional f32 [M][N]
  *   (NULL to skip), receive the gate and up products and h; hq does not
  *   depend on whether they are given.  hq is bitwise the Q8_1 of the h

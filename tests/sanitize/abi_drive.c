@@ -38,6 +38,7 @@ int main(void)
     EXPECT(q4_0_mmvq_m6(NULL, 8, 64, A, A, NULL), BQ8_ERR_NULL);
     EXPECT(q4_0_mmvq_m6(A, 8, 48, A, A, NULL), BQ8_ERR_SHAPE);
     EXPECT(q4_0_mmvq_m17(B + 4, 8, 64, A, A, NULL), BQ8_ERR_ALIGN);
+    EXPECT(q4_0_mmvq_m6(A, 8, 64, B + 4, A, NULL), BQ8_ERR_ALIGN); /* xq 4 mod 16 */
     EXPECT(q4_0_mmvq(A, 8, 64, A, 18, A, NULL), BQ8_ERR_SHAPE);
 
     /* packed layout */
@@ -45,6 +46,9 @@ int main(void)
     EXPECT(q4_0_pack_bytes(17408, 5000), -1);
     EXPECT(q4_0_pack(A, 16, 512, A, q4_0_pack_bytes(16, 512) - 1, NULL), BQ8_ERR_SIZE);
     EXPECT(q4_0_mmvq_packed(A, 16, 500, A, 6, A, NULL), BQ8_ERR_SHAPE);
+    EXPECT(q4_0_mmvq_packed(A, 16, 512, B + 8, 6, A, NULL), BQ8_ERR_ALIGN); /* xq 8 mod 16 */
+    EXPECT(q4_0_gate_up_silu_q8_1_packed(A, A, 64, 512, B + 4, 6, NULL, NULL, NULL, A, NULL),
+           BQ8_ERR_ALIGN);
     EXPECT(q4_0_mmvq_packed_ws(A, 16, 512, A, 6, A, NULL, 1 << 20, NULL), BQ8_ERR_NULL);
     EXPECT(q4_0_mmvq_packed_ws(A, 16, 500, A, 6, A, A, 1 << 20, NULL), BQ8_ERR_SHAPE);
     EXPECT(q4_0_mmvq_packed_ws(A, 16, 512, A, 6, A, (char *)A + 128, 1 << 20, NULL),

@@ -112,6 +112,7 @@ def test_mmvq_validation(L, m):
     assert f(A, 1 << 31, 64, A, A, None) == SHAPE
     assert f(A + 4, 8, 64, A, A, None) == ALIGN
     assert f(A, 8, 64, A + 2, A, None) == ALIGN
+    assert f(A, 8, 64, A + 4, A, None) == ALIGN   # xq: 16-byte pieces go to LDS
     assert f(A, 8, 64, A, A + 2, None) == ALIGN
 
 
@@ -238,6 +239,8 @@ def test_packed_q4_0_queries_and_validation(L):
     assert L.q4_0_mmvq_packed(A, 17408, 5376, A, 6, A, None) == SHAPE  # K % 512 != 0
     assert L.q4_0_mmvq_packed(A + 8, 17408, 5120, A, 6, A, None) == ALIGN
     assert L.q4_0_mmvq_packed(A, 17408, 5120, A + 2, 6, A, None) == ALIGN
+    assert L.q4_0_mmvq_packed(A, 17408, 5120, A + 4, 6, A, None) == ALIGN
+    assert L.q4_0_mmvq_packed(A, 17408, 5120, A + 8, 6, A, None) == ALIGN
     # the balanced launch: the same checks first, then its workspace's
     ws = 1 << 20
     assert L.q4_0_mmvq_packed_ws(A, 17408, 5120, A, 6, A, None, ws, None) == NULL
@@ -267,6 +270,7 @@ def test_gate_up_silu_validation(L):
     assert call(wg=A + 8) == ALIGN
     assert call(wu=A + 8) == ALIGN
     assert call(xq=A + 2) == ALIGN
+    assert call(xq=A + 4) == ALIGN
     assert call(hq=A + 2) == ALIGN
     assert call(g=A + 2) == ALIGN
     assert call(u=A + 1) == ALIGN

@@ -130,10 +130,11 @@ def _cus():
 def _ws_shapes():
     c = _cus()
     return [(6, 64, 512), (17, 1024, 1536), (6, 32 * (c + 37), 2048), (9, 32 * (c + 5), 4608),
-            (1, 32 * (2 * c + 3), 1024)]
+            (1, 32 * (2 * c + 3), 1024), (12, 32 * (c + 11), 1024), (4, 32 * (c + 7), 512),
+            (14, 32 * (2 * c + 1), 512)]
 
 
-@pytest.mark.parametrize("case", range(5))
+@pytest.mark.parametrize("case", range(8))
 def test_gate_up_silu_ws(case):
     M, N, K = _ws_shapes()[case]
     say(f"gate_up_silu_ws M={M} N={N} K={K}")
@@ -142,7 +143,7 @@ def test_gate_up_silu_ws(case):
     _check_ws(wg, wu, x, N, K, M)
 
 
-@pytest.mark.parametrize("M", [6, 17])
+@pytest.mark.parametrize("M", [1, 3, 6, 9, 12, 16, 17])
 def test_gate_up_silu_ws_full_ffn_shape(M):
     N, K = synth.FFN_UP["N"], synth.FFN_UP["K"]
     say(f"gate_up_silu_ws full ffn shape M={M}")

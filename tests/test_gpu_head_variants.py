@@ -23,6 +23,7 @@ if not torch.cuda.is_available():
 
 import oracle  # noqa: E402
 import block_quantized_gemv_q8_amd as bq  # noqa: E402
+from idcheck import check_ids  # noqa: E402
 from block_quantized_gemv_q8_amd import synth  # noqa: E402
 
 DEV = "cuda:0"
@@ -40,16 +41,6 @@ def dev(a):
 def host(t):
     torch.cuda.synchronize()
     return t.cpu().numpy()
-
-
-def check_ids(gpu_ids, ref_ids, logits, bound):
-    for r, (g, o) in enumerate(zip(gpu_ids, ref_ids)):
-        if g == o:
-            continue
-        assert 0 <= g < logits.shape[1], f"row {r}: id {g} out of range"
-        gap = logits[r, o] - logits[r, g]
-        tol = REL * (bound[r, o] + bound[r, g]) + 2 * ABS
-        assert gap <= tol, f"row {r}: gpu {g} oracle {o} gap {gap} > {tol}"
 
 
 def check_candidate_max(pack_d, N, K, x, row0, rows, cand, logits, bound, oid, compact=False):

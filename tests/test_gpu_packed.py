@@ -234,7 +234,8 @@ def test_rms_norm_q8_1_sum(P, M, K):
 # sums meet in the workspace (M <= 8: no tile is cut).  Outputs of the other tiles are bitwise the plain
 # launch's; the cut tiles' are within the oracle's tolerance; results repeat
 # bit for bit.  Shapes: fewer tiles than CUs (every tile cut), a remainder
-# with a ragged last tile, the full ffn_up and down shapes.  One workspace
+# with a ragged last tile, the full ffn_up and down shapes, every M = 1..17
+# (the bench times the M = 12 launch at the down shape).  One workspace
 # serves every shape and M in turn, and its counters are back at zero after
 # each call.
 WS_SMALL = [(1, 512), (37, 1024), (150, 1024), (4097, 1024), (6000, 5120)]
@@ -264,7 +265,7 @@ def test_mmvq_packed_ws_small():
         xq = oracle.q8_1_quantize(x)
         ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
         wp, xqd = bq.q4_0_pack(dev(w)), dev(xq)
-        for m in (1, 2, 6, 8, 9, 17):
+        for m in range(1, 18):
             r0 = _whole_rows(N, m)
             say(f"q4_0_mmvq_packed_ws N={N} K={K} M={m} (rows {r0}.. cut into K ranges)")
             plain = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
@@ -286,7 +287,7 @@ def test_mmvq_packed_ws_full(N, K):
     xqd = bq.q8_1_quantize(torch.randn((17, K), device=DEV))
     xq = host(xqd)
     ref, bound = oracle.q4_0_gemv(w_cut, N - r0, K, xq, 17)
-    for m in (1, 6, 9, 17):
+    for m in range(1, 18):
         say(f"q4_0_mmvq_packed_ws full N={N} K={K} M={m} (rows {r0}.. cut)")
         plain = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
         yw = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m, ws=ws))

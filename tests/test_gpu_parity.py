@@ -4,7 +4,7 @@ Bars: Q8_1 bytes, expanded packs and top-1 ids bit-exact; float outputs
 |gpu - oracle| <= 1e-5 * sum_b |t_b| + 1e-6 with t_b the 32-block
 contributions (the oracle returns that sum as `bound`); top-1 ids equal the
 oracle's unless the oracle's gap between the two candidates is within the
-two rows' tolerances and the rows differ.  Shapes span several tiles, a
+float bound of one logit and the rows differ (tests/idcheck.py).  Shapes span several tiles, a
 ragged tail, the unaligned-K path and the full workloads.
 """
 import sys
@@ -19,6 +19,7 @@ if not torch.cuda.is_available():
 
 import oracle  # noqa: E402
 import block_quantized_gemv_q8_amd as bq  # noqa: E402
+from idcheck import check_ids  # noqa: E402
 from block_quantized_gemv_q8_amd import synth  # noqa: E402
 
 DEV = "cuda:0"
@@ -48,18 +49,6 @@ def assert_close(gpu, ref, bound, what):
                              f"{tuple(i)}: gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r} "
                              f"tol={tol[tuple(i)]!r}")
     return float((err / tol).max())
-
-
-def check_ids(gpu_ids, ref_ids, logits, bound, pack_rows_equal=None):
-    for r, (g, o) in enumerate(zip(gpu_ids, ref_ids)):
-        if g == o:
-            continue
-        assert 0 <= g < logits.shape[1], f"row {r}: id {g} out of range"
-        gap = logits[r, o] - logits[r, g]
-        tol = REL * (bound[r, o] + bound[r, g]) + 2 * ABS
-        assert gap <= tol, f"row {r}: gpu {g} oracle {o} gap {gap} > {tol}"
-        if pack_rows_equal is not None:
-            assert not pack_rows_equal(g, o), f"row {r}: equal weight rows must give the lower id"
 
 
 # ------------------------------------------------------------------ Q8_1
@@ -288,6 +277,67 @@ def test_top1_lm_head_full(lm_head_full):
     again = [host(bq.q6k_lmhead_top1(f["packd"], N, K, xd, 1, 5)) for _ in range(2)]
     assert all((a == ids).all() for a in again)
     f["logits"], f["bound"] = logits, bound
+
+
+def _round256(n):
+    return (n + 255) // 256 * 256
+
+
+def _check_head_rows(scratch, x_rows, K, compact, what):
+    """The head's own Q8_1 rows, read from the scratch layout its quantize
+    step writes (areas start on 256-byte boundaries): the quants int8
+    [K/32][R][32] at 0; each block's d as binary32 [K/32][R] (the fp16 d,
+    widened exactly) at round256(R*K); on the compact pack, -32 x the sum of
+    each 16-value half's quants, int32 [K/32][R][2], after that.  All bit
+    for bit the oracle's Q8_1 of the same rows."""
+    R, nb = x_rows.shape[0], K // 32
+    ref = oracle.q8_1_quantize(x_rows).reshape(R, nb, 36)
+    rq = ref[:, :, 4:].view(np.int8)
+    s = host(scratch)
+    q = s[:R * K].view(np.int8).reshape(nb, R, 32).transpose(1, 0, 2)
+    assert np.array_equal(q, rq), f"{what}: quants differ from the oracle's"
+    off = _round256(R * K)
+    dx = s[off:off + R * nb * 4].view(np.float32).reshape(nb, R).T
+    d16 = np.ascontiguousarray(ref[:, :, 0:2]).view(np.float16).reshape(R, nb)
+    assert np.array_equal(dx.view(np.uint32), d16.astype(np.float32).view(np.uint32)), \
+        f"{what}: scales differ from the oracle's"
+    if compact:
+        off += _round256(R * nb * 4)
+        sx = s[off:off + R * nb * 8].view(np.int32).reshape(nb, R, 2).transpose(1, 0, 2)
+        want = -32 * rq.astype(np.int64).reshape(R, nb, 2, 16).sum(axis=3)
+        assert np.array_equal(sx, want), f"{what}: half sums differ from the oracle's"
+
+
+@pytest.mark.parametrize("N,K,row0,rows", [(300, 512, 1, 5), (64, 256, 0, 8), (1000, 1280, 2, 3)])
+def test_top1_head_rows_q8_1_bitexact_small(N, K, row0, rows):
+    rng = np.random.default_rng(330 + N + rows)
+    raw = synth.q6k_raw_weights(rng, N, K)
+    x = synth.normal_rows(rng, row0 + rows, K)
+    x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20
+    x[row0, 32:64] = 0.0                       # an all-zero block: d = 0, quants 0
+    x[row0 + rows - 1, 0:32] = 2.5             # a constant block: every quant 127
+    xd = dev(x)
+    for compact in (False, True):
+        pack = (bq.q6k_pack_compact if compact else bq.q6k_pack_expand)(dev(raw), N, K)
+        scratch = torch.full((bq.q6k_lmhead_top1_scratch_bytes(N, K, rows),), 0xA5,
+                             dtype=torch.uint8, device=DEV)
+        say(f"head rows Q8_1 N={N} K={K} rows {row0}..{row0 + rows - 1} compact={compact}")
+        bq.q6k_lmhead_top1(pack, N, K, xd, row0, rows, scratch=scratch, compact=compact)
+        _check_head_rows(scratch, x[row0:row0 + rows], K, compact, f"N{N} K{K}")
+
+
+def test_top1_head_rows_q8_1_bitexact_lm_head(lm_head_full):
+    f = lm_head_full
+    N, K, x = f["N"], f["K"], f["x"]
+    xd = dev(x)
+    cpk = bq.q6k_pack_compact(f["rawd"], N, K)
+    for row0, rows in ((1, 5), (0, 6)):
+        for compact, pack in ((False, f["packd"]), (True, cpk)):
+            scratch = torch.full((bq.q6k_lmhead_top1_scratch_bytes(N, K, rows),), 0xA5,
+                                 dtype=torch.uint8, device=DEV)
+            say(f"lm_head rows Q8_1 rows {row0}..{row0 + rows - 1} compact={compact}")
+            bq.q6k_lmhead_top1(pack, N, K, xd, row0, rows, scratch=scratch, compact=compact)
+            _check_head_rows(scratch, x[row0:row0 + rows], K, compact, "lm_head")
 
 
 TILE_PAIRS = [(63, 64), (1023, 1024), (65535, 65536), (131071, 131072), (248318, 248319)]

@@ -32,6 +32,7 @@ if not torch.cuda.is_available():
 
 import oracle  # noqa: E402
 import block_quantized_gemv_q8_amd as bq  # noqa: E402
+from idcheck import check_ids  # noqa: E402
 from block_quantized_gemv_q8_amd import synth  # noqa: E402
 
 DEV = "cuda:0"
@@ -102,11 +103,7 @@ def test_lm_head_vocab_shard():
                                     compact=True))
     say(f"shard ids gpu {list(ids_e)} oracle {list(oid)}")
     assert (ids_c == ids_e).all()
-    for r, (g, o) in enumerate(zip(ids_e, oid)):
-        if g != o:
-            assert 0 <= g < N
-            gap = logits[r, o] - logits[r, g]
-            assert gap <= REL * (bound[r, o] + bound[r, g]) + 2 * ABS, (r, g, o, gap)
+    check_ids(ids_e, oid, logits, bound, f"vocabulary rows {N}")
 
 
 @pytest.mark.parametrize("nbytes", [16, 1024 * 1024 + 48, synth.FFN_UP["N"] * 160 * 18])
@@ -141,8 +138,4 @@ def test_lm_head_split_widths(N):
     say(f"ids gpu {list(ids_e)} oracle {list(oid)}")
     assert (ids_c == ids_e).all()
     assert (ids_e != N - 1).all()
-    for r, (g, o) in enumerate(zip(ids_e, oid)):
-        if g != o:
-            assert 0 <= g < N
-            gap = logits[r, o] - logits[r, g]
-            assert gap <= REL * (bound[r, o] + bound[r, g]) + 2 * ABS, (r, g, o, gap)
+    check_ids(ids_e, oid, logits, bound, f"vocabulary rows {N}")

@@ -4,7 +4,8 @@
    bit for bit (same kernels, fixed reduction orders), on small shapes that
    take both the MFMA path (K % 256 == 0) and the dot4 path, at several M.
 2. At the full stream shape (64 layers of gate/up [5120 -> 17408] and down
-   [17408 -> 5120], M = 6), every stage of the last layer is checked against
+   [17408 -> 5120], M = 6), on both weight layouts, every stage of the last
+   layer is checked against
    the oracle given the GPU's own input to that stage: the RMS step and the
    two SiLU*up and Q8_1 steps to |d| <= 1e-5 |ref| + 1e-6 with the quantized
    bytes bit-exact given the GPU's f32 values, and the three projections to
@@ -168,13 +169,22 @@ def test_packed_stream_equals_composed_calls(M, hidden, ffn, layers):
 
 
 def test_packed_stream_full_shape_last_layer_stages():
+    """The packed pass the bench times: all 64 full-shape layers."""
     cfg = synth.STREAM
-    L, M, H, F = 8, cfg["M"], cfg["hidden"], cfg["ffn"]   # the full layer shape, 8 layers
-    say(f"packed stream: {L} full-shape layers")
-    wg, wu, wd = synth.stream_weights_device(L, H, F)
-    pg = [bq.q4_0_pack(w) for w in wg]
-    pu = [bq.q4_0_pack(w) for w in wu]
-    pd = [bq.q4_0_pack(w) for w in wd]
+    L, M, H, F = cfg["layers"], cfg["M"], cfg["hidden"], cfg["ffn"]
+    say(f"packed stream: {L} full-shape layers, generated and packed on the device")
+    pg, pu, pd = [], [], []
+    for l in range(L):
+        # pack layer by layer; only the last layer's standard-layout weights
+        # are kept (the oracle reads them)
+        wl = [synth.q4_0_weights_device(synth.stream_layer_seed(l, k), n, kk)
+              for k, n, kk in (("gate", F, H), ("up", F, H), ("down", H, F))]
+        pg.append(bq.q4_0_pack(wl[0]))
+        pu.append(bq.q4_0_pack(wl[1]))
+        pd.append(bq.q4_0_pack(wl[2]))
+        if l == L - 1:
+            wg, wu, wd = [wl[0]], [wl[1]], [wl[2]]
+        del wl
     x0 = torch.from_numpy(synth.stream_x0()).to(DEV)
     y_prev, _ = bq.q4_0_ffn_stream(pg[:-1], pu[:-1], pd[:-1], x0, EPS, packed=True, ffn=F)
     y_prev = y_prev.clone()
