@@ -10,6 +10,7 @@ _API_NAMES = {
     "Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "q4_0_mmvq",
     *[f"q4_0_mmvq_m{m}" for m in range(1, 18)], "q6k_pack_bytes", "q6k_pack_expand",
     "q6k_lmhead_top1_scratch_bytes", "q6k_lmhead_top1", "q6k_lmhead_candidate_max",
+    "q6k_lmhead_top1_noalloc",
     "q6k_compact_bytes", "q6k_pack_compact",
     "silu_mul_q8_1", "rms_norm_q8_1",
     "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed", "q4_0_mmvq_packed_ws_bytes",

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.q6k_lmhead_top1_scratch_bytes.argtypes = [_I64, _I64, _I64]
         L.q6k_lmhead_top1.restype = _ST
         L.q6k_lmhead_top1.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P, _P, _I64, _P]
+        L.q6k_lmhead_top1_noalloc.restype = _ST
+        L.q6k_lmhead_top1_noalloc.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P, _P]
         L.q6k_lmhead_candidate_max.restype = _ST
         L.q6k_lmhead_candidate_max.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _I64, _P, _I64,
                                                _P, _P, _P, _P, _I64, _P]
@@ -256,6 +258,20 @@ def q6k_lmhead_top1(pack: torch.Tensor, N: int, K: int, x: torch.Tensor, row0: i
         _dev(pack, "pack", torch.uint8), N, K, _dev(x, "x", torch.float32), M, row0, rows,
         _dev(ids, "ids", torch.int32), _dev(scratch, "scratch", torch.uint8), scratch.numel(),
         _stream()))
+    return ids
+
+
+def q6k_lmhead_top1_noalloc(pack: torch.Tensor, N: int, K: int, x: torch.Tensor, row0: int,
+                            rows: int, ids: torch.Tensor | None = None):
+    """q6k_lmhead_top1 on the expanded pack with the library's own per-GPU
+    scratch: nothing is allocated on the device but ids when not given."""
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [M][K]")
+    ids = _out(ids, (rows,), torch.int32, x.device, "ids")
+    _check("q6k_lmhead_top1_noalloc", lib().q6k_lmhead_top1_noalloc(
+        _dev(pack, "pack", torch.uint8), N, K, _dev(x, "x", torch.float32), M, row0, rows,
+        _dev(ids, "ids", torch.int32), _stream()))
     return ids
 
 

@@ -55,6 +55,8 @@
 // "Memory and startup": the expanded pack is kept beside the raw weights.
 #include "bq8_dev.h"
 
+#include <atomic>
+
 namespace bq8 {
 
 // ------------------------------------------------------------- expansion
@@ -816,6 +818,56 @@ BQ8_EXPORT bq8_status q6k_lmhead_candidate_max_compact(const void *pack, int64_t
 {
     return candidate_max(pack, true, N, K, x, M, row0, rows, cand_ids, ncand, ids, top_vals,
                          cand_scores, scratch, scratch_bytes, stream);
+}
+
+// ------------------------------------------------- allocation-free head
+namespace bq8 {
+namespace noalloc {
+// The scratch of q6k_lmhead_top1_noalloc.  Each GPU the library runs on has
+// its own copy, held until the process ends.  On the host this name is only
+// a stand-in: host code uses the device address noalloc_scratch() looks up.
+static __device__ __align__(256) uint8_t scratch[BQ8_TOP1_NOALLOC_SCRATCH_BYTES];
+} // namespace noalloc
+
+// This GPU's address of noalloc::scratch, looked up once per device with that
+// device current (hipGetSymbolAddress); nullptr if the runtime refuses.
+static void *noalloc_scratch()
+{
+    static std::atomic<void *> addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc::scratch)) != hipSuccess || !p)
+            return nullptr;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+} // namespace bq8
+
+BQ8_EXPORT bq8_status q6k_lmhead_top1_noalloc(const void *pack, int64_t N, int64_t K,
+                                              const float *x, int64_t M, int64_t row0,
+                                              int64_t rows, int32_t *ids, void *stream)
+{
+    if (!pack || !x || !ids)
+        return BQ8_ERR_NULL;
+    if (!top1_shape_ok(N, K) || rows < 1 || rows > TOP1_MAX_ROWS || M < 1 || row0 < 0 ||
+        row0 + rows > M || M * K >= (int64_t(1) << 31))
+        return BQ8_ERR_SHAPE;
+    if (!aligned(pack, 16) || !aligned(x, 4) || !aligned(ids, 4))
+        return BQ8_ERR_ALIGN;
+    if (q6k_lmhead_top1_scratch_bytes(N, K, rows) > BQ8_TOP1_NOALLOC_SCRATCH_BYTES)
+        return BQ8_ERR_SIZE;
+    void *scr = noalloc_scratch();
+    if (!scr)
+        return BQ8_ERR_HIP;
+    // every area of the scratch is written before it is read within the
+    // call (quantized rows by the first kernel, one key per workgroup by the
+    // second), so nothing needs clearing
+    return lmhead_run(pack, false, N, K, x, row0, rows, nullptr, 0, ids, nullptr, nullptr, scr,
+                      (hipStream_t)stream);
 }
 
 BQ8_EXPORT const char *bq8_status_string(bq8_status status)

@@ -285,6 +285,26 @@ bq8_status q6k_lmhead_top1(const void *pack, int64_t N, int64_t K, const float *
                            int64_t scratch_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * q6k_lmhead_top1 without a scratch argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The call allocates nothing: its
+ * scratch is a device array inside the library, one per GPU, of
+ * BQ8_TOP1_NOALLOC_SCRATCH_BYTES (256 KiB), held by each GPU the library runs
+ * on until the process ends.  Arguments, results and errors are those of
+ * q6k_lmhead_top1, plus:
+ *   q6k_lmhead_top1_scratch_bytes(N, K, rows) > BQ8_TOP1_NOALLOC_SCRATCH_BYTES
+ *     -> BQ8_ERR_SIZE (K <= 16384 always fits, at any N and rows <= 8);
+ *   the device address of the array could not be obtained -> BQ8_ERR_HIP.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, no ordering between them) race and must not be
+ * issued.  The array's contents on entry do not matter.
+ * ---------------------------------------------------------------------- */
+#define BQ8_TOP1_NOALLOC_SCRATCH_BYTES 262144
+bq8_status q6k_lmhead_top1_noalloc(const void *pack, int64_t N, int64_t K, const float *x,
+                                   int64_t M, int64_t row0, int64_t rows, int32_t *ids,
+                                   void *stream);
+
+/* ------------------------------------------------------------------------
  * The same fused head with the outputs target-verified speculation needs
  * ("Qwen3.6 27B AutoRound Handoff", "Current next-execution plan": a
  * candidate-max head gives the true top ids and values plus per-row

@@ -79,6 +79,9 @@ int main(void)
     EXPECT(q6k_lmhead_top1_compact(A, 248320, 5000, A, 6, 1, 5, A, A, sb, NULL), BQ8_ERR_SHAPE);
     EXPECT(q6k_lmhead_candidate_max(A, 248320, 5120, A, 6, 1, 5, NULL, 1, A, A, A, A, sb, NULL),
            BQ8_ERR_NULL); /* candidates asked for, no id array */
+    EXPECT(q6k_lmhead_top1_noalloc(A, 248320, 5120, A, 6, 1, 5, NULL, NULL), BQ8_ERR_NULL);
+    EXPECT(q6k_lmhead_top1_noalloc(A, 248320, 5120, A, 6, 2, 5, A, NULL), BQ8_ERR_SHAPE);
+    EXPECT(q6k_lmhead_top1_noalloc(A, 248320, 24576, A, 9, 1, 8, A, NULL), BQ8_ERR_SIZE);
 
     /* glue and the summed RMS step */
     EXPECT(silu_mul_q8_1(A, A, 6, 48, NULL, A, NULL), BQ8_ERR_SHAPE);

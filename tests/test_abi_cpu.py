@@ -41,7 +41,7 @@ def test_header_declares_expected_entry_points():
               "q6k_lmhead_candidate_max", "q6k_compact_bytes", "q6k_pack_compact",
               "q6k_lmhead_top1_compact", "q6k_lmhead_candidate_max_compact",
               "bq8_hbm_read_probe", "q4_0_mmvq_packed_ws", "q4_0_mmvq_packed_ws_bytes",
-              "q4_0_gate_up_silu_q8_1_packed_ws"]:
+              "q4_0_gate_up_silu_q8_1_packed_ws", "q6k_lmhead_top1_noalloc"]:
         assert n in names
 
 
@@ -157,6 +157,36 @@ def test_top1_validation(L):
     assert call(x=A + 2) == ALIGN
     assert call(scratch=A + 8) == ALIGN
     assert call(sb=s - 1) == SIZE
+
+
+NOALLOC_MAX = 262144   # BQ8_TOP1_NOALLOC_SCRATCH_BYTES
+
+
+def test_top1_noalloc_validation(L):
+    """The allocation-free head checks what q6k_lmhead_top1 checks, then that
+    the shape's scratch fits its built-in array -- all before any HIP call."""
+    args = dict(pack=A, N=248320, K=5120, x=A, M=6, row0=1, rows=5, ids=A)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.q6k_lmhead_top1_noalloc(a["pack"], a["N"], a["K"], a["x"], a["M"], a["row0"],
+                                         a["rows"], a["ids"], None)
+
+    assert call(pack=None) == NULL
+    assert call(x=None) == NULL
+    assert call(ids=None) == NULL
+    assert call(K=5000) == SHAPE
+    assert call(rows=9, M=12) == SHAPE
+    assert call(row0=2) == SHAPE
+    assert call(pack=A + 4) == ALIGN
+    assert call(x=A + 2) == ALIGN
+    assert call(ids=A + 2) == ALIGN
+    # the hot shape needs 72 KiB; K = 16384 fits at rows 8 and any N; eight
+    # rows at K = 24576 need more than the array whatever N is
+    assert L.q6k_lmhead_top1_scratch_bytes(248320, 5120, 5) <= NOALLOC_MAX
+    assert L.q6k_lmhead_top1_scratch_bytes(2 ** 31 - 2, 16384, 8) <= NOALLOC_MAX
+    assert L.q6k_lmhead_top1_scratch_bytes(1, 24576, 8) > NOALLOC_MAX
+    assert call(K=24576, M=9, rows=8) == SIZE
 
 
 def test_layer_glue_validation(L):
