@@ -404,13 +404,15 @@ __device__ __forceinline__ void pk_range_sum2(const float *p, const float *q, si
 // KIND fixes at compile time what a workgroup has to decide, since every
 // instruction before a wave's first load delays the whole stream.  With
 // N % 16 == 0 every tile is full and the chunk strides are constants
-// (PK_FULL_WHOLE: workgroup b is tile b; PK_FULL_SPLIT: the split launch;
-// PK_FULL_CUT: whole tiles then the cut ones).  PK_ANY decides all of it at
-// run time, for a ragged last tile.  Measured against PK_ANY on full tiles
-// (same process, interleaved): ffn_up M = 6 10.7 against 11.2 us, M = 1
-// 10.3 against 10.6 us; down split M = 6 11.4 against 11.6 us.  The results
-// are bitwise those of PK_ANY: only address arithmetic differs.
-enum { PK_ANY = 0, PK_FULL_WHOLE = 1, PK_FULL_SPLIT = 2, PK_FULL_CUT = 3 };
+// (PK_FULL_WHOLE: workgroup b is tile b; PK_FULL_SPLIT: the split launch).
+// PK_ANY decides all of it at run time: a ragged last tile, the cut
+// launch, and every launch at M >= 9.  Measured against PK_ANY (two builds
+// in one process, interleaved), ffn_up: M = 1 / 6 / 8 10.29 / 10.66 / 10.97
+// against 10.42 / 11.13 / 11.28 us; down, 4 K ranges: M = 1 10.59 against
+// 10.74 us.  At M >= 9 the specialized kernels were slower (ffn_up M = 17
+// 19.24 against 18.30 us), so those stay general.  The results are bitwise
+// those of PK_ANY: only address arithmetic differs.
+enum { PK_ANY = 0, PK_FULL_WHOLE = 1, PK_FULL_SPLIT = 2 };
 
 template <int M, int KIND>
 __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
         c0 = p * nch / nsplit;
         c1 = (p + 1) * nch / nsplit;
         y += (size_t)p * M * N;
-    } else if (KIND == PK_FULL_CUT || KIND == PK_ANY) {
+    } else if (KIND == PK_ANY) {
         if ((int)blockIdx.x >= whole) {
             j = blockIdx.x - whole;
             const int p = j % P;
@@ -759,15 +761,12 @@ static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const v
                            ws_count);
         return launch_status();
     };
-    if (N % PK_TILE != 0)
-        return launch(q4_0_mmvq_packed_kernel<M, PK_ANY>);
-    if (nsplit > 1)
-        return launch(q4_0_mmvq_packed_kernel<M, PK_FULL_SPLIT>);
-    if constexpr (M >= 9) {
-        if (whole < tiles)
-            return launch(q4_0_mmvq_packed_kernel<M, PK_FULL_CUT>);
+    if constexpr (M <= 8) {
+        if (N % PK_TILE == 0)
+            return nsplit > 1 ? launch(q4_0_mmvq_packed_kernel<M, PK_FULL_SPLIT>)
+                              : launch(q4_0_mmvq_packed_kernel<M, PK_FULL_WHOLE>);
     }
-    return launch(q4_0_mmvq_packed_kernel<M, PK_FULL_WHOLE>);
+    return launch(q4_0_mmvq_packed_kernel<M, PK_ANY>);
 }
 
 // Waves per gate/up workgroup: about 2176 waves in flight for M >= 3 and
