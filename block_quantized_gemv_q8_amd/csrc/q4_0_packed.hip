@@ -99,9 +99,19 @@ __global__ __launch_bounds__(256) void q4_0_pack_kernel(const uint8_t *__restric
 // activation row m = c16%8 (+8s) for block c16/8, zero outside its block's k
 // range (lanes outside it read a zeroed LDS row).  Results are 16x the exact
 // dots (scaled by 1/16 at the end, exact).
+//
+// Which activation row an A row holds: MFMA s of a block pair covers rows
+// 2X*s .. 2X*s + 2X - 1 of each block, X = ceil(M / (2*MS)) of them per
+// 4-row group.  A row c16 (group g = c16/4 = 2*block + h, position
+// x = c16%4) holds row m = 2X*s + X*h + x when x < X (pk_row), and output
+// lane l keeps that row's sum in acc[..][s][x] for its h = (l/16)%2.  With
+// X < 4 the positions x >= X are never formed (M = 6: X = 3; M = 1, 2:
+// X = 1; M = 17: X = 3 in 3 MFMAs instead of 4 positions); M = 8 and 16 give
+// the plain m = 8s + 4h + x.  Which row sits where does not change any sum.
 template <int M>
 struct PkShape {
     static constexpr int MS = (M + 7) / 8;
+    static constexpr int X = (M + 2 * MS - 1) / (2 * MS);    // rows per 4-row group
     static constexpr int XRUN = PK_CB * Q8_1_BYTES;          // activation bytes per row per chunk
     static constexpr int XPIECES = M * XRUN / 16;
     static constexpr int LOADS = (XPIECES + WAVE - 1) / WAVE; // DMA instructions per chunk
@@ -111,6 +121,19 @@ struct PkShape {
     static constexpr int WAVE_LDS = ZOFF + XRUN;
 };
 
+// Activation row of (MFMA s, 4-row group half h, position x); it exists when
+// x < X and the row is below M.
+template <int M>
+__device__ __forceinline__ int pk_row(int s, int h, int x)
+{
+    return 2 * PkShape<M>::X * s + PkShape<M>::X * h + x;
+}
+template <int M>
+__device__ __forceinline__ bool pk_row_ok(int s, int h, int x)
+{
+    return x < PkShape<M>::X && pk_row<M>(s, h, x) < M;
+}
+
 // The main loop shared by the products: this wave's partial sums over its
 // chunks for NT 16-row tiles that read the same activation rows.  Tile i's
 // packed nibbles start at tile[i], its scales at dtile[i]; every tile has
@@ -119,7 +142,7 @@ struct PkShape {
 // c).  The wave sums chunks c0 + wave, c0 + wave + S, ... below c0 + nc.  The activations are staged once per chunk and each A operand feeds NT
 // MFMAs.  ring is this wave's LDS (at least PkShape<M>::WAVE_LDS bytes).
 // acc[i][s][x] of lanes l and l + 32 are the two blocks' shares of the sum
-// for weight row l%16 of tile i and activation row 8s + 4*(l/16) + x, 16x
+// for weight row l%16 of tile i and activation row pk_row(s, (l/16)%2, x), 16x
 // the exact value.
 template <int M, int NT>
 __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
@@ -146,8 +169,9 @@ __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
     uint32_t aoff[MS];
 #pragma unroll
     for (int s = 0; s < MS; ++s) {
-        const int m = 8 * s + (c16 & 7);
-        a_on[s] = ((c16 >> 3) == hb) && (m < M);
+        const int ha = (c16 >> 2) & 1, xa = c16 & 3;
+        const int m = pk_row<M>(s, ha, xa);
+        a_on[s] = ((c16 >> 3) == hb) && pk_row_ok<M>(s, ha, xa);
         aoff[s] = (uint32_t)(a_on[s] ? m : 0) * SH::XRUN;
     }
     // Addresses are a uniform per-chunk base (scalar registers) plus a fixed
@@ -210,10 +234,13 @@ __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
         // d_x of the chunk's blocks as f32: dxs[b*8*MS + m], 0 past M
 #pragma unroll
         for (int i = lane; i < PK_CB * 8 * MS; i += WAVE) {
-            const int b = i / (8 * MS), m = i - (i / (8 * MS)) * (8 * MS);
+            // entry 8s + 4h + x of block b: d of row pk_row(s, h, x)
+            const int b = i / (8 * MS), j = i - (i / (8 * MS)) * (8 * MS);
+            const int sj = j >> 3, hj = (j >> 2) & 1, xj = j & 3;
+            const bool ok = pk_row_ok<M>(sj, hj, xj);
             const uint16_t bits = *reinterpret_cast<const uint16_t *>(
-                stage + (m < M ? m : 0) * SH::XRUN + b * Q8_1_BYTES);
-            dxs[i] = (m < M) ? h2f(bits) : 0.0f;
+                stage + (ok ? pk_row<M>(sj, hj, xj) : 0) * SH::XRUN + b * Q8_1_BYTES);
+            dxs[i] = ok ? h2f(bits) : 0.0f;
         }
         // per-lane parts of the LDS addresses, folded once per chunk: block
         // offset 36*hb, element half 16*h past the 4 header bytes
@@ -264,7 +291,7 @@ __device__ __forceinline__ void pk_accumulate(const uint8_t *const (&tile)[NT],
 #pragma unroll
                 for (int s = 0; s < MS; ++s)
 #pragma unroll
-                    for (int x = 0; x < 4; ++x)
+                    for (int x = 0; x < SH::X; ++x)
                         acc[i][s][x] = fmaf((float)Dm[i][s][x], dw * dx[s][x], acc[i][s][x]);
             }
         }
@@ -456,7 +483,8 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
                         c0, c1 - c0, xq, smem + (size_t)wave * STRIDE, acc);
     pk_store_partials<1, MS>(acc, smem + (size_t)wave * STRIDE, lane);
     __syncthreads();
-    // output (slot, l): activation row 8s + 4*(l/16) + x, weight row n0 + l%16
+    // output (slot, l), slot = 4s + x: activation row pk_row(s, l/16, x),
+    // weight row n0 + l%16
     auto wave_sum = [&](int idx) {
         const int slot = idx >> 5, l = idx & 31;
         float sacc = 0.0f;
@@ -466,9 +494,9 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
     };
     auto store_y = [&](int idx, float sacc) {
         const int slot = idx >> 5, l = idx & 31;
-        const int m = 8 * (slot >> 2) + 4 * (l >> 4) + (slot & 3);
+        const int m = pk_row<M>(slot >> 2, l >> 4, slot & 3);
         const int nn = n0 + (l & 15);
-        if (m < M && nn < N)
+        if (pk_row_ok<M>(slot >> 2, l >> 4, slot & 3) && nn < N)
             y[(size_t)m * N + nn] = sacc * 0.0625f;
     };
     if (KIND == PK_FULL_WHOLE || KIND == PK_FULL_SPLIT || j < 0) {
@@ -512,8 +540,11 @@ __device__ __forceinline__ void gate_up_epilogue(Sum sum, int N, int n0, int grp
         const int m = m0 + (int)(threadIdx.x >> 5);
         const bool valid = m < M;
         const int mc = valid ? m : M - 1;
-        const int slot = (mc >> 3) * 4 + (mc & 3);
-        const int l = 16 * ((mc >> 2) & 1) + (c & 15);
+        // the accumulator position of row mc (pk_row inverted)
+        constexpr int X = PkShape<M>::X;
+        const int sm = mc / (2 * X), hm = (mc - 2 * X * sm) / X, xm = mc - 2 * X * sm - X * hm;
+        const int slot = sm * 4 + xm;
+        const int l = 16 * hm + (c & 15);
         float sg, su;
         sum(half, slot, l, sg, su);
         const float gv = sg * 0.0625f, uv = su * 0.0625f;
