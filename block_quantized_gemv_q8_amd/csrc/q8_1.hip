@@ -67,7 +67,13 @@ __global__ __launch_bounds__(RMS_THREADS) void rms_norm_q8_1_kernel(
     float *__restrict__ x, uint8_t *__restrict__ xq)
 {
     __shared__ float wave_sums[RMS_THREADS / WAVE];
+    // workgroup (m, q): row m; every workgroup of the row forms the row's sum
+    // of squares the same way, and group grp writes and quantizes only its
+    // block grp + RMS_GROUPS * q (five workgroups per row at K = 5120
+    // instead of one quantizing five blocks per group in turn: 4.4 against
+    // 5.6 us for the four-part sum; the bits are the same)
     const int m = blockIdx.x;
+    const int q = blockIdx.y;
     const int nb = K / QK;
     const int grp = threadIdx.x >> 5;
     const int j = threadIdx.x & 31;
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(RMS_THREADS) void rms_norm_q8_1_kernel(
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int b = grp + RMS_GROUPS * i;
-            if (b < nb)
+            if (i == q && b < nb)
                 ysum[(size_t)m * K + b * QK + j] = v[i];
         }
     }
@@ -137,13 +143,11 @@ __global__ __launch_bounds__(RMS_THREADS) void rms_norm_q8_1_kernel(
     const float inv = 1.0f / sqrtf(tot / (float)K + eps);
 
     uint8_t *out = xq ? xq + (size_t)m * nb * Q8_1_BYTES : nullptr;
-    // one block after another: quantizing a group's blocks side by side
-    // measured slower (6.8 against 5.6 us for the four-part sum at K = 5120)
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
+        if (i != q) // uniform per workgroup
+            continue;
         const int b = grp + RMS_GROUPS * i;
-        if (b - grp >= nb) // no group has a block this far (uniform per workgroup)
-            break;
         const bool valid = b < nb;
         const float val = v[i] * inv;
         if (valid && x)
@@ -156,8 +160,10 @@ template <int VPT, int NP>
 static void launch_rms_np(const float *y, int64_t M, int64_t K, float eps, float *ysum, float *x,
                           void *xq, hipStream_t s)
 {
-    hipLaunchKernelGGL((rms_norm_q8_1_kernel<VPT, NP>), dim3((unsigned)M), dim3(RMS_THREADS), 0,
-                       s, y, (size_t)(M * K), (int)K, eps, ysum, x, (uint8_t *)xq);
+    const unsigned per_row = (unsigned)((K / QK + RMS_GROUPS - 1) / RMS_GROUPS);
+    hipLaunchKernelGGL((rms_norm_q8_1_kernel<VPT, NP>), dim3((unsigned)M, per_row),
+                       dim3(RMS_THREADS), 0, s, y, (size_t)(M * K), (int)K, eps, ysum, x,
+                       (uint8_t *)xq);
 }
 
 template <int VPT>
