@@ -441,7 +441,7 @@ __device__ __forceinline__ void pk_range_sum2(const float *p, const float *q, si
 // those of PK_ANY: only address arithmetic differs.
 enum { PK_ANY = 0, PK_FULL_WHOLE = 1, PK_FULL_SPLIT = 2 };
 
-template <int M, int KIND>
+template <int M, int KIND, int NT>
 __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
     const uint8_t *__restrict__ QS, const uint16_t *__restrict__ D, int N, int nb, int nsplit,
     int P, int whole, const uint8_t *__restrict__ xq, float *__restrict__ y,
@@ -449,19 +449,21 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
 {
     constexpr int MS = PkShape<M>::MS;
     constexpr int SLOTS = MS * 4;
-    constexpr int STRIDE = pk_wave_stride<M, 1>();
-    constexpr bool FULL = KIND != PK_ANY;
+    constexpr int UNIT = NT * SLOTS * 32; // sums of one workgroup's unit (NT tiles)
+    constexpr int STRIDE = pk_wave_stride<M, NT>();
+    // NT > 1 is launched only with N % (16 NT) == 0
+    constexpr bool FULL = KIND != PK_ANY || NT > 1;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int S = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
-    const int tiles = (N + PK_TILE - 1) / PK_TILE;
+    const int units = (N + PK_TILE * NT - 1) / (PK_TILE * NT);
     const int nch = nb / PK_CB;
     int t = blockIdx.x, c0 = 0, c1 = nch, j = -1;
     if (KIND == PK_FULL_SPLIT || (KIND == PK_ANY && nsplit > 1)) {
         // p * nch < 2^21 (p < 8, nch <= 2^18): 32-bit arithmetic suffices
-        const int p = (int)blockIdx.x / tiles;
-        t = blockIdx.x - p * tiles;
+        const int p = (int)blockIdx.x / units;
+        t = blockIdx.x - p * units;
         c0 = p * nch / nsplit;
         c1 = (p + 1) * nch / nsplit;
         y += (size_t)p * M * N;
@@ -474,40 +476,45 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
             c1 = (p + 1) * nch / P;
         }
     }
-    const int n0 = t * PK_TILE;
+    const int n0 = t * PK_TILE * NT;
     const int rows_t = FULL ? PK_TILE : ((N - n0 < PK_TILE) ? N - n0 : PK_TILE);
-    const uint8_t *tile[1] = {QS + (size_t)n0 * nb * 16};
-    const uint16_t *dtile[1] = {D + (size_t)n0 * nb};
-    float acc[1][MS][4];
-    pk_accumulate<M, 1>(tile, dtile, rows_t, (size_t)8 * rows_t * 16, (size_t)2 * rows_t * 8, nb,
-                        c0, c1 - c0, xq, smem + (size_t)wave * STRIDE, acc);
-    pk_store_partials<1, MS>(acc, smem + (size_t)wave * STRIDE, lane);
+    const uint8_t *tile[NT];
+    const uint16_t *dtile[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        tile[i] = QS + (size_t)(n0 + PK_TILE * i) * nb * 16;
+        dtile[i] = D + (size_t)(n0 + PK_TILE * i) * nb;
+    }
+    float acc[NT][MS][4];
+    pk_accumulate<M, NT>(tile, dtile, rows_t, (size_t)8 * rows_t * 16, (size_t)2 * rows_t * 8, nb,
+                         c0, c1 - c0, xq, smem + (size_t)wave * STRIDE, acc);
+    pk_store_partials<NT, MS>(acc, smem + (size_t)wave * STRIDE, lane);
     __syncthreads();
-    // output (slot, l), slot = 4s + x: activation row pk_row(s, l/16, x),
-    // weight row n0 + l%16
+    // output idx = (i * SLOTS + slot) * 32 + l, slot = 4s + x: tile i,
+    // activation row pk_row(s, l/16, x), weight row n0 + 16i + l%16
     auto wave_sum = [&](int idx) {
-        const int slot = idx >> 5, l = idx & 31;
+        const int i = idx / (SLOTS * 32), slot = (idx >> 5) % SLOTS, l = idx & 31;
         float sacc = 0.0f;
         for (int v = 0; v < S; ++v)
-            sacc += pk_partial_sum<1, MS>(smem, STRIDE, v, 0, slot, l);
+            sacc += pk_partial_sum<NT, MS>(smem, STRIDE, v, i, slot, l);
         return sacc;
     };
     auto store_y = [&](int idx, float sacc) {
-        const int slot = idx >> 5, l = idx & 31;
+        const int i = idx / (SLOTS * 32), slot = (idx >> 5) % SLOTS, l = idx & 31;
         const int m = pk_row<M>(slot >> 2, l >> 4, slot & 3);
-        const int nn = n0 + (l & 15);
+        const int nn = n0 + PK_TILE * i + (l & 15);
         if (pk_row_ok<M>(slot >> 2, l >> 4, slot & 3) && nn < N)
             y[(size_t)m * N + nn] = sacc * 0.0625f;
     };
     if (KIND == PK_FULL_WHOLE || KIND == PK_FULL_SPLIT || j < 0) {
-        for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x)
+        for (int idx = threadIdx.x; idx < UNIT; idx += blockDim.x)
             store_y(idx, wave_sum(idx));
         return;
     }
-    float *rsum = ws_sum + (size_t)(j - j % P) * SLOTS * 32; // the tile's P range sums
-    for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x)
-        __hip_atomic_store(rsum + (size_t)(j % P) * SLOTS * 32 + idx, wave_sum(idx),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float *rsum = ws_sum + (size_t)(j - j % P) * UNIT; // the unit's P range sums
+    for (int idx = threadIdx.x; idx < UNIT; idx += blockDim.x)
+        __hip_atomic_store(rsum + (size_t)(j % P) * UNIT + idx, wave_sum(idx), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     // the partial sums have been read: wave 0's first LDS word carries the verdict
@@ -518,8 +525,8 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
     __syncthreads();
     if (!*last)
         return;
-    for (int idx = threadIdx.x; idx < SLOTS * 32; idx += blockDim.x)
-        store_y(idx, pk_range_sum(rsum + idx, SLOTS * 32, P));
+    for (int idx = threadIdx.x; idx < UNIT; idx += blockDim.x)
+        store_y(idx, pk_range_sum(rsum + idx, UNIT, P));
     if (threadIdx.x == 0)
         __hip_atomic_store(ws_count + j / P, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -759,24 +766,45 @@ static int64_t pk_ws_bytes(int64_t cus)
 // 11.19 us uncut, 11.01 us for the cut launch with the meeting left out),
 // and at M = 1 the cut launch won on ffn_up but lost on down (11.95 against
 // 11.24 us).
-template <int M>
-static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const void *xq, int nsplit,
-                                float *y, void *ws, int64_t cus, hipStream_t stream)
+// Waves per workgroup of the two-tile product (M >= 9), from a sweep of
+// 2..6 waves at every M = 9..17 on ffn_up (the balanced launch) and down
+// (4 K ranges): three on an unsplit launch (ffn_up M = 9 / 12 / 16: 12.6 /
+// 13.1 / 14.5 us), four from three MFMAs per block pair on (M = 17: 16.6
+// against 17.1 us with three) and on a split launch (down M = 12 / 17:
+// 14.8 / 18.6 us; 15.9 / 19.6 with three).  Never more than a range has
+// chunks or the LDS holds.
+static int pair_waves(int M, int nsplit, int64_t chunks, int64_t wave_lds, int64_t limit)
+{
+    int64_t s = (M > 16 || nsplit > 1) ? 4 : 3;
+    if (s > chunks)
+        s = chunks;
+    while (s > 1 && s * wave_lds > limit)
+        --s;
+    return (int)(s < 1 ? 1 : s);
+}
+
+// One launch of the product with NT 16-row tiles per workgroup (the unit
+// the K ranges, the split and the cut apply to).
+template <int M, int NT>
+static bq8_status packed_launch_nt(const uint8_t *wp, int64_t N, int64_t K, const void *xq,
+                                   int nsplit, float *y, void *ws, int64_t cus,
+                                   hipStream_t stream)
 {
     const int nb = (int)(K / QK);
     const int64_t C = nb / PK_CB;
-    const int64_t tiles = (N + PK_TILE - 1) / PK_TILE;
+    const int64_t units = (N + PK_TILE * NT - 1) / (PK_TILE * NT);
     const int P = packed_parts(C);
-    const int64_t wave_lds = pk_wave_stride<M, 1>();
+    const int64_t wave_lds = pk_wave_stride<M, NT>();
     const int64_t limit = packed_lds_limit();
-    const int s = packed_waves(tiles * nsplit, C / nsplit, M, wave_lds, limit);
+    const int s = NT == 1 ? packed_waves(units * nsplit, C / nsplit, M, wave_lds, limit)
+                          : pair_waves(M, nsplit, C / nsplit, wave_lds, limit);
     const int64_t lds = (int64_t)s * wave_lds;
     if (lds > limit)
         return BQ8_ERR_SHAPE;
-    int64_t whole = tiles;
+    int64_t whole = units;
     if (ws && nsplit == 1 && M >= 9)
-        whole = tiles - tiles % cus;
-    const int64_t grid = nsplit > 1 ? tiles * nsplit : whole + (tiles - whole) * P;
+        whole = units - units % cus;
+    const int64_t grid = nsplit > 1 ? units * nsplit : whole + (units - whole) * P;
     const uint8_t *QS = wp;
     const uint16_t *D = reinterpret_cast<const uint16_t *>(wp + N * nb * 16);
     uint32_t *ws_count = static_cast<uint32_t *>(ws);
@@ -792,12 +820,33 @@ static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const v
                            ws_count);
         return launch_status();
     };
-    if constexpr (M <= 8) {
+    if constexpr (NT == 1 && M <= 8) {
         if (N % PK_TILE == 0)
-            return nsplit > 1 ? launch(q4_0_mmvq_packed_kernel<M, PK_FULL_SPLIT>)
-                              : launch(q4_0_mmvq_packed_kernel<M, PK_FULL_WHOLE>);
+            return nsplit > 1 ? launch(q4_0_mmvq_packed_kernel<M, PK_FULL_SPLIT, 1>)
+                              : launch(q4_0_mmvq_packed_kernel<M, PK_FULL_WHOLE, 1>);
     }
-    return launch(q4_0_mmvq_packed_kernel<M, PK_ANY>);
+    return launch(q4_0_mmvq_packed_kernel<M, PK_ANY, NT>);
+}
+
+// From M = 9 (M = 11 on a split launch) a workgroup takes two tiles when
+// N % 32 == 0 and the launch still has a workgroup for every CU: each staged
+// activation chunk and each A operand then serve two tiles (the activation
+// bytes per chunk outweigh the weight bytes from M = 8 up).  Against one
+// tile per workgroup: ffn_up (balanced) M = 9 / 12 / 17 12.6 / 13.1 / 16.6
+// against 13.7 / 14.1 / 18.5 us; down, 4 K ranges, M = 12 / 17 14.8 / 18.6
+// against 15.4 / 20.3 us, while at M = 9 and 10 one tile stays ahead
+// (13.9 against 14.4 us).
+template <int M>
+static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const void *xq, int nsplit,
+                                float *y, void *ws, int64_t cus, hipStream_t stream)
+{
+    if constexpr (M >= 9) {
+        const int64_t cu = cus > 0 ? cus : device_cus();
+        if (N % (2 * PK_TILE) == 0 && cu > 0 && N / (2 * PK_TILE) * nsplit >= cu &&
+            (nsplit == 1 || M >= 11))
+            return packed_launch_nt<M, 2>(wp, N, K, xq, nsplit, y, ws, cu, stream);
+    }
+    return packed_launch_nt<M, 1>(wp, N, K, xq, nsplit, y, ws, cus, stream);
 }
 
 // Waves per gate/up workgroup: about 2176 waves in flight for M >= 3 and

@@ -146,6 +146,34 @@ def test_mmvq_packed_wide_ragged(N, K):
         assert np.array_equal(one[0].view(np.uint32), yy.view(np.uint32))
 
 
+# From M = 9 a workgroup takes two 16-row tiles when N % 32 == 0 and there
+# are at least as many such pairs (times the split count) as CUs.  These
+# shapes take that path for the plain and the split launches: every M from 9
+# to 17 against the oracle, equal weight rows in different pairs bitwise
+# equal, and a single range bitwise the whole product.
+def test_mmvq_packed_two_tile_workgroups():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K = 32 * (cus + 44), 1024
+    w, x = synth.random_q4_0_case(3600, N, K, 17)
+    copies = [16, 31, 32, 47, N // 2 + 1, N - 1]
+    for r in copies:
+        w[r] = w[3]
+    xq = oracle.q8_1_quantize(x)
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
+    wp = bq.q4_0_pack(dev(w))
+    xqd = dev(xq)
+    for m in range(9, 18):
+        say(f"q4_0_mmvq_packed two-tile workgroups M={m} N={N} K={K}")
+        y = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
+        assert_close(y, ref[:m], bound[:m], f"two-tile m{m}")
+        for r in copies:
+            assert np.array_equal(y[:, r].view(np.uint32), y[:, 3].view(np.uint32)), r
+        one = host(bq.q4_0_mmvq_packed_split(wp, N, K, xqd[:m], m, 1))
+        assert np.array_equal(one[0].view(np.uint32), y.view(np.uint32))
+        parts = host(bq.q4_0_mmvq_packed_split(wp, N, K, xqd[:m], m, 3))
+        assert_close(part_sum(parts), ref[:m], bound[:m], f"two-tile split 3 m{m}")
+
+
 def part_sum(parts):
     """Sum of partial rows in part order, in binary32 (the documented order)."""
     y = parts[0].copy()
