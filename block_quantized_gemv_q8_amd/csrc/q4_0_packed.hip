@@ -849,13 +849,14 @@ static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const v
     return packed_launch_nt<M, 1>(wp, N, K, xq, nsplit, y, ws, cus, stream);
 }
 
-// Waves per gate/up workgroup: about 2176 waves in flight for M >= 3 and
-// 1088 for M <= 2 (measured on the 17408 x 5120 shape: four and two waves
-// per 32-column workgroup), at least one, at most eight, never more than the
-// row has chunks or the LDS holds.
+// Waves per gate/up workgroup: about 1088 waves in flight for M <= 2, 1632
+// for M = 3..8 and 2176 from M = 9 (two, three and four per 32-column
+// workgroup on the 17408 x 5120 shape; a sweep of 2..8 waves there put
+// M = 1 / 6 / 9 / 17 at 18.6 / 19.8 / 25.6 / 30.6 us), at least one, at most
+// eight, never more than the row has chunks or the LDS holds.
 static int gate_up_waves(int64_t groups, int nb, int M, int64_t wave_lds, int64_t limit)
 {
-    const int64_t target = M <= 2 ? 1088 : 2176;
+    const int64_t target = M <= 2 ? 1088 : M <= 8 ? 1632 : 2176;
     int64_t s = (target + groups - 1) / groups;
     if (s > 8)
         s = 8;
