@@ -29,6 +29,8 @@ Profiling helpers (one kernel family per process, for rocprofv3):
     python bench.py --profile-target \\
         packed_m6|mmvq_m6|gate_up|lmhead_top1|lmhead_compact|down_sweep|stream|stream_packed|copy|probe
         [--reps R]
+    python bench.py --profile-target packed_one --shape ffn_up|down --m M \
+        --launch whole|ws|split [--reps R]
 """
 from __future__ import annotations
 
@@ -465,7 +467,7 @@ def pmc_traffic(record=PMC_RECORD):
     return rec.get("hbm_bytes_per_launch")
 
 
-def profile_target(torch, bq, synth, target, reps):
+def profile_target(torch, bq, synth, target, reps, args=None):
     if target == "copy":
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -507,6 +509,29 @@ def profile_target(torch, bq, synth, target, reps):
                                s["scratch"], compact=True)
     elif target == "down_sweep":
         time_down_sweep(torch, bq, synth, reps)
+    elif target == "packed_one":
+        # one launch kind at one M on one shape, so that a counter record
+        # holds nothing else: --shape ffn_up|down, --m, --launch
+        # whole (no workspace) | ws (CU-balanced) | split (the default split)
+        cfg = synth.FFN_UP if args.shape == "ffn_up" else synth.DOWN_SWEEP
+        N, K, m = cfg["N"], cfg["K"], args.m
+        w0 = synth.q4_0_weights_device(cfg["seed"], N, K)
+        wps = [bq.q4_0_pack(w0)] + [None] * (ROTATE - 1)
+        for i in range(1, ROTATE):
+            wps[i] = wps[0].clone()
+        del w0
+        xq = bq.q8_1_quantize(torch.randn((m, K), device="cuda"))
+        P = bq.q4_0_mmvq_packed_splits(N, K)
+        y = torch.empty((P, m, N), dtype=torch.float32, device="cuda")
+        pw = bq.q4_0_mmvq_packed_workspace()
+        for i in range(reps):
+            wp = wps[i % ROTATE]
+            if args.launch == "split":
+                bq.q4_0_mmvq_packed_split(wp, N, K, xq, m, P, y)
+            elif args.launch == "ws":
+                bq.q4_0_mmvq_packed(wp, N, K, xq, m, y[0], ws=pw)
+            else:
+                bq.q4_0_mmvq_packed(wp, N, K, xq, m, y[0])
     elif target in ("stream", "stream_packed"):
         time_stream(torch, bq, synth, reps, target == "stream_packed")
     else:
@@ -523,6 +548,11 @@ def main():
     ap.add_argument("--profile-target", default=None)
     ap.add_argument("--reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shape", choices=("ffn_up", "down"), default="ffn_up",
+                    help="packed_one profile target: the workload shape")
+    ap.add_argument("--m", type=int, default=6, help="packed_one profile target: M")
+    ap.add_argument("--launch", choices=("whole", "ws", "split"), default="whole",
+                    help="packed_one profile target: which launch")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (each MI355X runs its "
@@ -539,7 +569,7 @@ def main():
     bq.lib()
 
     if args.profile_target:
-        profile_target(torch, bq, synth, args.profile_target, args.reps)
+        profile_target(torch, bq, synth, args.profile_target, args.reps, args)
         return
 
     log("bench: ffn_up setup (12 weight copies, packed once)")
