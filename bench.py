@@ -11,7 +11,9 @@ as the pages' verifier did with its offline-packed width-6 projections --
 is not timed, like the Q6_K expansion of the LM head.  Twelve copies of the
 weight (601 MB, more than twice the 256 MB last-level cache) are used
 round-robin so every step streams its weight from HBM; inputs are resident
-in device memory before timing starts.
+in device memory before timing starts.  The K timed steps are captured as
+one HIP graph and replayed (the eager issue of the same steps is reported
+beside it).
 
 Printed: one JSON line with the effective weight bandwidth of a step
 (value, GB/s), the product kernel's roofline against the 8 TB/s HBM peak,
@@ -29,7 +31,7 @@ Profiling helpers (one kernel family per process, for rocprofv3):
     python bench.py --profile-target \\
         packed_m6|mmvq_m6|gate_up|lmhead_top1|lmhead_compact|down_sweep|stream|stream_packed|copy|probe
         [--reps R]
-    python bench.py --profile-target packed_one --shape ffn_up|down --m M \
+    python bench.py --profile-target packed_one --shape ffn_up|down --m M \\
         --launch whole|ws|split [--reps R]
 """
 from __future__ import annotations
@@ -578,7 +580,9 @@ def main():
     wbytes = q4_0_bytes(N, K)
     # untimed warm-up: --warmup steps, then more until WARMUP_MIN_S of wall
     # time has passed (the first short region after a pause runs slow, and
-    # the driver's --warmup 5 is a few tens of microseconds)
+    # the driver's --warmup 5 is a few tens of microseconds); its last
+    # batch runs inside a Timer, so the timing events' first use is not in
+    # the timed region
     warm_steps = 0
     t0 = time.perf_counter()
     while warm_steps < args.warmup or time.perf_counter() - t0 < WARMUP_MIN_S:
@@ -587,20 +591,29 @@ def main():
             warm_steps += 1
         if warm_steps % 200 == 0:
             torch.cuda.synchronize()
-    with Timer(torch) as t:
-        for i in range(args.steps):
-            step_packed(bq, s, warm_steps + i)
-    step_us = t.ms * 1000.0 / args.steps
-    value = wbytes / step_us / 1e3  # GB/s
-    log(f"bench: step (quantize + packed M=6) {step_us:.3f} us, {value:.1f} GB/s")
-    # the same steps captured as one HIP graph and replayed, for comparison
-    g = capture(torch, lambda i: step_packed(bq, s, i), args.steps)
+    with Timer(torch):
+        for _ in range(20):
+            step_packed(bq, s, warm_steps)
+            warm_steps += 1
+    # the K timed steps, captured as one HIP graph and replayed once untimed
+    # first: one launch for the whole region, so the host's per-call cost
+    # and the first launch's latency do not leave the GPU idle between steps
+    # (with --steps 20 they did, by several microseconds a step)
+    g = capture(torch, lambda i: step_packed(bq, s, warm_steps + i), args.steps)
     g.replay()
     with Timer(torch) as t:
         g.replay()
-    graph_step_us = t.ms * 1000.0 / args.steps
-    log(f"bench: step as a replayed graph {graph_step_us:.3f} us")
     del g
+    step_us = t.ms * 1000.0 / args.steps
+    value = wbytes / step_us / 1e3  # GB/s
+    log(f"bench: step (quantize + packed M=6) as a replayed graph {step_us:.3f} us, "
+        f"{value:.1f} GB/s")
+    # the same steps issued eagerly, one library call at a time
+    with Timer(torch) as t:
+        for i in range(args.steps):
+            step_packed(bq, s, warm_steps + i)
+    eager_step_us = t.ms * 1000.0 / args.steps
+    log(f"bench: step issued eagerly {eager_step_us:.3f} us")
     step_b = time_batches(torch, lambda i: step_packed(bq, s, i), args.steps, 10)
     bq.q8_1_quantize(s["x"], s["xq"])
     reps = max(args.steps, 100)
@@ -705,10 +718,12 @@ def main():
             "step_us": round(step_us, 3),
             "warmup_steps_run": warm_steps,
             "warmup_min_s": WARMUP_MIN_S,
-            "step_us_batches": stats_us(step_b),
+            "step_timing": "the K steps captured as one HIP graph, replayed once untimed, "
+                           "then once inside the timed region",
+            "step_eager_us": round(eager_step_us, 3),
+            "step_eager_us_batches": stats_us(step_b),
             "product_launch": "q4_0_mmvq_packed_ws; at M <= 8 it runs every 16-row tile "
                               "whole (the q4_0_mmvq_packed launch)",
-            "step_graph_replay_us": round(graph_step_us, 3),
             "packed_mmvq_us": round(packed_us, 3),
             "packed_mmvq_us_batches": stats_us(packed_b),
             "hbm_read_probe": probe_ffn,
