@@ -78,6 +78,30 @@ MUTATIONS = {
         "double inv = 1.0 / sqrt(ss / (double)K + eps);",
         "double inv = 1.0 / sqrt(ss / (double)(K - 1) + eps);",
         ["test_oracle_stages.py"]),
+    "q8_1_amax_signed": (
+        "float a = fabsf(xb[j]);",
+        "float a = xb[j];",
+        ["test_oracle_q8_1.py"]),
+    "q4_0_dot_drops_dx": (
+        "int nib = (j < 16) ? (wb[2 + j] & 0x0F) : (wb[2 + j - 16] >> 4);\n"
+        "                    double wv = dw * (double)(nib - 8);\n"
+        "                    double xv = dx * (double)(int8_t)xb[4 + j];",
+        "int nib = (j < 16) ? (wb[2 + j] & 0x0F) : (wb[2 + j - 16] >> 4);\n"
+        "                    double wv = dw * (double)(nib - 8);\n"
+        "                    double xv = (double)(int8_t)xb[4 + j];",
+        ["test_oracle_q4_0.py"]),
+    "silu_sign": (
+        "h[i] = gv / (1.0 + exp(-gv)) * (double)u[i];",
+        "h[i] = gv / (1.0 + exp(gv)) * (double)u[i];",
+        ["test_oracle_stages.py"]),
+    "q6k_compact_subscale_pairs_swapped": (
+        "return N * (K / 2) + N * (K / 4) + pack_sc_at(n, 16 * s + i, N, K);",
+        "return N * (K / 2) + N * (K / 4) + pack_sc_at(n, 16 * s + (i ^ 1), N, K);",
+        ["test_oracle_q6k_compact.py"]),
+    "q6k_compact_scale_superblocks_swapped": (
+        "return N * (K / 2) + N * (K / 4) + N * (K / 16) + 2 * pack_d_at(n, s, N, K);",
+        "return N * (K / 2) + N * (K / 4) + N * (K / 16) + 2 * pack_d_at(n, s ^ 1, N, K);",
+        ["test_oracle_q6k_compact.py"]),
     "f16_truncates": (
         "double m = round_half_even(ldexp(a, 10 - e)); /* in [1024, 2048] */",
         "double m = floor(ldexp(a, 10 - e));",

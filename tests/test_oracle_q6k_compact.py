@@ -5,7 +5,9 @@ it must guarantee: it holds exactly the raw bytes (its size is the raw size
 and unpacking restores the raw superblocks bit for bit, ragged tiles
 included); each 64-row tile stores 16-byte piece p of all its rows
 contiguously, rows in order, for the ql and qh planes (the purpose of the
-layout); and the weights it encodes are the raw format's, so top-1 through
+layout); its subscale and scale planes are the expanded pack's, byte for
+byte (the expanded planes are pinned value by value against the decoded raw
+blocks); and the weights it encodes are the raw format's, so top-1 through
 it equals top-1 through the raw weights' expanded pack, logits bitwise.
 """
 import numpy as np
@@ -62,6 +64,20 @@ def test_pieces_are_contiguous_per_tile(orc):
                 assert (row_of[o:o + 16] == n0 + r).all()
                 assert (sb_of[o:o + 16] == p // 4).all()
                 assert (byte_of[o:o + 16] == 128 + np.arange(16) + 16 * (p % 4)).all()
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_subscale_and_scale_planes_are_the_expanded_packs(orc, N, K):
+    rng = np.random.default_rng(970 + N + K)
+    raw = synth.q6k_raw_weights(rng, N, K)
+    cp = orc.q6k_pack_compact(raw, N, K)
+    ep = orc.q6k_pack_expand(raw, N, K)
+    c_sc = N * K // 2 + N * K // 4       # after the ql and qh planes
+    e_sc = N * K                         # after the int8 quants
+    n_sc, n_d = N * K // 16, N * K // 128
+    assert (cp[c_sc:c_sc + n_sc] == ep[e_sc:e_sc + n_sc]).all()
+    assert (cp[c_sc + n_sc:] == ep[e_sc + n_sc:]).all()
+    assert cp.size - (c_sc + n_sc) == n_d == ep.size - (e_sc + n_sc)
 
 
 @pytest.mark.parametrize("N,K,rows", [(300, 512, 5), (65, 768, 6), (1, 256, 3)])
