@@ -530,11 +530,15 @@ static bq8_status mmvq_launch(const void *w, int64_t N, int64_t K, const void *x
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     {
-        // MFMA path for K a multiple of 256: the longest chunk (32, 16 or 8
-        // blocks) that divides the row
-        // 8-block chunks; a ring of two stages up to M = 6, three above
-        // (measured on the ffn_up and down shapes)
-        constexpr int NST = M <= 6 ? 2 : 3;
+        // MFMA path for K a multiple of 256: 8-block chunks in a ring of two
+        // stages.  A third stage grows each wave's ring by a chunk of M
+        // activation rows and, from M = 7, leaves fewer workgroups per CU:
+        // two builds in one process, interleaved, three stages against two,
+        // down [5120 x 17408] M = 7 / 9 / 13 / 16 / 17: 20.3 / 24.4 / 26.9 /
+        // 41.0 / 52.7 against 19.5 / 24.1 / 25.5 / 27.6 / 33.9 us; ffn_up
+        // [17408 x 5120] M = 7 / 9 / 13 / 16 / 17: 18.4 / 23.3 / 25.5 / 38.8 /
+        // 48.5 against 16.5 / 19.6 / 21.4 / 25.0 / 31.8 us
+        constexpr int NST = 2;
         if (al && MfmaShape<M, 8, NST>::WAVE_LDS <= limit)
             return launch_mfma<M, 8, NST>(w, N, nb, xq, y, s, limit, 0);
     }
