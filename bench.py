@@ -40,6 +40,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -448,12 +449,26 @@ def host_info():
     return {"cpu_model": model, "logical_cpus": os.cpu_count()}
 
 
+def gpu_clocks():
+    """The clocks rocm-smi reports for the card (a child process, run after
+    the timed regions), or None where it is missing or fails."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        cards = json.loads(r.stdout)
+        card = next(iter(cards.values()))
+        return {k: v for k, v in card.items() if "clk" in k.lower() or "clock" in k.lower()}
+    except Exception:
+        return None
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
             "compute_units": p.multi_processor_count,
             "memory_GiB": round(p.total_memory / 2**30, 1), "torch": torch.__version__,
-            "hip": getattr(torch.version, "hip", None), "numpy": np.__version__}
+            "hip": getattr(torch.version, "hip", None), "numpy": np.__version__,
+            "clocks_after_timing": gpu_clocks()}
 
 
 def pmc_traffic(record=PMC_RECORD):
