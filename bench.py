@@ -11,9 +11,10 @@ as the pages' verifier did with its offline-packed width-6 projections --
 is not timed, like the Q6_K expansion of the LM head.  Twelve copies of the
 weight (601 MB, more than twice the 256 MB last-level cache) are used
 round-robin so every step streams its weight from HBM; inputs are resident
-in device memory before timing starts.  The K timed steps are captured as
-one HIP graph and replayed (the eager issue of the same steps is reported
-beside it).
+in device memory before timing starts.  The K timed steps' library calls
+are issued behind an untimed backlog of steps, so the timed region holds
+the K steps back to back.  The same K steps from an idle GPU, as one
+replayed HIP graph and issued through the binding, are reported beside it.
 
 Printed: one JSON line with the effective weight bandwidth of a step
 (value, GB/s), the product kernel's roofline against the 8 TB/s HBM peak,
@@ -37,6 +38,7 @@ Profiling helpers (one kernel family per process, for rocprofv3):
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -52,6 +54,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 ROTATE = 12
 WARMUP_MIN_S = 0.3  # untimed steps before the timed region, at least this long
+STEP_BACKLOG = 200  # untimed steps queued ahead of the timed ones
 PMC_RECORD = os.path.join(ROOT, "profiles", "pmc_q4_0_mmvq_packed_m6_ffn_up.json")
 PMC_RECORD_GATE_UP = os.path.join(ROOT, "profiles", "pmc_q4_0_gate_up_silu_q8_1_packed_m6_ffn.json")
 KERNEL_SOURCES = ["block_quantized_gemv_q8_amd/csrc/q4_0_packed.hip",
@@ -188,6 +191,24 @@ def setup_ffn_up(torch, bq, synth):
     # the product's workspace: the CU-balanced launch (q4_0_mmvq_packed_ws)
     pws = bq.q4_0_mmvq_packed_workspace()
     return dict(N=N, K=K, M=M, ws=ws, wps=wps, pws=pws, x=xd, xq=xq, y=y, u=u, hq=hq)
+
+
+def raw_step(torch, bq, s):
+    """step_packed as direct calls of the two C entry points the binding
+    wraps (q8_1_quantize, q4_0_mmvq_packed_ws), with the same arguments as
+    raw pointers taken once; a nonzero status raises."""
+    L = bq.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    xp, xqp, yp = s["x"].data_ptr(), s["xq"].data_ptr(), s["y"].data_ptr()
+    wps = [w.data_ptr() for w in s["wps"]]
+    wsp, wsn = s["pws"].data_ptr(), s["pws"].numel()
+    N, K, M = s["N"], s["K"], s["M"]
+
+    def step(i):
+        if (L.q8_1_quantize(xp, M, K, xqp, st) != 0 or
+                L.q4_0_mmvq_packed_ws(wps[i % ROTATE], N, K, xqp, M, yp, wsp, wsn, st) != 0):
+            raise RuntimeError("step launch failed")
+    return step
 
 
 def step_packed(bq, s, i):
@@ -449,26 +470,39 @@ def host_info():
     return {"cpu_model": model, "logical_cpus": os.cpu_count()}
 
 
-def gpu_clocks():
-    """The clocks rocm-smi reports for the card (a child process, run after
-    the timed regions), or None where it is missing or fails."""
+def clocks_under_load(torch, fn, max_s=10.0):
+    """The clocks rocm-smi reports while fn(i) runs back to back, untimed: the
+    child process starts first and batches of 200 calls are issued until it
+    exits.  None where rocm-smi is missing or fails."""
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
-                           text=True, timeout=30)
-        cards = json.loads(r.stdout)
-        card = next(iter(cards.values()))
-        return {k: v for k, v in card.items() if "clk" in k.lower() or "clock" in k.lower()}
+        p = subprocess.Popen(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
+                             stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    i = 0
+    while p.poll() is None and time.perf_counter() - t0 < max_s:
+        for _ in range(200):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    try:
+        out, _ = p.communicate(timeout=30)
+        card = next(iter(json.loads(out).values()))
+        return {k.strip(" :"): v for k, v in card.items()
+                if "clk" in k.lower() or "clock" in k.lower()}
     except Exception:
+        p.kill()
         return None
 
 
-def device_info(torch):
+def device_info(torch, clocks=None):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
             "compute_units": p.multi_processor_count,
             "memory_GiB": round(p.total_memory / 2**30, 1), "torch": torch.__version__,
             "hip": getattr(torch.version, "hip", None), "numpy": np.__version__,
-            "clocks_after_timing": gpu_clocks()}
+            "clocks_under_load": clocks}
 
 
 def pmc_traffic(record=PMC_RECORD):
@@ -610,19 +644,39 @@ def main():
         for _ in range(20):
             step_packed(bq, s, warm_steps)
             warm_steps += 1
-    # the K timed steps, captured as one HIP graph and replayed once untimed
-    # first: one launch for the whole region, so the host's per-call cost
-    # and the first launch's latency do not leave the GPU idle between steps
-    # (with --steps 20 they did, by several microseconds a step)
+    # the K timed steps: the step's two C entry points called on raw device
+    # pointers (the host then spends about 9 us a step, under the GPU's
+    # 12.8), behind an untimed backlog of STEP_BACKLOG steps, so that the
+    # GPU is still busy when the first timing event is recorded and runs the
+    # K steps back to back; the collector is paused meanwhile
+    raw = raw_step(torch, bq, s)
+    ev_a = torch.cuda.Event(enable_timing=True)
+    ev_b = torch.cuda.Event(enable_timing=True)
+    gc.disable()
+    try:
+        torch.cuda.synchronize()
+        for i in range(STEP_BACKLOG):
+            raw(warm_steps + i)
+        ev_a.record()
+        for i in range(args.steps):
+            raw(warm_steps + STEP_BACKLOG + i)
+        ev_b.record()
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
+    step_us = ev_a.elapsed_time(ev_b) * 1000.0 / args.steps
+    value = wbytes / step_us / 1e3  # GB/s
+    log(f"bench: step (quantize + packed M=6) {step_us:.3f} us, {value:.1f} GB/s")
+    # the same K steps from an idle GPU: as one replayed HIP graph (each
+    # graph launch costs the GPU about 10 us: 13.3 us a step at K = 20,
+    # 12.8 at K = 200), and issued eagerly through the binding
     g = capture(torch, lambda i: step_packed(bq, s, warm_steps + i), args.steps)
     g.replay()
     with Timer(torch) as t:
         g.replay()
     del g
-    step_us = t.ms * 1000.0 / args.steps
-    value = wbytes / step_us / 1e3  # GB/s
-    log(f"bench: step (quantize + packed M=6) as a replayed graph {step_us:.3f} us, "
-        f"{value:.1f} GB/s")
+    step_graph_us = t.ms * 1000.0 / args.steps
+    log(f"bench: step as one replayed graph from an idle GPU {step_graph_us:.3f} us")
     # the same steps issued eagerly, one library call at a time
     with Timer(torch) as t:
         for i in range(args.steps):
@@ -645,6 +699,9 @@ def main():
     probe_ffn = hbm_probe(torch, bq, s["wps"], 100)
     log(f"bench: HBM read probe over the same 12 packed copies {probe_ffn['us_median']:.3f} us, "
         f"{probe_ffn['GBps']} GB/s ({probe_ffn['launch']})")
+    clocks = clocks_under_load(torch, lambda i: bq.q4_0_mmvq_packed(
+        s["wps"][i % ROTATE], N, K, s["xq"], M, s["y"], ws=s["pws"]))
+    log(f"bench: clocks while the product runs untimed: {clocks}")
     std_us = time_calls(torch, lambda i: bq.q4_0_mmvq_m6(s["ws"][i % ROTATE], s["xq"], s["y"]),
                         reps, warm=20)
     std_step_us = time_calls(torch, lambda i: step_standard(bq, s, i), reps, warm=20)
@@ -733,8 +790,10 @@ def main():
             "step_us": round(step_us, 3),
             "warmup_steps_run": warm_steps,
             "warmup_min_s": WARMUP_MIN_S,
-            "step_timing": "the K steps captured as one HIP graph, replayed once untimed, "
-                           "then once inside the timed region",
+            "step_timing": "the K steps' library calls issued behind an untimed backlog "
+                           f"of {STEP_BACKLOG} steps, so the region between the two events "
+                           "holds the K steps back to back",
+            "step_graph_us_from_idle": round(step_graph_us, 3),
             "step_eager_us": round(eager_step_us, 3),
             "step_eager_us_batches": stats_us(step_b),
             "product_launch": "q4_0_mmvq_packed_ws; at M <= 8 it runs every 16-row tile "
@@ -780,7 +839,7 @@ def main():
             "shards_8_way": shards,
             "stream_64_layer_pass": stream_p,
             "stream_64_layer_pass_gguf_layout": stream_s,
-            "device": device_info(torch),
+            "device": device_info(torch, clocks),
             "cpu_oracle_one_thread": cpu1,
             "host": host_info(),
         },
