@@ -787,6 +787,11 @@ def main():
                         "projection (weight in the offline-packed layout, packed once, untimed)",
             "N": N, "K": K, "M": M,
             "weight_bytes": wbytes,
+            # the 4-bit codes alone (16 of every 18 bytes), the basis of the
+            # pages' "~45 MB" for this projection
+            "nibble_bytes": wbytes * 16 // 18,
+            "step_GBps_nibble_only": round(wbytes * 16 / 18 / step_us / 1e3, 1),
+            "packed_mmvq_GBps_nibble_only": round(wbytes * 16 / 18 / packed_us / 1e3, 1),
             "step_us": round(step_us, 3),
             "warmup_steps_run": warm_steps,
             "warmup_min_s": WARMUP_MIN_S,
