@@ -496,9 +496,18 @@ def clocks_under_load(torch, fn, max_s=10.0):
         return None
 
 
+def rocm_version():
+    """The ROCm release installed at /opt/rocm, or None."""
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
 def device_info(torch, clocks=None):
     p = torch.cuda.get_device_properties(0)
-    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "rocm": rocm_version(),
             "compute_units": p.multi_processor_count,
             "memory_GiB": round(p.total_memory / 2**30, 1), "torch": torch.__version__,
             "hip": getattr(torch.version, "hip", None), "numpy": np.__version__,
