@@ -538,7 +538,8 @@ __global__ __launch_bounds__(512) void q4_0_mmvq_packed_kernel(
                            __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // the partial sums have been read: wave 0's first LDS word carries the verdict
+    // the partial sums have been read: wave 0's first LDS word then tells the
+    // workgroup whether it arrived last
     int *last = reinterpret_cast<int *>(smem);
     if (threadIdx.x == 0)
         *last = __hip_atomic_fetch_add(ws_count + j / P, 1u, __ATOMIC_RELAXED,
@@ -671,7 +672,8 @@ __global__ __launch_bounds__(512) void q4_0_gate_up_packed_kernel(
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // the partial sums have been read: wave 0's first LDS word carries the verdict
+    // the partial sums have been read: wave 0's first LDS word then tells the
+    // workgroup whether it arrived last
     int *last = reinterpret_cast<int *>(smem);
     if (threadIdx.x == 0)
         *last = __hip_atomic_fetch_add(ws_count + j / P, 1u, __ATOMIC_RELAXED,
