@@ -59,8 +59,10 @@ def _quantize_inputs():
         x = synth.normal_rows(rng, M, K)
         x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20
         cases.append(x)
-    # edge blocks: zero, constant, exact half-way ties, tiny/subnormal amax
-    e = np.zeros((4, 128), np.float32)
+    # edge blocks: zero, constant, exact half-way ties, tiny/subnormal amax;
+    # large amax: s = d * sum(q) past binary16's 65504 (-> inf), and d itself
+    # exactly 65504, at the half-way point 65520 (rounds to inf) and beyond
+    e = np.zeros((6, 128), np.float32)
     e[0, 32:64] = 3.25
     k = np.arange(31, dtype=np.float64)
     e[1, 0] = 127 / 128
@@ -70,6 +72,12 @@ def _quantize_inputs():
     e[2, 32] = np.float32(1e-45)
     e[2, 64:96] = np.float32(1e-40) * np.linspace(-1, 1, 32, dtype=np.float32)
     e[3] = np.float32(6.1e-5) * rng.standard_normal(128).astype(np.float32)
+    e[4, 0:32] = 3000.0  # d = 3000/127, sum(q) = 32 * 127: s overflows
+    e[4, 32:128] = np.float32(1000.0) * rng.standard_normal(96).astype(np.float32)
+    e[5, 0:32] = np.float32(1e7) * np.linspace(-1, 1, 32, dtype=np.float32)
+    e[5, 32:64] = np.float32(127 * 65504) * np.linspace(1, 0, 32, dtype=np.float32)
+    e[5, 64:96] = np.float32(127 * 65520) * np.linspace(0, 1, 32, dtype=np.float32)
+    e[5, 96:128] = np.float32(3e38) * np.linspace(-1, 1, 32, dtype=np.float32)
     cases.append(e)
     return cases
 
