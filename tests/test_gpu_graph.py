@@ -118,3 +118,41 @@ def test_graph_of_packed_stream_and_top1():
         torch.cuda.synchronize()
         for t, r in zip(outs, refs):
             assert torch.equal(t, r)
+
+
+def test_graph_of_noalloc_head():
+    """q6k_lmhead_top1_noalloc, the entry point for callers under capture,
+    captured with two calls of different shapes: every replay gives the ids
+    of the eager q6k_lmhead_top1, with eager calls of the same entry point
+    (which share its per-GPU scratch) between replays."""
+    shapes = [(4096 + 17, 1024, 5), (3000, 512, 3)]
+    packs, xs, ids, refs = [], [], [], []
+    for i, (Nv, Kv, rows) in enumerate(shapes):
+        raw = synth.q6k_raw_weights_device(120 + i, Nv, Kv)
+        packs.append(bq.q6k_pack_expand(raw, Nv, Kv))
+        xs.append(torch.from_numpy(synth.normal_rows(np.random.default_rng(130 + i), 6,
+                                                     Kv)).to(DEV))
+        ids.append(torch.empty((rows,), dtype=torch.int32, device=DEV))
+        refs.append(bq.q6k_lmhead_top1(packs[i], Nv, Kv, xs[i], 1, rows))
+
+    def heads():
+        for i, (Nv, Kv, rows) in enumerate(shapes):
+            bq.q6k_lmhead_top1_noalloc(packs[i], Nv, Kv, xs[i], 1, rows, ids[i])
+
+    heads()
+    torch.cuda.synchronize()
+    for a, r in zip(ids, refs):
+        assert torch.equal(a, r)
+    g = _capture(heads)
+    other = torch.from_numpy(synth.normal_rows(np.random.default_rng(140), 6, 1024)).to(DEV)
+    for rep in range(3):
+        say(f"graph replay {rep}")
+        for t in ids:
+            t.fill_(-7)
+        # eager use of the same per-GPU scratch between replays
+        bq.q6k_lmhead_top1_noalloc(packs[0], shapes[0][0], 1024, other, 0, 6)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, r in zip(ids, refs):
+            assert torch.equal(a, r)
