@@ -31,3 +31,21 @@ def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h0
     (tmp_path / bench.KERNEL_SOURCES[0]).write_text("int f(int a) { return a + 2; }\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_committed_traffic_records_match_the_kernel_sources():
+    """The HBM-traffic records under profiles/ were taken on the kernel
+    sources as they are: bench.py reports their bytes as the roofline's
+    traffic only then (else null), so a kernel change without new counter
+    passes shows here."""
+    import json
+
+    import bench
+
+    h = bench.kernel_source_hash()
+    for path in (bench.PMC_RECORD, bench.PMC_RECORD_GATE_UP):
+        with open(path) as f:
+            rec = json.load(f)
+        assert rec["kernel_source_hash"] == h, os.path.basename(path)
+        assert rec["hbm_bytes_per_launch"] > 0
+    assert bench.pmc_traffic() is not None
