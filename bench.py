@@ -655,7 +655,7 @@ def main():
             warm_steps += 1
     # the K timed steps: the step's two C entry points called on raw device
     # pointers (the host then spends about 9 us a step, under the GPU's
-    # 12.8), behind an untimed backlog of STEP_BACKLOG steps, so that the
+    # 12.6), behind an untimed backlog of STEP_BACKLOG steps, so that the
     # GPU is still busy when the first timing event is recorded and runs the
     # K steps back to back; the collector is paused meanwhile
     raw = raw_step(torch, bq, s)
