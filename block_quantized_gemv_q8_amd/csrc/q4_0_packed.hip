@@ -823,8 +823,13 @@ static bq8_status packed_launch_nt(const uint8_t *wp, int64_t N, int64_t K, cons
     const int P = packed_parts(C);
     const int64_t wave_lds = pk_wave_stride<M, NT>();
     const int64_t limit = packed_lds_limit();
-    const int s = NT == 1 ? packed_waves(units * nsplit, C / nsplit, M, wave_lds, limit)
-                          : pair_waves(M, nsplit, C / nsplit, wave_lds, limit);
+    int s = NT == 1 ? packed_waves(units * nsplit, C / nsplit, M, wave_lds, limit)
+                    : pair_waves(M, nsplit, C / nsplit, wave_lds, limit);
+    // split launches at M <= 2 take a third wave per workgroup: down with 4
+    // K ranges, M = 1 / 2: 10.18 / 10.20 -> 9.92 / 9.92 us (at M = 6 and 9
+    // the third wave lost: 11.15 -> 11.31, 13.37 -> 14.71 us)
+    if (NT == 1 && nsplit > 1 && M <= 2 && s < 3 && C / nsplit >= 3 && 3 * wave_lds <= limit)
+        s = 3;
     const int64_t lds = (int64_t)s * wave_lds;
     if (lds > limit)
         return BQ8_ERR_SHAPE;
