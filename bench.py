@@ -30,7 +30,7 @@ oracle's CPU throughput on a bounded sample.
 
 Profiling helpers (one kernel family per process, for rocprofv3):
     python bench.py --profile-target \\
-        packed_m6|mmvq_m6|gate_up|lmhead_top1|lmhead_compact|down_sweep|stream|stream_packed|copy|probe
+        packed_m6|packed_m6_graph|mmvq_m6|gate_up|lmhead_top1|lmhead_compact|down_sweep|stream|stream_packed|copy|probe
         [--reps R]
     python bench.py --profile-target packed_one --shape ffn_up|down --m M \\
         --launch whole|ws|split [--reps R]
@@ -549,6 +549,21 @@ def profile_target(torch, bq, synth, target, reps, args=None):
             bq.hbm_read_probe(s["wps"][i % ROTATE], wgs, 8, out)
         torch.cuda.synchronize()
         log(f"probe: {reps} reads of {s['wps'][0].numel()} bytes")
+        return
+    if target == "packed_m6_graph":
+        # the roofline kernel as bench.py times it, back to back: one HIP
+        # graph of 100 launches rotating the 12 weight copies, replayed reps
+        # times, so that a kernel trace sees the launches without the host's
+        # per-launch gaps
+        s = setup_ffn_up(torch, bq, synth)
+        N, K, M = s["N"], s["K"], s["M"]
+        bq.q8_1_quantize(s["x"], s["xq"])
+        g = capture(torch, lambda i: bq.q4_0_mmvq_packed(
+            s["wps"][i % ROTATE], N, K, s["xq"], M, s["y"], ws=s["pws"]), 100)
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        log(f"packed_m6_graph: {reps} replays of 100 launches")
         return
     if target in ("packed_m6", "mmvq_m6", "gate_up"):
         s = setup_ffn_up(torch, bq, synth)
