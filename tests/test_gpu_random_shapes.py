@@ -51,24 +51,24 @@ def assert_close(gpu, ref, bound, what):
 
 def _draws():
     rng = np.random.default_rng(9000)
-    q8 = [(int(rng.integers(1, 18)), 32 * int(rng.integers(1, 200))) for _ in range(10)]
+    q8 = [(int(rng.integers(1, 18)), 32 * int(rng.integers(1, 200))) for _ in range(20)]
     gguf = [(int(rng.integers(1, 3001)), 32 * int(rng.integers(1, 129)), int(rng.integers(1, 18)))
-            for _ in range(16)]
+            for _ in range(30)]
     packed = []
-    for _ in range(16):
+    for _ in range(30):
         K = 512 * int(rng.integers(1, 9))
         packed.append((int(rng.integers(1, 3001)), K, int(rng.integers(1, 18)),
                        int(rng.integers(1, min(8, K // 256) + 1))))
     joint = [(32 * int(rng.integers(1, 101)), 512 * int(rng.integers(1, 7)),
-              int(rng.integers(1, 18))) for _ in range(10)]
+              int(rng.integers(1, 18))) for _ in range(20)]
     head = []
-    for _ in range(12):
+    for _ in range(24):
         rows = int(rng.integers(1, 9))
         M = rows + int(rng.integers(0, 3))
         head.append((int(rng.integers(1, 5001)), 256 * int(rng.integers(1, 9)), M,
                      int(rng.integers(0, M - rows + 1)), rows, int(rng.integers(0, 9))))
     glue = [(int(rng.integers(1, 18)), 32 * int(rng.integers(1, 400)), int(rng.integers(1, 5)))
-            for _ in range(8)]
+            for _ in range(16)]
     return q8, gguf, packed, joint, head, glue
 
 
