@@ -2,7 +2,8 @@
 
 1. The native pass equals the same steps made one C-ABI call at a time,
    bit for bit (same kernels, fixed reduction orders), on small shapes that
-   take both the MFMA path (K % 256 == 0) and the dot4 path, at several M.
+   take both the MFMA path (K % 256 == 0) and the dot4 path, at several M,
+   and on seeded random widths, row counts and layer counts.
 2. At the full stream shape (64 layers of gate/up [5120 -> 17408] and down
    [17408 -> 5120], M = 6), on both weight layouts, every stage of the last
    layer is checked against
@@ -57,8 +58,17 @@ def composed(wg, wu, wd, x0, eps):
     return y, dict(xq=xq, g=g, u=u, hq=hq)
 
 
+def _random_stream_shapes(seed, granule, n):
+    """Seeded (M, hidden, ffn, layers) draws: widths multiples of granule."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 18)), granule * int(rng.integers(1, 4096 // granule + 1)),
+             granule * int(rng.integers(1, 4096 // granule + 1)), int(rng.integers(1, 4)))
+            for _ in range(n)]
+
+
 @pytest.mark.parametrize("M,hidden,ffn,layers", [(6, 512, 1024, 3), (1, 256, 768, 2),
-                                                 (9, 288, 352, 3), (17, 1280, 512, 2)])
+                                                 (9, 288, 352, 3), (17, 1280, 512, 2)]
+                         + _random_stream_shapes(9700, 32, 6))
 def test_stream_equals_composed_calls(M, hidden, ffn, layers):
     say(f"stream vs composed M={M} hidden={hidden} ffn={ffn} layers={layers}")
     wg = [synth.q4_0_weights_device(900 + 3 * l, ffn, hidden) for l in range(layers)]
@@ -152,7 +162,8 @@ def composed_packed(wg, wu, wd, x0, eps, hidden, ffn):
 
 
 @pytest.mark.parametrize("M,hidden,ffn,layers", [(6, 512, 1024, 3), (17, 1024, 1536, 2),
-                                                 (1, 512, 512, 2), (6, 5120, 1024, 2)])
+                                                 (1, 512, 512, 2), (6, 5120, 1024, 2)]
+                         + _random_stream_shapes(9701, 512, 6))
 def test_packed_stream_equals_composed_calls(M, hidden, ffn, layers):
     say(f"packed stream vs composed M={M} hidden={hidden} ffn={ffn} layers={layers} "
         f"down split {bq.q4_0_mmvq_packed_splits(hidden, ffn)}")
