@@ -58,7 +58,8 @@ STEP_BACKLOG = 200  # untimed steps queued ahead of the timed ones
 PMC_RECORD = os.path.join(ROOT, "profiles", "pmc_q4_0_mmvq_packed_m6_ffn_up.json")
 PMC_RECORD_GATE_UP = os.path.join(ROOT, "profiles", "pmc_q4_0_gate_up_silu_q8_1_packed_m6_ffn.json")
 KERNEL_SOURCES = ["block_quantized_gemv_q8_amd/csrc/q4_0_packed.hip",
-                  "block_quantized_gemv_q8_amd/csrc/bq8_dev.h"]
+                  "block_quantized_gemv_q8_amd/csrc/bq8_dev.h",
+                  "block_quantized_gemv_q8_amd/csrc/bq8_host.h"]
 
 METRIC = "µs + effective weight GB/s (% of HBM peak) per Q4_0 M=6 proj; LM-head top-1 µs"
 

@@ -18,6 +18,7 @@
 // step adds (one last sum writes y).  Every shape and every layer's pointers are validated
 // before the first launch, so a rejected call enqueues nothing.
 #include "bq8_dev.h"
+#include "bq8_host.h"
 
 namespace bq8 {
 
@@ -119,10 +120,8 @@ static bq8_status ffn_stream(proj_fn proj, bool joint, int64_t align_k,
     // are cleared here once, and every completed launch leaves them clear
     void *ws = nullptr;
     int64_t wsb = 0;
-    int cus = 0, dev = 0;
-    if (joint && hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus > 0) {
+    const int64_t cus = joint ? device_cus() : -1;
+    if (cus > 0) {
         wsb = q4_0_mmvq_packed_ws_bytes();
         if (wsb > 0 && work_bytes >= L.total + align256(wsb))
             ws = base + L.total;

@@ -22,6 +22,7 @@
 // sums of a row meet in LDS and are added in wave order, so results are
 // deterministic and equal rows give equal outputs.
 #include "bq8_dev.h"
+#include "bq8_host.h"
 
 #include <utility>
 
@@ -459,22 +460,6 @@ static int pick_splits(int64_t N, int64_t units, int M, int64_t lds_limit, bool 
     return (int)(s < 1 ? 1 : s);
 }
 
-// Largest dynamic LDS a workgroup may use on the current device (queried
-// once; 160 KB on gfx950).
-static int64_t lds_limit()
-{
-    static int64_t cached = -1;
-    if (cached < 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-            v <= 0)
-            v = 65536;
-        cached = v;
-    }
-    return cached;
-}
-
 // Waves per workgroup for the MFMA kernel: four (measured best on the
 // ffn_up and down shapes for every M, against 1..8), fewer when the row has
 // fewer chunks or LDS cannot hold four rings.
@@ -500,13 +485,8 @@ static bq8_status launch_mfma(const void *w, int64_t N, int nb, const void *xq, 
     const int64_t ring = (int64_t)s * SH::WAVE_LDS;
     const int64_t partial = (int64_t)s * SH::MS * 4 * 32 * (int64_t)sizeof(float);
     const int64_t lds = ring > partial ? ring : partial;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)q4_0_mmvq_mfma_kernel<M, CB, NST>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit) != hipSuccess)
-            return BQ8_ERR_HIP;
-        attr_set = true;
-    }
+    if (!allow_dynamic_lds((const void *)q4_0_mmvq_mfma_kernel<M, CB, NST>, limit))
+        return BQ8_ERR_HIP;
     hipLaunchKernelGGL((q4_0_mmvq_mfma_kernel<M, CB, NST>), dim3((unsigned)tiles), dim3(WAVE * s),
                        (size_t)lds, stream, (const uint8_t *)w, (int)N, nb, (const uint8_t *)xq, y);
     return launch_status();
@@ -526,7 +506,7 @@ static bq8_status mmvq_launch(const void *w, int64_t N, int64_t K, const void *x
         return BQ8_ERR_ALIGN;
     const int nb = (int)(K / QK);
     const bool al = (K % 256 == 0);
-    const int64_t limit = lds_limit();
+    const int64_t limit = device_lds_limit();
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     {
@@ -550,14 +530,8 @@ static bq8_status mmvq_launch(const void *w, int64_t N, int64_t K, const void *x
     const size_t stage_bytes = al ? (size_t)S * STAGE_BYTES : 0;
     const size_t lds = partial_bytes > stage_bytes ? partial_bytes : stage_bytes;
     if (al) {
-        static bool attr_set = false;
-        if (!attr_set) {
-            if (hipFuncSetAttribute((const void *)q4_0_mmvq_dot4_kernel<M, true>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)limit) != hipSuccess)
-                return BQ8_ERR_HIP;
-            attr_set = true;
-        }
+        if (!allow_dynamic_lds((const void *)q4_0_mmvq_dot4_kernel<M, true>, limit))
+            return BQ8_ERR_HIP;
         hipLaunchKernelGGL((q4_0_mmvq_dot4_kernel<M, true>), grid, block, lds, s,
                            (const uint8_t *)w, (int)N, nb, (const uint8_t *)xq, y);
     } else

@@ -27,8 +27,7 @@
 // gate/up launch with the SiLU*up + Q8_1 epilogue
 // (q4_0_gate_up_silu_q8_1_packed).
 #include "bq8_dev.h"
-
-#include <mutex>
+#include "bq8_host.h"
 
 namespace bq8 {
 
@@ -695,41 +694,6 @@ __global__ __launch_bounds__(512) void q4_0_gate_up_packed_kernel(
         __hip_atomic_store(ws_count + j / P, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Lets `kernel` take up to `limit` bytes of dynamic LDS, once per kernel per
-// process (a few kernels; later calls find it in the table).
-static bool set_lds_limit(const void *kernel, int64_t limit)
-{
-    static std::mutex mu;
-    static const void *done[512];
-    static int ndone = 0;
-    std::lock_guard<std::mutex> lock(mu);
-    for (int i = 0; i < ndone; ++i)
-        if (done[i] == kernel)
-            return true;
-    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit) !=
-        hipSuccess)
-        return false;
-    if (ndone < 512)
-        done[ndone++] = kernel;
-    return true;
-}
-
-// Largest dynamic LDS a workgroup may use on the current device (queried
-// once; 160 KB on gfx950).
-static int64_t packed_lds_limit()
-{
-    static int64_t cached = -1;
-    if (cached < 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-            v <= 0)
-            v = 65536;
-        cached = v;
-    }
-    return cached;
-}
-
 // Waves per workgroup: about 1600 waves in flight for M >= 3 and 2560 for
 // the lighter M <= 2 (measured on the ffn_up and down shapes: two and five
 // waves per 16-row tile at M = 6, three and eight at M = 1), at least two, at
@@ -754,23 +718,6 @@ static int packed_waves(int64_t wgs, int64_t chunks, int M, int64_t wave_lds, in
 static int packed_parts(int64_t C)
 {
     return (int)(C < 4 ? C : 4);
-}
-
-// Compute units of the current device (queried once per device).
-static int64_t device_cus()
-{
-    static int64_t cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return -1;
-    if (cached[dev] <= 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            v <= 0)
-            return -1;
-        cached[dev] = v;
-    }
-    return cached[dev];
 }
 
 // Workspace of the balanced launches: ws_count (one uint32 per cut tile or
@@ -822,7 +769,7 @@ static bq8_status packed_launch_nt(const uint8_t *wp, int64_t N, int64_t K, cons
     const int64_t units = (N + PK_TILE * NT - 1) / (PK_TILE * NT);
     const int P = packed_parts(C);
     const int64_t wave_lds = pk_wave_stride<M, NT>();
-    const int64_t limit = packed_lds_limit();
+    const int64_t limit = device_lds_limit();
     int s = NT == 1 ? packed_waves(units * nsplit, C / nsplit, M, wave_lds, limit)
                     : pair_waves(M, nsplit, C / nsplit, wave_lds, limit);
     // split launches at M <= 2 take a third wave per workgroup: down with 4
@@ -844,7 +791,7 @@ static bq8_status packed_launch_nt(const uint8_t *wp, int64_t N, int64_t K, cons
                                                    pk_ws_count_bytes(cus))
                        : nullptr;
     auto launch = [&](auto kernel) -> bq8_status {
-        if (!set_lds_limit((const void *)kernel, limit))
+        if (!allow_dynamic_lds((const void *)kernel, limit))
             return BQ8_ERR_HIP;
         (void)hipGetLastError();
         hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(WAVE * s), (size_t)lds, stream, QS,
@@ -906,18 +853,13 @@ static bq8_status gate_up_launch(const uint8_t *wg, const uint8_t *wu, int64_t N
 {
     const int nb = (int)(K / QK);
     const int64_t groups = N / (2 * PK_TILE);
-    const int64_t limit = packed_lds_limit();
+    const int64_t limit = device_lds_limit();
     const int s = gate_up_waves(groups, nb, M, pk_wave_stride<M, 4>(), limit);
     const int64_t lds = (int64_t)s * pk_wave_stride<M, 4>();
     if (lds > limit)
         return BQ8_ERR_SHAPE;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)q4_0_gate_up_packed_kernel<M>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)limit) != hipSuccess)
-            return BQ8_ERR_HIP;
-        attr_set = true;
-    }
+    if (!allow_dynamic_lds((const void *)q4_0_gate_up_packed_kernel<M>, limit))
+        return BQ8_ERR_HIP;
     const size_t dplane = (size_t)N * nb * 16;
     // with a workspace and at least as many groups as CUs, the groups past
     // the last multiple of the CU count are cut into P K ranges each (ffn

@@ -20,8 +20,11 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless the comment says otherwise.  The
- *     caller allocates and owns every buffer; the library allocates nothing
- *     and keeps no state between calls.
+ *     caller allocates and owns every buffer; the library allocates nothing.
+ *     Between calls it keeps only device properties, cached per device, and
+ *     the allocation-free head's own scratch array (q6k_lmhead_top1_noalloc).
+ *     Any host thread may call, with any device current: the call runs on
+ *     the current device.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work; results are valid once the stream reaches
  *     them.  Nothing synchronizes inside the library.
