@@ -272,12 +272,13 @@ def time_down_sweep(torch, bq, synth, reps):
     wps = [bq.q4_0_pack(wi) for wi in ws]
     xq = bq.q8_1_quantize(torch.from_numpy(x).to("cuda"))
     wb = q4_0_bytes(N, K)
-    P = bq.q4_0_mmvq_packed_splits(N, K)
     pw = bq.q4_0_mmvq_packed_workspace()
-    out = {"packed_split_ranges": P, "packed_launch": "q4_0_mmvq_packed_ws"}
+    out = {"packed_split_ranges": {m: bq.q4_0_mmvq_packed_splits_rows(N, K, m) for m in cfg["Ms"]},
+           "packed_launch": "q4_0_mmvq_packed_ws"}
     for m in cfg["Ms"]:
         f = getattr(bq, f"q4_0_mmvq_m{m}")
         xm = xq[:m]
+        P = out["packed_split_ranges"][m]
         y = torch.empty((m, N), dtype=torch.float32, device="cuda")
         yp = torch.empty((P, m, N), dtype=torch.float32, device="cuda")
         usp = time_batches(torch, lambda i: bq.q4_0_mmvq_packed(wps[i % ROTATE], N, K, xm, m, y,
@@ -588,7 +589,7 @@ def profile_target(torch, bq, synth, target, reps, args=None):
     elif target == "packed_one":
         # one launch kind at one M on one shape, so that a counter record
         # holds nothing else: --shape ffn_up|down, --m, --launch
-        # whole (no workspace) | ws (CU-balanced) | split (the default split)
+        # whole (no workspace) | ws (CU-balanced) | split (the split count for m rows)
         cfg = synth.FFN_UP if args.shape == "ffn_up" else synth.DOWN_SWEEP
         N, K, m = cfg["N"], cfg["K"], args.m
         w0 = synth.q4_0_weights_device(cfg["seed"], N, K)
@@ -597,7 +598,7 @@ def profile_target(torch, bq, synth, target, reps, args=None):
             wps[i] = wps[0].clone()
         del w0
         xq = bq.q8_1_quantize(torch.randn((m, K), device="cuda"))
-        P = bq.q4_0_mmvq_packed_splits(N, K)
+        P = bq.q4_0_mmvq_packed_splits_rows(N, K, m)
         y = torch.empty((P, m, N), dtype=torch.float32, device="cuda")
         pw = bq.q4_0_mmvq_packed_workspace()
         for i in range(reps):

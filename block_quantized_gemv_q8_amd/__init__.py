@@ -15,7 +15,8 @@ _API_NAMES = {
     "silu_mul_q8_1", "rms_norm_q8_1",
     "q4_0_pack_bytes", "q4_0_pack", "q4_0_mmvq_packed", "q4_0_mmvq_packed_ws_bytes",
     "q4_0_mmvq_packed_workspace", "q4_0_gate_up_silu_q8_1_packed",
-    "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "rms_norm_q8_1_sum",
+    "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits", "q4_0_mmvq_packed_splits_rows",
+    "rms_norm_q8_1_sum",
     "q4_0_ffn_stream_layout", "q4_0_ffn_stream", "stream_weight_table", "stream_stages",
     "hbm_read_probe",
 }

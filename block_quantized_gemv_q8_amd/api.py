@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.q4_0_mmvq_packed_split.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _P, _P]
         L.q4_0_mmvq_packed_splits.restype = _I64
         L.q4_0_mmvq_packed_splits.argtypes = [_I64, _I64]
+        L.q4_0_mmvq_packed_splits_rows.restype = _I64
+        L.q4_0_mmvq_packed_splits_rows.argtypes = [_I64, _I64, _I64]
         L.rms_norm_q8_1_sum.restype = _ST
         L.rms_norm_q8_1_sum.argtypes = [_P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P]
         L.q4_0_gate_up_silu_q8_1_packed.restype = _ST
@@ -422,6 +424,12 @@ def q4_0_mmvq_packed_splits(N: int, K: int) -> int:
     return int(lib().q4_0_mmvq_packed_splits(N, K))
 
 
+def q4_0_mmvq_packed_splits_rows(N: int, K: int, M: int) -> int:
+    """The K-range count for a split launch of M rows on the current device
+    (-1 for an invalid shape, or without a device at M >= 11)."""
+    return int(lib().q4_0_mmvq_packed_splits_rows(N, K, M))
+
+
 def q4_0_mmvq_packed_split(wp: torch.Tensor, N: int, K: int, xq: torch.Tensor, M: int,
                            nsplit: int, ypart: torch.Tensor | None = None) -> torch.Tensor:
     """ypart f32 [nsplit][M][N]: the packed product with K cut into nsplit
@@ -533,6 +541,7 @@ __all__ = ["Bq8Error", "lib", "status_string", "abi_version", "q8_1_quantize", "
            "q6k_lmhead_candidate_max", "q6k_compact_bytes", "q6k_pack_compact",
            "silu_mul_q8_1", "rms_norm_q8_1", "rms_norm_q8_1_sum", "q4_0_pack_bytes", "q4_0_pack",
            "q4_0_mmvq_packed", "q4_0_mmvq_packed_split", "q4_0_mmvq_packed_splits",
+           "q4_0_mmvq_packed_splits_rows",
            "q4_0_gate_up_silu_q8_1_packed", "q4_0_ffn_stream_layout", "q4_0_ffn_stream",
            "stream_weight_table", "stream_stages", "synth"]
 

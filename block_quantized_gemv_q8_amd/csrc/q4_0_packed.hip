@@ -905,6 +905,61 @@ static int packed_default_splits(int64_t N, int64_t K)
     return (int)(p < 1 ? 1 : p);
 }
 
+// The split count for M rows.  Up to M = 10 a split launch keeps one tile
+// per workgroup and the count is packed_default_splits.  From M = 11 two
+// tiles share a workgroup, and the count (2..8, at most one range per
+// chunk, every workgroup resident at once by the runtime's occupancy figure)
+// is the one that spreads the workgroups most evenly over the CUs: the
+// least ratio of the busiest CU's workgroups to the mean, the smaller count
+// on a tie.  Down [5120 x 17408], 160 two-tile units, us for 2 / 3 / 4 / 5 /
+// 6 / 8 ranges: M = 12 16.5 / 13.0 / 14.7 / 15.0 / 13.5 / 15.1, M = 17
+// 20.5 / 16.3 / 18.5 / 20.2 / 17.8 / 20.3, following that ratio (1.6, 1.07,
+// 1.2, 1.28, 1.07 at 256 CUs; 8 ranges exceed the resident count).  -1
+// without a device.
+template <int M>
+static int64_t packed_splits_rows(int64_t N, int64_t K)
+{
+    const int64_t dflt = packed_default_splits(N, K);
+    if constexpr (M >= 11) {
+        const int64_t cus = device_cus();
+        if (cus <= 0)
+            return -1;
+        if (N % (2 * PK_TILE) != 0)
+            return dflt;
+        const int64_t units = N / (2 * PK_TILE);
+        const int64_t C = K / QK / PK_CB;
+        const int64_t limit = device_lds_limit();
+        const int64_t wave_lds = pk_wave_stride<M, 2>();
+        const void *kernel = (const void *)q4_0_mmvq_packed_kernel<M, PK_ANY, 2>;
+        if (!allow_dynamic_lds(kernel, limit))
+            return -1;
+        int64_t best = 0, best_w = 1, best_top = 0;
+        for (int64_t n = 2; n <= MAX_SPLIT && n <= C; ++n) {
+            const int64_t w = units * n;
+            if (w < cus) // the launch would keep one tile per workgroup
+                continue;
+            const int s = pair_waves(M, (int)n, C / n, wave_lds, limit);
+            int per_cu = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, WAVE * s,
+                                                             (size_t)s * wave_lds) != hipSuccess ||
+                per_cu <= 0)
+                return -1;
+            if (w > per_cu * cus)
+                continue;
+            // busiest CU against the mean: top / (w / cus), compared exactly
+            const int64_t top = (w + cus - 1) / cus;
+            if (best == 0 || top * best_w < best_top * w) {
+                best = n;
+                best_w = w;
+                best_top = top;
+            }
+        }
+        if (best > 0)
+            return best;
+    }
+    return dflt;
+}
+
 static bq8_status packed_product(const void *wp, int64_t N, int64_t K, const void *xq, int64_t M,
                                  int nsplit, float *y, void *ws, int64_t ws_bytes, void *stream)
 {
@@ -1007,6 +1062,22 @@ BQ8_EXPORT int64_t q4_0_mmvq_packed_splits(int64_t N, int64_t K)
     if (!packed_shape_ok(N, K))
         return -1;
     return packed_default_splits(N, K);
+}
+
+BQ8_EXPORT int64_t q4_0_mmvq_packed_splits_rows(int64_t N, int64_t K, int64_t M)
+{
+    if (!packed_shape_ok(N, K) || M < 1 || M > 17)
+        return -1;
+    switch (M) {
+    case 11: return packed_splits_rows<11>(N, K);
+    case 12: return packed_splits_rows<12>(N, K);
+    case 13: return packed_splits_rows<13>(N, K);
+    case 14: return packed_splits_rows<14>(N, K);
+    case 15: return packed_splits_rows<15>(N, K);
+    case 16: return packed_splits_rows<16>(N, K);
+    case 17: return packed_splits_rows<17>(N, K);
+    default: return packed_default_splits(N, K);
+    }
 }
 
 BQ8_EXPORT bq8_status q4_0_mmvq_packed_split(const void *wp, int64_t N, int64_t K,

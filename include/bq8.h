@@ -189,6 +189,15 @@ bq8_status q4_0_mmvq(const void *w, int64_t N, int64_t K, const void *xq, int64_
  *   [N][K] projection (enough ranges for at least 1024 workgroups, at most
  *   8), or -1 if the shape is invalid.  1 for [17408 x 5120], 4 for
  *   [5120 x 17408].
+ * q4_0_mmvq_packed_splits_rows: host; the nsplit for a split launch of M
+ *   rows on the current device.  M <= 10: q4_0_mmvq_packed_splits(N, K).
+ *   M >= 11 (two 16-row tiles per workgroup when N % 32 == 0): of the
+ *   counts 2..8, at most K/256, whose workgroups are all resident at once
+ *   by the runtime's occupancy figure, the one that spreads them most
+ *   evenly over the CUs (least ratio of the busiest CU's workgroups to the
+ *   mean; the smaller count on a tie), else q4_0_mmvq_packed_splits(N, K).
+ *   3 for [5120 x 17408] at M = 11..17 on MI355X.  -1 for an invalid shape
+ *   or M, or when M >= 11 and no device can be queried.
  * Shape: 1 <= N < 2^31, 512 <= K <= 2^26, K % 512 == 0.
  * ---------------------------------------------------------------------- */
 int64_t q4_0_pack_bytes(int64_t N, int64_t K);
@@ -202,6 +211,7 @@ int64_t q4_0_mmvq_packed_ws_bytes(void);
 bq8_status q4_0_mmvq_packed_split(const void *wp, int64_t N, int64_t K, const void *xq,
                                   int64_t M, int64_t nsplit, float *ypart, void *stream);
 int64_t q4_0_mmvq_packed_splits(int64_t N, int64_t K);
+int64_t q4_0_mmvq_packed_splits_rows(int64_t N, int64_t K, int64_t M);
 
 /* ------------------------------------------------------------------------
  * Joint gate/up projection with SiLU(gate)*up and its Q8_1 requantization

@@ -54,6 +54,9 @@ int main(void)
     EXPECT(q4_0_mmvq_packed_ws(A, 16, 512, A, 6, A, (char *)A + 128, 1 << 20, NULL),
            BQ8_ERR_ALIGN);
     EXPECT(q4_0_mmvq_packed_splits(5120, 17408), 4);
+    EXPECT(q4_0_mmvq_packed_splits_rows(5120, 17408, 6), 4);
+    EXPECT(q4_0_mmvq_packed_splits_rows(5120, 17408, 18), -1);
+    EXPECT(q4_0_mmvq_packed_splits_rows(16, 256, 12), -1);
     EXPECT(q4_0_mmvq_packed_split(A, 16, 512, A, 6, 9, A, NULL), BQ8_ERR_SHAPE);
     EXPECT(q4_0_gate_up_silu_q8_1_packed(A, A, 48, 512, A, 6, NULL, NULL, NULL, A, NULL),
            BQ8_ERR_SHAPE); /* N % 32 != 0 */

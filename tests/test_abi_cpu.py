@@ -41,7 +41,8 @@ def test_header_declares_expected_entry_points():
               "q6k_lmhead_candidate_max", "q6k_compact_bytes", "q6k_pack_compact",
               "q6k_lmhead_top1_compact", "q6k_lmhead_candidate_max_compact",
               "bq8_hbm_read_probe", "q4_0_mmvq_packed_ws", "q4_0_mmvq_packed_ws_bytes",
-              "q4_0_gate_up_silu_q8_1_packed_ws", "q6k_lmhead_top1_noalloc"]:
+              "q4_0_gate_up_silu_q8_1_packed_ws", "q6k_lmhead_top1_noalloc",
+              "q4_0_mmvq_packed_splits_rows"]:
         assert n in names
 
 
@@ -321,6 +322,15 @@ def test_split_product_and_summed_rms_validation(L):
     assert b.q4_0_mmvq_packed_splits(16, 512) == 2        # capped at the 2 chunks
     assert b.q4_0_mmvq_packed_splits(16, 4096) == 8       # capped at 8
     assert b.q4_0_mmvq_packed_splits(16, 256) == -1
+    # the per-M count: the shape's count up to M = 10; from M = 11 it reads the
+    # device's occupancy, so with no device it reports -1
+    for m in range(1, 11):
+        assert b.q4_0_mmvq_packed_splits_rows(5120, 17408, m) == 4
+        assert b.q4_0_mmvq_packed_splits_rows(17408, 5120, m) == 1
+    for m in range(11, 18):
+        assert b.q4_0_mmvq_packed_splits_rows(5120, 17408, m) == -1
+    for bad in ((5120, 17408, 0), (5120, 17408, 18), (16, 256, 6), (16, 256, 12)):
+        assert b.q4_0_mmvq_packed_splits_rows(*bad) == -1
     f = L.q4_0_mmvq_packed_split
     assert f(None, 5120, 17408, A, 6, 4, A, None) == NULL
     assert f(A, 5120, 17408, A, 6, 0, A, None) == SHAPE

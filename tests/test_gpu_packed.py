@@ -235,6 +235,34 @@ def test_mmvq_packed_split_down_full():
         assert_close(part_sum(parts), ref[:m], bound[:m], f"down split m{m}")
 
 
+def test_mmvq_packed_split_rows_count_down_full():
+    """The per-M split count at the down shape: the shape's count up to
+    M = 10, then a count whose two-tile workgroups are all resident; its
+    split launch meets the oracle bar at M = 11, 12 and 17."""
+    w, x = synth.down_sweep()
+    N, K = 5120, 17408
+    counts = {m: bq.q4_0_mmvq_packed_splits_rows(N, K, m) for m in range(1, 18)}
+    say(f"split counts {counts}")
+    for m in range(1, 11):
+        assert counts[m] == bq.q4_0_mmvq_packed_splits(N, K)
+    for m in range(11, 18):
+        assert 2 <= counts[m] <= 8
+    import torch
+
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        # 160 two-tile units: 3 ranges put 480 workgroups 1 or 2 to a CU
+        assert all(counts[m] == 3 for m in range(11, 18)), counts
+    xqd = bq.q8_1_quantize(dev(x))
+    xq = host(xqd)
+    ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
+    wp = bq.q4_0_pack(dev(w))
+    for m in (11, 12, 17):
+        P = counts[m]
+        say(f"down split {P} M={m}")
+        parts = host(bq.q4_0_mmvq_packed_split(wp, N, K, xqd[:m], m, P))
+        assert_close(part_sum(parts), ref[:m], bound[:m], f"down split {P} m{m}")
+
+
 @pytest.mark.parametrize("P,M,K", [(4, 6, 5120), (1, 6, 5120), (3, 17, 1056), (8, 2, 32768),
                                    (2, 1, 32)])
 def test_rms_norm_q8_1_sum(P, M, K):
