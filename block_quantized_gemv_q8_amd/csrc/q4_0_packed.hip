@@ -757,137 +757,6 @@ static int pair_waves(int M, int nsplit, int64_t chunks, int64_t wave_lds, int64
     return (int)(s < 1 ? 1 : s);
 }
 
-// One launch of the product with NT 16-row tiles per workgroup (the unit
-// the K ranges, the split and the cut apply to).
-template <int M, int NT>
-static bq8_status packed_launch_nt(const uint8_t *wp, int64_t N, int64_t K, const void *xq,
-                                   int nsplit, float *y, void *ws, int64_t cus,
-                                   hipStream_t stream)
-{
-    const int nb = (int)(K / QK);
-    const int64_t C = nb / PK_CB;
-    const int64_t units = (N + PK_TILE * NT - 1) / (PK_TILE * NT);
-    const int P = packed_parts(C);
-    const int64_t wave_lds = pk_wave_stride<M, NT>();
-    const int64_t limit = device_lds_limit();
-    int s = NT == 1 ? packed_waves(units * nsplit, C / nsplit, M, wave_lds, limit)
-                    : pair_waves(M, nsplit, C / nsplit, wave_lds, limit);
-    // split launches at M <= 2 take a third wave per workgroup: down with 4
-    // K ranges, M = 1 / 2: 10.18 / 10.20 -> 9.92 / 9.92 us (at M = 6 and 9
-    // the third wave lost: 11.15 -> 11.31, 13.37 -> 14.71 us)
-    if (NT == 1 && nsplit > 1 && M <= 2 && s < 3 && C / nsplit >= 3 && 3 * wave_lds <= limit)
-        s = 3;
-    const int64_t lds = (int64_t)s * wave_lds;
-    if (lds > limit)
-        return BQ8_ERR_SHAPE;
-    int64_t whole = units;
-    if (ws && nsplit == 1 && M >= 9)
-        whole = units - units % cus;
-    const int64_t grid = nsplit > 1 ? units * nsplit : whole + (units - whole) * P;
-    const uint8_t *QS = wp;
-    const uint16_t *D = reinterpret_cast<const uint16_t *>(wp + N * nb * 16);
-    uint32_t *ws_count = static_cast<uint32_t *>(ws);
-    float *ws_sum = ws ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
-                                                   pk_ws_count_bytes(cus))
-                       : nullptr;
-    auto launch = [&](auto kernel) -> bq8_status {
-        if (!allow_dynamic_lds((const void *)kernel, limit))
-            return BQ8_ERR_HIP;
-        (void)hipGetLastError();
-        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(WAVE * s), (size_t)lds, stream, QS,
-                           D, (int)N, nb, nsplit, P, (int)whole, (const uint8_t *)xq, y, ws_sum,
-                           ws_count);
-        return launch_status();
-    };
-    if constexpr (NT == 1 && M <= 8) {
-        if (N % PK_TILE == 0)
-            return nsplit > 1 ? launch(q4_0_mmvq_packed_kernel<M, PK_FULL_SPLIT, 1>)
-                              : launch(q4_0_mmvq_packed_kernel<M, PK_FULL_WHOLE, 1>);
-    }
-    return launch(q4_0_mmvq_packed_kernel<M, PK_ANY, NT>);
-}
-
-// From M = 9 (M = 11 on a split launch) a workgroup takes two tiles when
-// N % 32 == 0 and the launch still has a workgroup for every CU: each staged
-// activation chunk and each A operand then serve two tiles (the activation
-// bytes per chunk outweigh the weight bytes from M = 8 up).  Against one
-// tile per workgroup: ffn_up (balanced) M = 9 / 12 / 17 12.6 / 13.1 / 16.6
-// against 13.7 / 14.1 / 18.5 us; down, 4 K ranges, M = 12 / 17 14.8 / 18.6
-// against 15.4 / 20.3 us, while at M = 9 and 10 one tile stays ahead
-// (13.9 against 14.4 us).
-template <int M>
-static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const void *xq, int nsplit,
-                                float *y, void *ws, int64_t cus, hipStream_t stream)
-{
-    if constexpr (M >= 9) {
-        const int64_t cu = cus > 0 ? cus : device_cus();
-        if (N % (2 * PK_TILE) == 0 && cu > 0 && N / (2 * PK_TILE) * nsplit >= cu &&
-            (nsplit == 1 || M >= 11))
-            return packed_launch_nt<M, 2>(wp, N, K, xq, nsplit, y, ws, cu, stream);
-    }
-    return packed_launch_nt<M, 1>(wp, N, K, xq, nsplit, y, ws, cus, stream);
-}
-
-// Waves per gate/up workgroup: about 1088 waves in flight for M <= 2, 1632
-// for M = 3..8 and 2176 from M = 9 (two, three and four per 32-column
-// workgroup on the 17408 x 5120 shape; a sweep of 2..8 waves there put
-// M = 1 / 6 / 9 / 17 at 18.6 / 19.8 / 25.6 / 30.6 us), at least one, at most
-// eight, never more than the row has chunks or the LDS holds.
-static int gate_up_waves(int64_t groups, int nb, int M, int64_t wave_lds, int64_t limit)
-{
-    const int64_t target = M <= 2 ? 1088 : M <= 8 ? 1632 : 2176;
-    int64_t s = (target + groups - 1) / groups;
-    if (s > 8)
-        s = 8;
-    if (s > nb / PK_CB)
-        s = nb / PK_CB;
-    while (s > 1 && s * wave_lds > limit)
-        --s;
-    return (int)(s < 1 ? 1 : s);
-}
-
-template <int M>
-static bq8_status gate_up_launch(const uint8_t *wg, const uint8_t *wu, int64_t N, int64_t K,
-                                 const void *xq, float *g, float *u, float *h, void *hq, void *ws,
-                                 int64_t cus, hipStream_t stream)
-{
-    const int nb = (int)(K / QK);
-    const int64_t groups = N / (2 * PK_TILE);
-    const int64_t limit = device_lds_limit();
-    const int s = gate_up_waves(groups, nb, M, pk_wave_stride<M, 4>(), limit);
-    const int64_t lds = (int64_t)s * pk_wave_stride<M, 4>();
-    if (lds > limit)
-        return BQ8_ERR_SHAPE;
-    if (!allow_dynamic_lds((const void *)q4_0_gate_up_packed_kernel<M>, limit))
-        return BQ8_ERR_HIP;
-    const size_t dplane = (size_t)N * nb * 16;
-    // with a workspace and at least as many groups as CUs, the groups past
-    // the last multiple of the CU count are cut into P K ranges each (ffn
-    // shape, M = 6 / 1 / 9 / 17: 22.4 / 21.5 / 28.1 / 34.5 us uncut, 20.6 /
-    // 19.9 / 26.1 / 31.6 us cut).  With fewer groups than CUs every group
-    // would be cut, and the meeting outweighs the balance (the 8-way shard,
-    // 68 groups: 9.5 us uncut, 12.3 us cut).
-    const int P = packed_parts(nb / PK_CB);
-    const int64_t whole = ws && groups >= cus ? groups - groups % cus : groups;
-    const int64_t grid = whole + (groups - whole) * P;
-    uint32_t *ws_count = static_cast<uint32_t *>(ws);
-    float *ws_sum = ws ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
-                                                   pk_ws_count_bytes(cus))
-                       : nullptr;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL((q4_0_gate_up_packed_kernel<M>), dim3((unsigned)grid), dim3(WAVE * s),
-                       (size_t)lds, stream, wg, reinterpret_cast<const uint16_t *>(wg + dplane), wu,
-                       reinterpret_cast<const uint16_t *>(wu + dplane), (int)N, nb, P, (int)whole,
-                       (const uint8_t *)xq, g, u, h, (uint8_t *)hq, ws_sum, ws_count);
-    return launch_status();
-}
-
-static bool packed_shape_ok(int64_t N, int64_t K)
-{
-    return N >= 1 && N < (int64_t(1) << 31) && K >= 512 && K % 512 == 0 &&
-           K <= (int64_t(1) << 26) && N * (K / QK) * Q4_0_BYTES < (int64_t(1) << 40);
-}
-
 constexpr int MAX_SPLIT = 8;
 
 // The split count for a shape: enough K ranges that the launch has at least
@@ -958,6 +827,150 @@ static int64_t packed_splits_rows(int64_t N, int64_t K)
             return best;
     }
     return dflt;
+}
+
+// One launch of the product with NT 16-row tiles per workgroup (the unit
+// the K ranges, the split and the cut apply to).
+template <int M, int NT>
+static bq8_status packed_launch_nt(const uint8_t *wp, int64_t N, int64_t K, const void *xq,
+                                   int nsplit, float *y, void *ws, int64_t cus,
+                                   hipStream_t stream, int cut_all = 0)
+{
+    const int nb = (int)(K / QK);
+    const int64_t C = nb / PK_CB;
+    const int64_t units = (N + PK_TILE * NT - 1) / (PK_TILE * NT);
+    const int P = cut_all > 0 ? cut_all : packed_parts(C);
+    const int64_t wave_lds = pk_wave_stride<M, NT>();
+    const int64_t limit = device_lds_limit();
+    const int ranges = cut_all > 0 ? cut_all : nsplit;
+    int s = NT == 1 ? packed_waves(units * nsplit, C / nsplit, M, wave_lds, limit)
+                    : pair_waves(M, ranges, C / ranges, wave_lds, limit);
+    // split launches at M <= 2 take a third wave per workgroup: down with 4
+    // K ranges, M = 1 / 2: 10.18 / 10.20 -> 9.92 / 9.92 us (at M = 6 and 9
+    // the third wave lost: 11.15 -> 11.31, 13.37 -> 14.71 us)
+    if (NT == 1 && nsplit > 1 && M <= 2 && s < 3 && C / nsplit >= 3 && 3 * wave_lds <= limit)
+        s = 3;
+    const int64_t lds = (int64_t)s * wave_lds;
+    if (lds > limit)
+        return BQ8_ERR_SHAPE;
+    int64_t whole = units;
+    if (cut_all > 0)
+        whole = 0;
+    else if (ws && nsplit == 1 && M >= 9)
+        whole = units - units % cus;
+    const int64_t grid = nsplit > 1 ? units * nsplit : whole + (units - whole) * P;
+    const uint8_t *QS = wp;
+    const uint16_t *D = reinterpret_cast<const uint16_t *>(wp + N * nb * 16);
+    uint32_t *ws_count = static_cast<uint32_t *>(ws);
+    float *ws_sum = ws ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
+                                                   pk_ws_count_bytes(cus))
+                       : nullptr;
+    auto launch = [&](auto kernel) -> bq8_status {
+        if (!allow_dynamic_lds((const void *)kernel, limit))
+            return BQ8_ERR_HIP;
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(WAVE * s), (size_t)lds, stream, QS,
+                           D, (int)N, nb, nsplit, P, (int)whole, (const uint8_t *)xq, y, ws_sum,
+                           ws_count);
+        return launch_status();
+    };
+    if constexpr (NT == 1 && M <= 8) {
+        if (N % PK_TILE == 0)
+            return nsplit > 1 ? launch(q4_0_mmvq_packed_kernel<M, PK_FULL_SPLIT, 1>)
+                              : launch(q4_0_mmvq_packed_kernel<M, PK_FULL_WHOLE, 1>);
+    }
+    return launch(q4_0_mmvq_packed_kernel<M, PK_ANY, NT>);
+}
+
+// From M = 9 (M = 11 on a split launch) a workgroup takes two tiles when
+// N % 32 == 0 and the launch still has a workgroup for every CU: each staged
+// activation chunk and each A operand then serve two tiles (the activation
+// bytes per chunk outweigh the weight bytes from M = 8 up).  Against one
+// tile per workgroup: ffn_up (balanced) M = 9 / 12 / 17 12.6 / 13.1 / 16.6
+// against 13.7 / 14.1 / 18.5 us; down, 4 K ranges, M = 12 / 17 14.8 / 18.6
+// against 15.4 / 20.3 us, while at M = 9 and 10 one tile stays ahead
+// (13.9 against 14.4 us).
+template <int M>
+static bq8_status packed_launch(const uint8_t *wp, int64_t N, int64_t K, const void *xq, int nsplit,
+                                float *y, void *ws, int64_t cus, hipStream_t stream)
+{
+    if constexpr (M >= 9) {
+        const int64_t cu = cus > 0 ? cus : device_cus();
+        if (N % (2 * PK_TILE) == 0 && cu > 0 && N / (2 * PK_TILE) * nsplit >= cu &&
+            (nsplit == 1 || M >= 11))
+            return packed_launch_nt<M, 2>(wp, N, K, xq, nsplit, y, ws, cu, stream);
+        if constexpr (M >= 11) {
+            // a balanced launch with fewer two-tile units than CUs: every
+            // unit is cut into the split count's K ranges, which meet in the
+            // workspace
+            if (ws && nsplit == 1 && N % (2 * PK_TILE) == 0 && cu > 0) {
+                const int64_t P = packed_splits_rows<M>(N, K);
+                if (P >= 2 && N / (2 * PK_TILE) * P >= cu)
+                    return packed_launch_nt<M, 2>(wp, N, K, xq, 1, y, ws, cu, stream, (int)P);
+            }
+        }
+    }
+    return packed_launch_nt<M, 1>(wp, N, K, xq, nsplit, y, ws, cus, stream);
+}
+
+// Waves per gate/up workgroup: about 1088 waves in flight for M <= 2, 1632
+// for M = 3..8 and 2176 from M = 9 (two, three and four per 32-column
+// workgroup on the 17408 x 5120 shape; a sweep of 2..8 waves there put
+// M = 1 / 6 / 9 / 17 at 18.6 / 19.8 / 25.6 / 30.6 us), at least one, at most
+// eight, never more than the row has chunks or the LDS holds.
+static int gate_up_waves(int64_t groups, int nb, int M, int64_t wave_lds, int64_t limit)
+{
+    const int64_t target = M <= 2 ? 1088 : M <= 8 ? 1632 : 2176;
+    int64_t s = (target + groups - 1) / groups;
+    if (s > 8)
+        s = 8;
+    if (s > nb / PK_CB)
+        s = nb / PK_CB;
+    while (s > 1 && s * wave_lds > limit)
+        --s;
+    return (int)(s < 1 ? 1 : s);
+}
+
+template <int M>
+static bq8_status gate_up_launch(const uint8_t *wg, const uint8_t *wu, int64_t N, int64_t K,
+                                 const void *xq, float *g, float *u, float *h, void *hq, void *ws,
+                                 int64_t cus, hipStream_t stream)
+{
+    const int nb = (int)(K / QK);
+    const int64_t groups = N / (2 * PK_TILE);
+    const int64_t limit = device_lds_limit();
+    const int s = gate_up_waves(groups, nb, M, pk_wave_stride<M, 4>(), limit);
+    const int64_t lds = (int64_t)s * pk_wave_stride<M, 4>();
+    if (lds > limit)
+        return BQ8_ERR_SHAPE;
+    if (!allow_dynamic_lds((const void *)q4_0_gate_up_packed_kernel<M>, limit))
+        return BQ8_ERR_HIP;
+    const size_t dplane = (size_t)N * nb * 16;
+    // with a workspace and at least as many groups as CUs, the groups past
+    // the last multiple of the CU count are cut into P K ranges each (ffn
+    // shape, M = 6 / 1 / 9 / 17: 22.4 / 21.5 / 28.1 / 34.5 us uncut, 20.6 /
+    // 19.9 / 26.1 / 31.6 us cut).  With fewer groups than CUs every group
+    // would be cut, and the meeting outweighs the balance (the 8-way shard,
+    // 68 groups: 9.5 us uncut, 12.3 us cut).
+    const int P = packed_parts(nb / PK_CB);
+    const int64_t whole = ws && groups >= cus ? groups - groups % cus : groups;
+    const int64_t grid = whole + (groups - whole) * P;
+    uint32_t *ws_count = static_cast<uint32_t *>(ws);
+    float *ws_sum = ws ? reinterpret_cast<float *>(static_cast<uint8_t *>(ws) +
+                                                   pk_ws_count_bytes(cus))
+                       : nullptr;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((q4_0_gate_up_packed_kernel<M>), dim3((unsigned)grid), dim3(WAVE * s),
+                       (size_t)lds, stream, wg, reinterpret_cast<const uint16_t *>(wg + dplane), wu,
+                       reinterpret_cast<const uint16_t *>(wu + dplane), (int)N, nb, P, (int)whole,
+                       (const uint8_t *)xq, g, u, h, (uint8_t *)hq, ws_sum, ws_count);
+    return launch_status();
+}
+
+static bool packed_shape_ok(int64_t N, int64_t K)
+{
+    return N >= 1 && N < (int64_t(1) << 31) && K >= 512 && K % 512 == 0 &&
+           K <= (int64_t(1) << 26) && N * (K / QK) * Q4_0_BYTES < (int64_t(1) << 40);
 }
 
 static bq8_status packed_product(const void *wp, int64_t N, int64_t K, const void *xq, int64_t M,

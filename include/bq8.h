@@ -165,9 +165,12 @@ bq8_status q4_0_mmvq(const void *w, int64_t N, int64_t K, const void *xq, int64_
  *   (range p = chunks
  *   floor(p*C/P) .. floor((p+1)*C/P) - 1 of the C = K/256 chunks of 8
  *   blocks), computed by separate workgroups whose range sums meet in the
- *   workspace and are added in range order.  Outputs of those tiles equal
- *   q4_0_mmvq_packed's up to the binary32 summation order, the others bit
- *   for bit; results are reproducible bit for bit.
+ *   workspace and are added in range order.  From M = 11, when N % 32 == 0
+ *   and there are fewer 32-row pairs of tiles than CUs, every pair is cut
+ *   instead, into P = q4_0_mmvq_packed_splits_rows(N, K, M) ranges (when
+ *   that count is at least 2 and gives a workgroup per CU).  Outputs of cut
+ *   tiles equal q4_0_mmvq_packed's up to the binary32 summation order, the
+ *   others bit for bit; results are reproducible bit for bit.
  *   ws: device memory, 256-byte aligned, ws_bytes >= q4_0_mmvq_packed_ws_bytes();
  *   caller-owned.  Zero-fill it once before its first use: every call that
  *   completes leaves it ready for the next (its counters back at zero).

@@ -287,7 +287,8 @@ def test_rms_norm_q8_1_sum(P, M, K):
 
 # The balanced launch (q4_0_mmvq_packed_ws): for M >= 9 the tiles past the
 # last multiple of the CU count are cut into min(4, K/256) ranges of K whose
-# sums meet in the workspace (M <= 8: no tile is cut).  Outputs of the other tiles are bitwise the plain
+# sums meet in the workspace (M <= 8: no tile is cut; from M = 11 with fewer
+# 32-row tile pairs than CUs, as at the down shape, every pair is cut).  Outputs of the other tiles are bitwise the plain
 # launch's; the cut tiles' are within the oracle's tolerance; results repeat
 # bit for bit.  Shapes: fewer tiles than CUs (every tile cut), a remainder
 # with a ragged last tile, the full ffn_up and down shapes, every M = 1..17
@@ -306,9 +307,14 @@ def _ws_count_bytes():
     return (_cus() * 4 + 255) // 256 * 256
 
 
-def _whole_rows(N, M):
+def _whole_rows(N, K, M):
     if M <= 8:
         return N
+    if M >= 11 and N % 32 == 0 and N // 32 < _cus():
+        # fewer tile pairs than CUs: every pair is cut into the per-M split count
+        P = bq.q4_0_mmvq_packed_splits_rows(N, K, M)
+        if P >= 2 and N // 32 * P >= _cus():
+            return 0
     tiles = (N + 15) // 16
     return min(N, 16 * (tiles - tiles % _cus()))
 
@@ -322,7 +328,7 @@ def test_mmvq_packed_ws_small():
         ref, bound = oracle.q4_0_gemv(w, N, K, xq, 17)
         wp, xqd = bq.q4_0_pack(dev(w)), dev(xq)
         for m in range(1, 18):
-            r0 = _whole_rows(N, m)
+            r0 = _whole_rows(N, K, m)
             say(f"q4_0_mmvq_packed_ws N={N} K={K} M={m} (rows {r0}.. cut into K ranges)")
             plain = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
             yw = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m, ws=ws))
@@ -337,7 +343,7 @@ def test_mmvq_packed_ws_small():
 def test_mmvq_packed_ws_full(N, K):
     ws = bq.q4_0_mmvq_packed_workspace()
     wd = synth.q4_0_weights_device(5200 + N, N, K)
-    r0 = _whole_rows(N, 17)
+    r0 = min(_whole_rows(N, K, m) for m in range(9, 18))
     w_cut = host(wd[r0:])                       # the cut tiles' rows, for the oracle
     wp = bq.q4_0_pack(wd)
     xqd = bq.q8_1_quantize(torch.randn((17, K), device=DEV))
@@ -347,7 +353,7 @@ def test_mmvq_packed_ws_full(N, K):
         say(f"q4_0_mmvq_packed_ws full N={N} K={K} M={m} (rows {r0}.. cut)")
         plain = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m))
         yw = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m, ws=ws))
-        whole = _whole_rows(N, m)
+        whole = _whole_rows(N, K, m)
         assert np.array_equal(yw[:, :whole].view(np.uint32), plain[:, :whole].view(np.uint32))
         assert_close(yw[:, r0:], ref[:m], bound[:m], f"ws full cut rows m{m}")
         again = host(bq.q4_0_mmvq_packed(wp, N, K, xqd[:m], m, ws=ws))
